@@ -1,0 +1,278 @@
+"""Plain scalar CPU oracle for the quantized Delta-rule decode step.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product library
+(``quantized_delta_rule_03_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``qdr_oracle.c`` (scalar C, fp32 state arithmetic with
+fp64 dot products, built with ``-ffp-contract=off``); this module only builds and
+loads it and marshals numpy arrays. See ``qdr_oracle.h`` for the contract and the
+page citations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qdr_oracle.c")
+_LIB = os.path.join(_HERE, "libqdr_oracle.so")
+
+GDN = 0
+KDA = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no SIMD intrinsics, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = [
+            "gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+            "-fPIC", "-shared", "-o", tmp, _SRC, "-lm",
+        ]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_long, ctypes.c_float
+        sig = {
+            "oref_assign_bits": (i32, [i32, i32, i32, P, P]),
+            "oref_layout": (i64, [i32, i32, P, P, P]),
+            "oref_pack": (i32, [i32, i32, P, P, P]),
+            "oref_unpack": (i32, [i32, i32, P, P, P]),
+            "oref_quantize": (None, [i32, i32, P, P, P, P, P]),
+            "oref_dequantize": (None, [i32, i32, P, P, P, P]),
+            "oref_step": (None, [i32, i32, i32, P, P, P, P, P, P, P, P, f32, P, P]),
+            "oref_window": (None, [i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, P, P]),
+            "oref_recur_fp64": (None, [i32, i32, i32, P, P, P, P, P, f32, P]),
+            "oref_request_bytes": (i64, [i32, i32, i32, P]),
+            "oref_quantize_pool": (i32, [i32, i32, i32, i32, P, P, P, P, P]),
+            "oref_dequantize_pool": (i32, [i32, i32, i32, i32, P, P, P, P, P]),
+            "oref_step_pool": (i32, [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                     i64, i64]),
+            "oref_window_pool": (i32, [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, P, P,
+                                       P, P, i64, i64]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(arr):
+    return None if arr is None else arr.ctypes.data
+
+
+def _c(arr, dtype):
+    a = np.ascontiguousarray(arr, dtype=dtype)
+    return a
+
+
+# ---------------------------------------------------------------------------
+# per-unit logical interface
+# ---------------------------------------------------------------------------
+
+def assign_bits(gate: int, halflife: np.ndarray, dk: int) -> np.ndarray:
+    """Lifetime quartile bit map; GDN halflife [n_head], KDA halflife [n_head, dk]."""
+    hl = _c(halflife, np.float64)
+    n_head = hl.shape[0]
+    out = np.zeros((n_head, dk), np.uint8)
+    if lib().oref_assign_bits(gate, n_head, dk, _p(hl), _p(out)) != 0:
+        raise ValueError("oref_assign_bits failed")
+    return out
+
+
+def layout(bits: np.ndarray, dv: int = 128):
+    """(tile_bytes, perm[dk], seg_bits[dk/32]) for one head's bit map."""
+    b = _c(bits, np.uint8)
+    dk = b.shape[0]
+    perm = np.zeros(dk, np.uint8)
+    seg = np.zeros(max(dk // 32, 1), np.uint8)
+    n = lib().oref_layout(dv, dk, _p(b), _p(perm), _p(seg))
+    if n < 0:
+        raise ValueError("bit map not representable in the packed format")
+    return int(n), perm, seg
+
+
+def pack(codes: np.ndarray, bits: np.ndarray) -> np.ndarray:
+    c = _c(codes, np.int8)
+    b = _c(bits, np.uint8)
+    dv, dk = c.shape
+    n, _, _ = layout(b, dv)
+    tile = np.zeros(n, np.uint8)
+    if lib().oref_pack(dv, dk, _p(b), _p(c), _p(tile)) != 0:
+        raise ValueError("oref_pack failed")
+    return tile
+
+
+def unpack(tile: np.ndarray, bits: np.ndarray, dv: int = 128) -> np.ndarray:
+    b = _c(bits, np.uint8)
+    t = _c(tile, np.uint8)
+    dk = b.shape[0]
+    codes = np.zeros((dv, dk), np.int8)
+    if lib().oref_unpack(dv, dk, _p(b), _p(t), _p(codes)) != 0:
+        raise ValueError("oref_unpack failed")
+    return codes
+
+
+def quantize(S: np.ndarray, bits: np.ndarray):
+    """fp32 state [dv, dk] -> (codes int8 [dv, dk], R [dk], c [dv])."""
+    S = _c(S, np.float32)
+    b = _c(bits, np.uint8)
+    dv, dk = S.shape
+    codes = np.zeros((dv, dk), np.int8)
+    R = np.zeros(dk, np.float32)
+    c = np.zeros(dv, np.float32)
+    lib().oref_quantize(dv, dk, _p(b), _p(S), _p(codes), _p(R), _p(c))
+    return codes, R, c
+
+
+def dequantize(codes: np.ndarray, R: np.ndarray, c: np.ndarray) -> np.ndarray:
+    codes = _c(codes, np.int8)
+    R = _c(R, np.float32)
+    c = _c(c, np.float32)
+    dv, dk = codes.shape
+    S = np.zeros((dv, dk), np.float32)
+    lib().oref_dequantize(dv, dk, _p(codes), _p(R), _p(c), _p(S))
+    return S
+
+
+def step(codes, R, c, bits, gate, q, k, v, a, b, return_state=False):
+    """One decode step on one unit. Returns (codes, R, c, o[, S_new])."""
+    codes = _c(codes, np.int8).copy()
+    R = _c(R, np.float32).copy()
+    c = _c(c, np.float32).copy()
+    bb = _c(bits, np.uint8)
+    dv, dk = codes.shape
+    q, k = _c(q, np.float32), _c(k, np.float32)
+    v = _c(v, np.float32)
+    a = _c(np.atleast_1d(a), np.float32)
+    o = np.zeros(dv, np.float32)
+    S_new = np.zeros((dv, dk), np.float32) if return_state else None
+    lib().oref_step(dv, dk, gate, _p(bb), _p(codes), _p(R), _p(c), _p(q), _p(k), _p(v),
+                    _p(a), float(b), _p(o), _p(S_new))
+    if return_state:
+        return codes, R, c, o, S_new
+    return codes, R, c, o
+
+
+def window(codes, R, c, bits, gate, q, k, v, a, b, return_state=False):
+    """One window (W = len(b) tokens) on one unit. Returns (codes, R, c, o[W, dv][, S])."""
+    codes = _c(codes, np.int8).copy()
+    R = _c(R, np.float32).copy()
+    c = _c(c, np.float32).copy()
+    bb = _c(bits, np.uint8)
+    dv, dk = codes.shape
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    a = _c(a, np.float32)
+    b = _c(b, np.float32)
+    W = b.shape[0]
+    o = np.zeros((W, dv), np.float32)
+    S_end = np.zeros((dv, dk), np.float32) if return_state else None
+    lib().oref_window(dv, dk, gate, _p(bb), _p(codes), _p(R), _p(c), W, _p(q), _p(k),
+                      _p(v), _p(a), _p(b), _p(o), _p(S_end))
+    if return_state:
+        return codes, R, c, o, S_end
+    return codes, R, c, o
+
+
+def recur_fp64(S: np.ndarray, gate, q, k, v, a, b):
+    """One unquantized fp64 step, in place on S (float64 [dv, dk]); returns o."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    dv, dk = S.shape
+    o = np.zeros(dv, np.float32)
+    lib().oref_recur_fp64(dv, dk, gate, _p(S), _p(_c(q, np.float32)), _p(_c(k, np.float32)),
+                          _p(_c(v, np.float32)), _p(_c(np.atleast_1d(a), np.float32)),
+                          float(b), _p(o))
+    return o
+
+
+# ---------------------------------------------------------------------------
+# pool interface (the packed layout the product library uses)
+# ---------------------------------------------------------------------------
+
+class Pool:
+    """Host copy of a packed state pool: packed[n_req, req_bytes], scales, bit map."""
+
+    def __init__(self, n_req, n_head, bits, dv=128, dk=128):
+        self.n_req, self.n_head, self.dv, self.dk = n_req, n_head, dv, dk
+        self.bits = _c(bits, np.uint8).reshape(n_head, dk)
+        rb = lib().oref_request_bytes(n_head, dv, dk, _p(self.bits))
+        if rb < 0:
+            raise ValueError("bit map not representable")
+        self.req_bytes = int(rb)
+        self.packed = np.zeros((n_req, self.req_bytes), np.uint8)
+        self.row_scale = np.zeros((n_req, n_head, dk), np.float32)
+        self.col_scale = np.zeros((n_req, n_head, dv), np.float32)
+
+    def copy(self):
+        p = Pool.__new__(Pool)
+        p.__dict__.update(self.__dict__)
+        p.packed = self.packed.copy()
+        p.row_scale = self.row_scale.copy()
+        p.col_scale = self.col_scale.copy()
+        return p
+
+    def quantize(self, S: np.ndarray):
+        S = _c(S, np.float32)
+        assert S.shape == (self.n_req, self.n_head, self.dv, self.dk)
+        rc = lib().oref_quantize_pool(self.n_req, self.n_head, self.dv, self.dk,
+                                      _p(self.bits), _p(S), _p(self.packed),
+                                      _p(self.row_scale), _p(self.col_scale))
+        if rc:
+            raise RuntimeError("oref_quantize_pool failed")
+
+    def dequantize(self) -> np.ndarray:
+        S = np.zeros((self.n_req, self.n_head, self.dv, self.dk), np.float32)
+        rc = lib().oref_dequantize_pool(self.n_req, self.n_head, self.dv, self.dk,
+                                        _p(self.bits), _p(self.packed), _p(self.row_scale),
+                                        _p(self.col_scale), _p(S))
+        if rc:
+            raise RuntimeError("oref_dequantize_pool failed")
+        return S
+
+    def step(self, gate, q, k, v, a, b, u0=0, u1=None):
+        """One decode step on units [u0, u1) in place; returns o [n_req, n_head, dv]."""
+        n_unit = self.n_req * self.n_head
+        u1 = n_unit if u1 is None else u1
+        o = np.zeros((self.n_req, self.n_head, self.dv), np.float32)
+        q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        rc = lib().oref_step_pool(self.n_req, self.n_head, self.dv, self.dk, gate,
+                                  _p(self.bits), _p(self.packed), _p(self.row_scale),
+                                  _p(self.col_scale), _p(q), _p(k), _p(v), _p(a), _p(b),
+                                  _p(o), u0, u1)
+        if rc:
+            raise RuntimeError("oref_step_pool failed")
+        return o
+
+    def window(self, gate, q, k, v, a, b, u0=0, u1=None):
+        """One window over W tokens (inputs [W, n_req, n_head, ...]); returns o."""
+        n_unit = self.n_req * self.n_head
+        u1 = n_unit if u1 is None else u1
+        q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        W = b.shape[0]
+        o = np.zeros((W, self.n_req, self.n_head, self.dv), np.float32)
+        rc = lib().oref_window_pool(self.n_req, self.n_head, self.dv, self.dk, gate,
+                                    _p(self.bits), _p(self.packed), _p(self.row_scale),
+                                    _p(self.col_scale), W, _p(q), _p(k), _p(v), _p(a),
+                                    _p(b), _p(o), u0, u1)
+        if rc:
+            raise RuntimeError("oref_window_pool failed")
+        return o

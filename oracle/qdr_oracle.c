@@ -1,0 +1,475 @@
+/*
+ * qdr_oracle.c -- plain scalar CPU oracle (TEST INFRASTRUCTURE; see qdr_oracle.h).
+ *
+ * Written for readability against the pages, not for speed: scalar loops, one IEEE
+ * rounding per written operation, no blocking, no reordering. Build with
+ *   gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared -lm
+ */
+#include "qdr_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int qmax_of(int bits) { return (1 << (bits - 1)) - 1; }
+static int valid_bits(int b) { return b == 4 || b == 6 || b == 8; }
+
+/* ------------------------------------------------------------------------------
+ * S0. Lifetime-based precision map. [STEP] Fig. 1(b): longer gate half-life means
+ * larger accumulated state error; Fig. 4 / Figure B1: units ordered by increasing
+ * half-life, the longest-lived quarter carries most of the error. [ABS] STEPQuant
+ * abstract: precision follows error magnitude and memory lifetime. Reading: shortest
+ * quarter 4 bits, longest quarter 8 bits, middle half 6 bits (nominal 6.0 bits).
+ * ---------------------------------------------------------------------------- */
+typedef struct { double tau; int idx; } rank_item;
+
+static int cmp_rank(const void *pa, const void *pb) {
+    const rank_item *a = (const rank_item *)pa, *b = (const rank_item *)pb;
+    if (a->tau < b->tau) return -1;
+    if (a->tau > b->tau) return 1;
+    return (a->idx > b->idx) - (a->idx < b->idx);
+}
+
+static void quartile_bits(int n, const double *tau, uint8_t *out) {
+    rank_item *it = (rank_item *)malloc(sizeof(rank_item) * (size_t)n);
+    for (int i = 0; i < n; ++i) { it[i].tau = tau[i]; it[i].idx = i; }
+    qsort(it, (size_t)n, sizeof(rank_item), cmp_rank);
+    int quarter = n / 4;
+    for (int r = 0; r < n; ++r) {
+        uint8_t b = 6;
+        if (r < quarter) b = 4;
+        else if (r >= n - quarter) b = 8;
+        out[it[r].idx] = b;
+    }
+    free(it);
+}
+
+int oref_assign_bits(int gate, int n_head, int dk, const double *halflife, uint8_t *bits_out) {
+    if (n_head <= 0 || dk <= 0 || !halflife || !bits_out) return -1;
+    if (gate == OREF_GDN) {
+        uint8_t *hb = (uint8_t *)malloc((size_t)n_head);
+        quartile_bits(n_head, halflife, hb);
+        for (int h = 0; h < n_head; ++h)
+            for (int j = 0; j < dk; ++j) bits_out[h * dk + j] = hb[h];
+        free(hb);
+        return 0;
+    }
+    if (gate == OREF_KDA) {
+        for (int h = 0; h < n_head; ++h) quartile_bits(dk, halflife + (size_t)h * dk, bits_out + (size_t)h * dk);
+        return 0;
+    }
+    return -1;
+}
+
+/* ------------------------------------------------------------------------------
+ * Packed tile format. [MEAS] counts packed codes, scales and precision maps as the
+ * state's memory; [STEP] Key contributions: mixed widths per unit. The format itself
+ * is this project's own (the pages do not print one):
+ *  - physical key order = channels sorted by width 8, 6, 4, ties by channel index;
+ *  - segment s = physical positions 32s..32s+31, all of one width b_s;
+ *  - segment s stores dv value rows, row i = 32 codes x b_s bits = 4*b_s bytes,
+ *    segments concatenated, rows in order inside a segment;
+ *  - inside a row the code of position 32s+m occupies bits [m*b, m*b+b) of the row's
+ *    little-endian bit stream (bit t lives in byte t/8 at bit t%8);
+ *  - each field holds the offset-binary value code + 2^(b-1).
+ * ---------------------------------------------------------------------------- */
+long oref_layout(int dv, int dk, const uint8_t *bits, uint8_t *perm, uint8_t *seg_bits) {
+    if (dv <= 0 || dk <= 0 || (dk % 32) != 0 || !bits) return -1;
+    static const int widths[3] = {8, 6, 4};
+    int p = 0;
+    long bytes = 0;
+    for (int w = 0; w < 3; ++w) {
+        int count = 0;
+        for (int j = 0; j < dk; ++j) {
+            if (!valid_bits(bits[j])) return -1;
+            if (bits[j] == widths[w]) {
+                if (perm) perm[p] = (uint8_t)j;
+                ++p;
+                ++count;
+            }
+        }
+        if (count % 32) return -1;
+        for (int s = 0; s < count / 32; ++s) {
+            if (seg_bits) seg_bits[(p - count) / 32 + s] = (uint8_t)widths[w];
+        }
+        bytes += (long)dv * count * widths[w] / 8;
+    }
+    return bytes;
+}
+
+static void put_bits(uint8_t *row, int bitpos, int nbits, unsigned value) {
+    for (int t = 0; t < nbits; ++t) {
+        int pos = bitpos + t;
+        unsigned bit = (value >> t) & 1u;
+        row[pos / 8] = (uint8_t)((row[pos / 8] & ~(1u << (pos % 8))) | (bit << (pos % 8)));
+    }
+}
+
+static unsigned get_bits(const uint8_t *row, int bitpos, int nbits) {
+    unsigned v = 0;
+    for (int t = 0; t < nbits; ++t) {
+        int pos = bitpos + t;
+        v |= (unsigned)((row[pos / 8] >> (pos % 8)) & 1u) << t;
+    }
+    return v;
+}
+
+int oref_pack(int dv, int dk, const uint8_t *bits, const int8_t *codes, uint8_t *tile) {
+    uint8_t perm[256], seg[8];
+    if (dk > 256) return -1;
+    long total = oref_layout(dv, dk, bits, perm, seg);
+    if (total < 0) return -1;
+    memset(tile, 0, (size_t)total);
+    long off = 0;
+    for (int s = 0; s < dk / 32; ++s) {
+        int b = seg[s];
+        int row_bytes = 4 * b;
+        for (int i = 0; i < dv; ++i) {
+            uint8_t *row = tile + off + (long)i * row_bytes;
+            for (int m = 0; m < 32; ++m) {
+                int j = perm[32 * s + m];
+                int code = codes[(size_t)i * dk + j];
+                int qm = qmax_of(b);
+                if (code < -qm || code > qm) return -1;
+                put_bits(row, m * b, b, (unsigned)(code + (1 << (b - 1))));
+            }
+        }
+        off += (long)dv * row_bytes;
+    }
+    return 0;
+}
+
+int oref_unpack(int dv, int dk, const uint8_t *bits, const uint8_t *tile, int8_t *codes) {
+    uint8_t perm[256], seg[8];
+    if (dk > 256) return -1;
+    if (oref_layout(dv, dk, bits, perm, seg) < 0) return -1;
+    long off = 0;
+    for (int s = 0; s < dk / 32; ++s) {
+        int b = seg[s];
+        int row_bytes = 4 * b;
+        for (int i = 0; i < dv; ++i) {
+            const uint8_t *row = tile + off + (long)i * row_bytes;
+            for (int m = 0; m < 32; ++m) {
+                int j = perm[32 * s + m];
+                int field = (int)get_bits(row, m * b, b);
+                codes[(size_t)i * dk + j] = (int8_t)(field - (1 << (b - 1)));
+            }
+        }
+        off += (long)dv * row_bytes;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------
+ * Scale refit and requantization. [ABS] STEPQuant abstract: key-row and value-column
+ * scales fitted jointly to the state distribution; [STEP] Fig. 5 / Figure B2: the
+ * state has outliers along both rows and columns. Reading (two-stage absmax, key axis
+ * first, the key row's bit range carried by its scale):
+ *   A_j = max_i |S_ij| (1 if 0),  R_j = A_j / Qmax_j,  y_ij = S_ij * (1/A_j),
+ *   c_i = max_j |y_ij| (1 if 0),  code_ij = RNE(y_ij * (Qmax_j * (1/c_i))),
+ * with the last product exact (fp64) before the single round-half-even.
+ * ---------------------------------------------------------------------------- */
+void oref_quantize(int dv, int dk, const uint8_t *bits, const float *S, int8_t *codes,
+                   float *R, float *c) {
+    float *invA = (float *)malloc(sizeof(float) * (size_t)dk);
+    for (int j = 0; j < dk; ++j) {
+        float A = 0.0f;
+        for (int i = 0; i < dv; ++i) {
+            float m = fabsf(S[(size_t)i * dk + j]);
+            if (m > A) A = m;
+        }
+        if (A == 0.0f) A = 1.0f;
+        R[j] = A / (float)qmax_of(bits[j]);
+        invA[j] = 1.0f / A;
+    }
+    for (int i = 0; i < dv; ++i) {
+        float cm = 0.0f;
+        for (int j = 0; j < dk; ++j) {
+            float y = S[(size_t)i * dk + j] * invA[j];
+            if (fabsf(y) > cm) cm = fabsf(y);
+        }
+        if (cm == 0.0f) cm = 1.0f;
+        c[i] = cm;
+        float invc = 1.0f / cm;
+        for (int j = 0; j < dk; ++j) {
+            int qm = qmax_of(bits[j]);
+            float y = S[(size_t)i * dk + j] * invA[j];
+            float M = (float)qm * invc;
+            double t = rint((double)y * (double)M); /* exact product, one RNE rounding */
+            if (t > qm) t = qm;
+            if (t < -qm) t = -qm;
+            codes[(size_t)i * dk + j] = (int8_t)t;
+        }
+    }
+    free(invA);
+}
+
+void oref_dequantize(int dv, int dk, const int8_t *codes, const float *R, const float *c,
+                     float *S) {
+    for (int i = 0; i < dv; ++i)
+        for (int j = 0; j < dk; ++j) {
+            float p = (float)codes[(size_t)i * dk + j] * R[j];
+            S[(size_t)i * dk + j] = p * c[i];
+        }
+}
+
+/* ------------------------------------------------------------------------------
+ * One decode step. [DEV] running-sum section: S <- S(I - k k^T) + v k^T; with the gate
+ * and the write strength (GDN scalar gate / KDA per-channel gate, [ABS] DASC abstract):
+ *   S_new = S diag(a) (I - b k k^T) + b v k^T = S' + w k^T,
+ *   S' = S diag(a) (KDA) or a S (GDN),  u = S' k,  w = b (v - u),  o = S_new q.
+ * S' is the dequantized state with the gate folded into a scale:
+ *   GDN: cf_j = R_j, rf_i = fl(a c_i);  KDA: cf_j = fl(a_j R_j), rf_i = c_i;
+ *   S'_ij = fl(fl(code_ij cf_j) rf_i).
+ * u_i is the exact dequantized-and-gated row times k, accumulated in fp64 and rounded
+ * once: u_i = fl32(rf_i * sum_j code_ij (cf_j k_j)).
+ * S_new_ij = fma(w_i, k_j, S'_ij) (one rounding); o_i = fl32(sum_j S_new_ij q_j) in fp64.
+ * The new state is then refit and requantized (oref_quantize).
+ * ---------------------------------------------------------------------------- */
+void oref_step(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
+               float *c, const float *q, const float *k, const float *v, const float *a,
+               float b, float *o, float *S_new_out) {
+    float *cf = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *rf = (float *)malloc(sizeof(float) * (size_t)dv);
+    float *w = (float *)malloc(sizeof(float) * (size_t)dv);
+    float *Sn = (float *)malloc(sizeof(float) * (size_t)dv * dk);
+
+    for (int j = 0; j < dk; ++j) cf[j] = (gate == OREF_KDA) ? a[j] * R[j] : R[j];
+    for (int i = 0; i < dv; ++i) rf[i] = (gate == OREF_GDN) ? a[0] * c[i] : c[i];
+
+    /* u = S' k and w = b (v - u) */
+    for (int i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dk; ++j)
+            acc += (double)codes[(size_t)i * dk + j] * ((double)cf[j] * (double)k[j]);
+        float u = (float)((double)rf[i] * acc);
+        w[i] = b * (v[i] - u);
+    }
+    /* S_new = S' + w k^T */
+    for (int i = 0; i < dv; ++i)
+        for (int j = 0; j < dk; ++j) {
+            float p = (float)codes[(size_t)i * dk + j] * cf[j];
+            float sp = p * rf[i];
+            Sn[(size_t)i * dk + j] = fmaf(w[i], k[j], sp);
+        }
+    /* o = S_new q */
+    for (int i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dk; ++j) acc += (double)Sn[(size_t)i * dk + j] * (double)q[j];
+        o[i] = (float)acc;
+    }
+    if (S_new_out) memcpy(S_new_out, Sn, sizeof(float) * (size_t)dv * dk);
+    oref_quantize(dv, dk, bits, Sn, codes, R, c);
+
+    free(cf);
+    free(rf);
+    free(w);
+    free(Sn);
+}
+
+/* ------------------------------------------------------------------------------
+ * Unquantized recurrence, fp64 (same algebra as oref_step without quantization).
+ * ---------------------------------------------------------------------------- */
+void oref_recur_fp64(int dv, int dk, int gate, double *S, const float *q, const float *k,
+                     const float *v, const float *a, float b, float *o) {
+    for (int i = 0; i < dv; ++i)
+        for (int j = 0; j < dk; ++j)
+            S[(size_t)i * dk + j] *= (gate == OREF_KDA) ? (double)a[j] : (double)a[0];
+    for (int i = 0; i < dv; ++i) {
+        double u = 0.0;
+        for (int j = 0; j < dk; ++j) u += S[(size_t)i * dk + j] * (double)k[j];
+        double wi = (double)b * ((double)v[i] - u);
+        for (int j = 0; j < dk; ++j) S[(size_t)i * dk + j] += wi * (double)k[j];
+    }
+    if (o) {
+        for (int i = 0; i < dv; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * (double)q[j];
+            o[i] = (float)acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------------
+ * Window mode. [ABS] LeapQuant abstract: keep the state low-bit across a window of
+ * tokens, compute each output from the fixed low-bit state plus high-precision
+ * buffered updates, quantize once at the window end. Semantically the outputs are
+ * those of the exact recurrence started from the dequantized state; this function
+ * runs that recurrence directly (fp64) and requantizes at the end.
+ * ---------------------------------------------------------------------------- */
+void oref_window(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
+                 float *c, int W, const float *q, const float *k, const float *v,
+                 const float *a, const float *b, float *o, float *S_end) {
+    float *Sh = (float *)malloc(sizeof(float) * (size_t)dv * dk);
+    double *S = (double *)malloc(sizeof(double) * (size_t)dv * dk);
+    oref_dequantize(dv, dk, codes, R, c, Sh);
+    for (size_t e = 0; e < (size_t)dv * dk; ++e) S[e] = (double)Sh[e];
+    for (int t = 0; t < W; ++t) {
+        const float *at = (gate == OREF_KDA) ? a + (size_t)t * dk : a + t;
+        oref_recur_fp64(dv, dk, gate, S, q + (size_t)t * dk, k + (size_t)t * dk,
+                        v + (size_t)t * dv, at, b[t], o + (size_t)t * dv);
+    }
+    for (size_t e = 0; e < (size_t)dv * dk; ++e) Sh[e] = (float)S[e];
+    if (S_end) memcpy(S_end, Sh, sizeof(float) * (size_t)dv * dk);
+    oref_quantize(dv, dk, bits, Sh, codes, R, c);
+    free(Sh);
+    free(S);
+}
+
+/* ------------------------------------------------------------------------------
+ * Batched drivers over the packed pool ([MEAS] per-request packed pages).
+ * ---------------------------------------------------------------------------- */
+long oref_request_bytes(int n_head, int dv, int dk, const uint8_t *bits) {
+    long total = 0;
+    for (int h = 0; h < n_head; ++h) {
+        long t = oref_layout(dv, dk, bits + (size_t)h * dk, NULL, NULL);
+        if (t < 0) return -1;
+        total += t;
+    }
+    return total;
+}
+
+typedef struct {
+    long req_bytes;
+    long *head_off;
+    uint8_t *perm; /* [n_head][dk] */
+} pool_geom;
+
+static int geom_init(pool_geom *g, int n_head, int dv, int dk, const uint8_t *bits) {
+    g->head_off = (long *)malloc(sizeof(long) * (size_t)n_head);
+    g->perm = (uint8_t *)malloc((size_t)n_head * dk);
+    long off = 0;
+    for (int h = 0; h < n_head; ++h) {
+        long t = oref_layout(dv, dk, bits + (size_t)h * dk, g->perm + (size_t)h * dk, NULL);
+        if (t < 0) return -1;
+        g->head_off[h] = off;
+        off += t;
+    }
+    g->req_bytes = off;
+    return 0;
+}
+
+static void geom_free(pool_geom *g) {
+    free(g->head_off);
+    free(g->perm);
+}
+
+/* physical-order scales <-> logical-order scales */
+static void scales_to_logical(int dk, const uint8_t *perm, const float *phys, float *logical) {
+    for (int p = 0; p < dk; ++p) logical[perm[p]] = phys[p];
+}
+static void scales_to_physical(int dk, const uint8_t *perm, const float *logical, float *phys) {
+    for (int p = 0; p < dk; ++p) phys[p] = logical[perm[p]];
+}
+
+int oref_quantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                       const float *S, uint8_t *packed, float *row_scale, float *col_scale) {
+    pool_geom g;
+    if (geom_init(&g, n_head, dv, dk, bits)) { geom_free(&g); return -1; }
+    int8_t *codes = (int8_t *)malloc((size_t)dv * dk);
+    float *R = (float *)malloc(sizeof(float) * (size_t)dk);
+    for (int r = 0; r < n_req; ++r)
+        for (int h = 0; h < n_head; ++h) {
+            size_t u = (size_t)r * n_head + h;
+            const uint8_t *bh = bits + (size_t)h * dk;
+            oref_quantize(dv, dk, bh, S + u * dv * dk, codes, R, col_scale + u * dv);
+            scales_to_physical(dk, g.perm + (size_t)h * dk, R, row_scale + u * dk);
+            oref_pack(dv, dk, bh, codes, packed + (size_t)r * g.req_bytes + g.head_off[h]);
+        }
+    free(codes);
+    free(R);
+    geom_free(&g);
+    return 0;
+}
+
+int oref_dequantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                         const uint8_t *packed, const float *row_scale,
+                         const float *col_scale, float *S) {
+    pool_geom g;
+    if (geom_init(&g, n_head, dv, dk, bits)) { geom_free(&g); return -1; }
+    int8_t *codes = (int8_t *)malloc((size_t)dv * dk);
+    float *R = (float *)malloc(sizeof(float) * (size_t)dk);
+    for (int r = 0; r < n_req; ++r)
+        for (int h = 0; h < n_head; ++h) {
+            size_t u = (size_t)r * n_head + h;
+            const uint8_t *bh = bits + (size_t)h * dk;
+            oref_unpack(dv, dk, bh, packed + (size_t)r * g.req_bytes + g.head_off[h], codes);
+            scales_to_logical(dk, g.perm + (size_t)h * dk, row_scale + u * dk, R);
+            oref_dequantize(dv, dk, codes, R, col_scale + u * dv, S + u * dv * dk);
+        }
+    free(codes);
+    free(R);
+    geom_free(&g);
+    return 0;
+}
+
+int oref_step_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
+                   uint8_t *packed, float *row_scale, float *col_scale, const float *q,
+                   const float *k, const float *v, const float *a, const float *b, float *o,
+                   long u0, long u1) {
+    pool_geom g;
+    if (geom_init(&g, n_head, dv, dk, bits)) { geom_free(&g); return -1; }
+    int8_t *codes = (int8_t *)malloc((size_t)dv * dk);
+    float *R = (float *)malloc(sizeof(float) * (size_t)dk);
+    for (long u = u0; u < u1; ++u) {
+        int r = (int)(u / n_head), h = (int)(u % n_head);
+        const uint8_t *bh = bits + (size_t)h * dk;
+        const uint8_t *perm = g.perm + (size_t)h * dk;
+        uint8_t *tile = packed + (size_t)r * g.req_bytes + g.head_off[h];
+        const float *au = (gate == OREF_KDA) ? a + (size_t)u * dk : a + u;
+        oref_unpack(dv, dk, bh, tile, codes);
+        scales_to_logical(dk, perm, row_scale + (size_t)u * dk, R);
+        oref_step(dv, dk, gate, bh, codes, R, col_scale + (size_t)u * dv, q + (size_t)u * dk,
+                  k + (size_t)u * dk, v + (size_t)u * dv, au, b[u], o + (size_t)u * dv, NULL);
+        scales_to_physical(dk, perm, R, row_scale + (size_t)u * dk);
+        oref_pack(dv, dk, bh, codes, tile);
+    }
+    free(codes);
+    free(R);
+    geom_free(&g);
+    return 0;
+}
+
+int oref_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
+                     uint8_t *packed, float *row_scale, float *col_scale, int W,
+                     const float *q, const float *k, const float *v, const float *a,
+                     const float *b, float *o, long u0, long u1) {
+    pool_geom g;
+    if (geom_init(&g, n_head, dv, dk, bits)) { geom_free(&g); return -1; }
+    size_t n_unit = (size_t)n_req * n_head;
+    size_t a_len = (gate == OREF_KDA) ? (size_t)dk : 1;
+    int8_t *codes = (int8_t *)malloc((size_t)dv * dk);
+    float *R = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *tq = (float *)malloc(sizeof(float) * (size_t)W * dk);
+    float *tk = (float *)malloc(sizeof(float) * (size_t)W * dk);
+    float *tv = (float *)malloc(sizeof(float) * (size_t)W * dv);
+    float *ta = (float *)malloc(sizeof(float) * (size_t)W * a_len);
+    float *tb = (float *)malloc(sizeof(float) * (size_t)W);
+    float *to = (float *)malloc(sizeof(float) * (size_t)W * dv);
+    for (long u = u0; u < u1; ++u) {
+        int r = (int)(u / n_head), h = (int)(u % n_head);
+        const uint8_t *bh = bits + (size_t)h * dk;
+        const uint8_t *perm = g.perm + (size_t)h * dk;
+        uint8_t *tile = packed + (size_t)r * g.req_bytes + g.head_off[h];
+        for (int t = 0; t < W; ++t) {
+            size_t base = (size_t)t * n_unit + (size_t)u;
+            memcpy(tq + (size_t)t * dk, q + base * dk, sizeof(float) * (size_t)dk);
+            memcpy(tk + (size_t)t * dk, k + base * dk, sizeof(float) * (size_t)dk);
+            memcpy(tv + (size_t)t * dv, v + base * dv, sizeof(float) * (size_t)dv);
+            memcpy(ta + (size_t)t * a_len, a + base * a_len, sizeof(float) * a_len);
+            tb[t] = b[base];
+        }
+        oref_unpack(dv, dk, bh, tile, codes);
+        scales_to_logical(dk, perm, row_scale + (size_t)u * dk, R);
+        oref_window(dv, dk, gate, bh, codes, R, col_scale + (size_t)u * dv, W, tq, tk, tv, ta,
+                    tb, to, NULL);
+        scales_to_physical(dk, perm, R, row_scale + (size_t)u * dk);
+        oref_pack(dv, dk, bh, codes, tile);
+        for (int t = 0; t < W; ++t)
+            memcpy(o + ((size_t)t * n_unit + (size_t)u) * dv, to + (size_t)t * dv,
+                   sizeof(float) * (size_t)dv);
+    }
+    free(codes); free(R); free(tq); free(tk); free(tv); free(ta); free(tb); free(to);
+    geom_free(&g);
+    return 0;
+}
