@@ -1,0 +1,157 @@
+/*
+ * qdr.h -- C ABI of libqdr: the per-token decode step of a Delta-rule linear-attention
+ * layer over a low-bit quantized recurrent state, on one MI355X (gfx950).
+ *
+ * Every (request, head) pair is one "unit": a state S in R^{dv x dk}, dv = dk = 128,
+ * row i = value index, column j = key channel, readout o = S q. The pages' "key row j"
+ * is column j of S and their "value column i" is row i of S.
+ *
+ * Sources, cited by page title and section:
+ *  - dev.to, "Uniform INT8 on recurrent states is a default, not a decision", section
+ *    "The state is a running sum, not a buffer": the Delta-rule update
+ *    S <- S (I - k k^T) + v k^T.
+ *  - thelatestinai page titled "DAMP: Decay-Aware Mixed-Precision Recurrent-State
+ *    Quantization": the STEPQuant abstract (precision by error and memory lifetime;
+ *    key-row and value-column scales), the LeapQuant abstract (per-window quantization:
+ *    outputs from the fixed low-bit state plus high-precision buffered updates, one
+ *    quantization at the window end) and the DASC abstract (GDN decays per head, KDA per
+ *    key channel).
+ *  - "STEPQuant: When and Where Errors Matter in Delta-Rule Recurrent State
+ *    Quantization" (signal-papers page): Fig. 1(b) and Fig. 4 / Figure B1 (gate
+ *    half-life orders the units; the longest-lived quarter matters most), Fig. 5 /
+ *    Figure B2 (128x128 states with row and column outliers).
+ *  - freedom251, "Recurrent-state INT8 quantization: measure before you make it the
+ *    default", section "Memory and speed gains are implementation-specific": per-request
+ *    packed pages; the checklist under "How to decide for a deployment" counts codes,
+ *    scales and precision maps as state memory.
+ *
+ * Conventions shared by every entry point
+ *  - Return value: QDR_OK (0) or a negative QDR_E* code. On error nothing is launched
+ *    and qdr_last_error() (thread-local) describes the failure. No exception crosses
+ *    the ABI.
+ *  - Pointers: every array argument is a DEVICE pointer (memory of the GPU current on
+ *    the calling thread) except qdr_desc.bits and the host arrays of qdr_assign_bits /
+ *    qdr_state_bytes, which are HOST pointers. Device arrays must be 16-byte aligned
+ *    and contiguous in the stated layout. The caller owns every buffer and the stream;
+ *    the library allocates, frees and synchronizes nothing on these paths.
+ *  - stream: a hipStream_t passed as void* (NULL = the null stream). All device work
+ *    is enqueued asynchronously on it in call order.
+ *  - Non-finite inputs are undefined behaviour and are not checked.
+ *  - Layouts (all fp32, row-major):
+ *      q, k        [n_req][n_head][dk]   logical key-channel order
+ *      v, o        [n_req][n_head][dv]
+ *      a (GDN)     [n_req][n_head]       scalar gate
+ *      a (KDA)     [n_req][n_head][dk]   per-key-channel gate, logical order
+ *      b           [n_req][n_head]       write strength
+ *      row_scale   [n_req][n_head][dk]   key-row scales R_j, PHYSICAL key order
+ *      col_scale   [n_req][n_head][dv]   value-column scales c_i
+ *      packed      [n_req][req_bytes]    heads concatenated inside a request
+ *  - Packed tile of one head: key channels sorted by width (8, 6, 4; ties by index)
+ *    give the physical order; physical positions 32s..32s+31 form segment s (one
+ *    width b_s); segment s stores dv rows of 32 codes, each row 4*b_s bytes, code of
+ *    position 32s+m in bits [m*b, m*b+b) of the row's little-endian bit stream, as the
+ *    offset-binary field code + 2^(b-1). Tile bytes = 16 * sum_j bits_j.
+ */
+#ifndef QDR_H
+#define QDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QDR_OK 0
+#define QDR_EINVAL (-1)       /* null / negative / inconsistent argument            */
+#define QDR_EUNSUPPORTED (-2) /* dims != 128, bits not in {4,6,8}, bad width counts,  */
+                              /* window position out of range                       */
+#define QDR_EALIGN (-3)       /* a device pointer is not 16-byte aligned              */
+#define QDR_EHIP (-4)         /* HIP launch or runtime error (text in last_error)     */
+
+#define QDR_GATE_GDN 0 /* scalar gate per (request, head) */
+#define QDR_GATE_KDA 1 /* diagonal gate, one value per key channel */
+
+typedef struct qdr_desc {
+    int32_t n_req;        /* requests (>= 0; 0 makes every call a no-op)            */
+    int32_t n_head;       /* heads per request (1..1024)                            */
+    int32_t dk, dv;       /* must both be 128                                       */
+    int32_t gate;         /* QDR_GATE_GDN or QDR_GATE_KDA                           */
+    const uint8_t *bits;  /* HOST [n_head][dk], each in {4,6,8}; per head, the count */
+                          /* of channels of each width is a multiple of 32           */
+    int32_t window;       /* W >= 1 for qdr_decode_window, 0 otherwise               */
+} qdr_desc;
+
+/* S0 -- lifetime-based bit map (STEPQuant abstract; STEPQuant page Fig. 1(b), Fig. 4 /
+ * Figure B1). HOST only. Units ranked by (half-life, index) ascending: the shortest
+ * floor(n/4) get 4 bits, the longest floor(n/4) get 8 bits, the rest 6 bits.
+ *   GDN: halflife[n_head], the unit is a head (all its channels share the width).
+ *   KDA: halflife[n_head][dk], units are the key channels of each head.
+ * bits_out: HOST [n_head][dk]. Errors: QDR_EINVAL. */
+int qdr_assign_bits(int32_t gate, int32_t n_head, int32_t dk, const double *halflife,
+                    uint8_t *bits_out);
+
+/* Sizes of the caller-owned buffers for a descriptor (HOST outputs, any may be NULL):
+ *   packed  -- n_req * req_bytes bytes (codes)
+ *   scales  -- bytes of ONE of row_scale / col_scale (n_req*n_head*128*4)
+ *   meta    -- bytes of the device metadata table written by qdr_init_state
+ *   window_buf -- bytes of the window buffer (0 when desc->window == 0)
+ * Errors: QDR_EINVAL, QDR_EUNSUPPORTED. */
+int qdr_state_bytes(const qdr_desc *desc, size_t *packed, size_t *scales, size_t *meta,
+                    size_t *window_buf);
+
+/* Initialise: write the metadata table (per-head tile offsets, segment widths and the
+ * physical key order) and the zero state (every code 0, R_j = 1/Qmax_j, c_i = 1),
+ * i.e. the state that qdr_quantize_state gives for S = 0. Errors: all codes. */
+int qdr_init_state(const qdr_desc *desc, void *packed, float *row_scale, float *col_scale,
+                   void *meta, void *stream);
+
+/* Refit scales and quantize a caller fp32 state S [n_req][n_head][dv][dk] (logical key
+ * order) into (packed, row_scale, col_scale): the scale rule of the STEPQuant abstract
+ * read as a two-stage absmax, key axis first:
+ *   A_j = max_i |S_ij| (1 if 0), R_j = A_j/Qmax_j, y_ij = S_ij*(1/A_j),
+ *   c_i = max_j |y_ij| (1 if 0), code_ij = RNE(y_ij * (Qmax_j*(1/c_i))).
+ * meta must come from qdr_init_state with the same descriptor. Errors: all codes. */
+int qdr_quantize_state(const qdr_desc *desc, const void *meta, const float *S,
+                       void *packed, float *row_scale, float *col_scale, void *stream);
+
+/* One decode step for every unit, in place on (packed, row_scale, col_scale):
+ * dequantize, apply the gated delta update
+ *   S <- S diag(a) (I - b k k^T) + b v k^T   (GDN: diag(a) = a I)
+ * (dev.to page, running-sum section; gate families per the DASC abstract), read out
+ * o = S q from the updated fp32 state, then refit the scales and requantize (same rule
+ * as qdr_quantize_state). Arithmetic: S'_ij = fl(fl(code*cf_j)*rf_i) with GDN
+ * cf_j = R_j, rf_i = fl(a c_i) and KDA cf_j = fl(a_j R_j), rf_i = c_i;
+ * u_i = fl32(rf_i * sum_j code_ij (cf_j k_j)) accumulated in fp64;
+ * w_i = fl(b fl(v_i - u_i)); S_new_ij = fma(w_i, k_j, S'_ij).
+ * Each unit is read completely before it is written, by one work-group, so in-place
+ * update is safe; calls on one stream are ordered. Errors: all codes. */
+int qdr_decode_step(const qdr_desc *desc, const void *meta, void *packed, float *row_scale,
+                    float *col_scale, const float *q, const float *k, const float *v,
+                    const float *a, const float *b, float *o, void *stream);
+
+/* One token of window mode (LeapQuant abstract): the packed state stays fixed for W
+ * tokens; token t (0 <= t < W, the same for all units) reads it plus the buffered
+ * high-precision updates of tokens 0..t-1 from window_buf, produces o_t, and appends
+ * its own update. At t = W-1 the buffered updates are folded into the state and the
+ * state is requantized once (same scale rule). window_buf is caller-owned, sized by
+ * qdr_state_bytes; its contents at t = 0 are ignored. Errors: all codes;
+ * QDR_EUNSUPPORTED if t is out of range or desc->window < 1. */
+int qdr_decode_window(const qdr_desc *desc, const void *meta, void *packed,
+                      float *row_scale, float *col_scale, void *window_buf, int32_t t,
+                      const float *q, const float *k, const float *v, const float *a,
+                      const float *b, float *o, void *stream);
+
+/* Read back the dequantized state S_hat_ij = fl(fl(code_ij*R_j)*c_i) as
+ * S_out [n_req][n_head][dv][dk] (logical key order). Errors: all codes. */
+int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *packed,
+                         const float *row_scale, const float *col_scale, float *S_out,
+                         void *stream);
+
+/* Text of the last error on the calling thread ("" if none). Never NULL. */
+const char *qdr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QDR_H */

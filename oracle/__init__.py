@@ -261,6 +261,29 @@ class Pool:
             raise RuntimeError("oref_step_pool failed")
         return o
 
+    def step_threads(self, gate, q, k, v, a, b, threads=8):
+        """``step`` over all units, split into contiguous unit ranges on host threads
+        (the C code releases the GIL; ranges are disjoint, so results are identical)."""
+        from concurrent.futures import ThreadPoolExecutor
+
+        n_unit = self.n_req * self.n_head
+        q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        o = np.zeros((self.n_req, self.n_head, self.dv), np.float32)
+        cuts = np.linspace(0, n_unit, max(1, min(threads, n_unit)) + 1).astype(int)
+
+        def run(i):
+            return lib().oref_step_pool(self.n_req, self.n_head, self.dv, self.dk, gate,
+                                        _p(self.bits), _p(self.packed), _p(self.row_scale),
+                                        _p(self.col_scale), _p(q), _p(k), _p(v), _p(a),
+                                        _p(b), _p(o), int(cuts[i]), int(cuts[i + 1]))
+
+        with ThreadPoolExecutor(len(cuts) - 1) as ex:
+            rcs = list(ex.map(run, range(len(cuts) - 1)))
+        if any(rcs):
+            raise RuntimeError("oref_step_pool failed")
+        return o
+
     def window(self, gate, q, k, v, a, b, u0=0, u1=None):
         """One window over W tokens (inputs [W, n_req, n_head, ...]); returns o."""
         n_unit = self.n_req * self.n_head

@@ -1,0 +1,286 @@
+// qdr_api.cpp -- C ABI of libqdr (declared in include/qdr.h): argument validation,
+// layout/metadata construction, kernel selection. No allocation, no synchronization.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/qdr.h"
+#include "qdr_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return QDR_OK;
+}
+
+// Host view of one head's layout (the same rules as the format in include/qdr.h).
+struct HeadLayout {
+  uint32_t tile_bytes;
+  uint8_t seg_bits[4];
+  uint8_t perm[qdr::kD];
+  bool identity;
+};
+
+int head_layout(const uint8_t* bits, HeadLayout* out, int h) {
+  static const int widths[3] = {8, 6, 4};
+  int p = 0;
+  uint32_t bytes = 0;
+  for (int wi = 0; wi < 3; ++wi) {
+    int count = 0;
+    for (int j = 0; j < qdr::kD; ++j) {
+      const int b = bits[j];
+      if (b != 4 && b != 6 && b != 8)
+        return fail(QDR_EUNSUPPORTED, "bits[%d][%d] = %d is not 4, 6 or 8", h, j, b);
+      if (b == widths[wi]) {
+        out->perm[p++] = (uint8_t)j;
+        ++count;
+      }
+    }
+    if (count % qdr::kSeg)
+      return fail(QDR_EUNSUPPORTED, "head %d has %d channels of width %d (not a multiple of 32)",
+                  h, count, widths[wi]);
+    bytes += (uint32_t)(qdr::kD * count * widths[wi] / 8);
+  }
+  for (int s = 0; s < 4; ++s) out->seg_bits[s] = bits[out->perm[s * qdr::kSeg]];
+  out->identity = true;
+  for (int q = 0; q < qdr::kD; ++q) out->identity = out->identity && out->perm[q] == q;
+  out->tile_bytes = bytes;
+  return QDR_OK;
+}
+
+struct Geometry {
+  std::vector<HeadLayout> heads;
+  std::vector<uint32_t> off;
+  uint32_t req_bytes = 0;
+};
+
+int check_desc(const qdr_desc* d, Geometry* g) {
+  if (!d) return fail(QDR_EINVAL, "desc is NULL");
+  if (d->n_req < 0) return fail(QDR_EINVAL, "n_req = %d < 0", d->n_req);
+  if (d->n_head < 1 || d->n_head > 1024)
+    return fail(QDR_EINVAL, "n_head = %d outside [1, 1024]", d->n_head);
+  if (d->dk != qdr::kD || d->dv != qdr::kD)
+    return fail(QDR_EUNSUPPORTED, "dk = %d, dv = %d: only 128 x 128 states are supported", d->dk,
+                d->dv);
+  if (d->gate != QDR_GATE_GDN && d->gate != QDR_GATE_KDA)
+    return fail(QDR_EINVAL, "gate = %d is neither GDN (0) nor KDA (1)", d->gate);
+  if (!d->bits) return fail(QDR_EINVAL, "desc->bits is NULL");
+  if (d->window < 0) return fail(QDR_EINVAL, "window = %d < 0", d->window);
+  if ((long long)d->n_req * d->n_head > (1LL << 31) - 1)
+    return fail(QDR_EINVAL, "n_req * n_head overflows");
+  if (g) {
+    g->heads.resize(d->n_head);
+    g->off.resize(d->n_head);
+    uint64_t off = 0;
+    for (int h = 0; h < d->n_head; ++h) {
+      int rc = head_layout(d->bits + (size_t)h * qdr::kD, &g->heads[h], h);
+      if (rc) return rc;
+      g->off[h] = (uint32_t)off;
+      off += g->heads[h].tile_bytes;
+    }
+    if (off > 0xFFFFFFFFull) return fail(QDR_EINVAL, "request too large");
+    g->req_bytes = (uint32_t)off;
+  }
+  return QDR_OK;
+}
+
+int check_ptr(const void* p, const char* name, bool required) {
+  if (!p) return required ? fail(QDR_EINVAL, "%s is NULL", name) : QDR_OK;
+  if (reinterpret_cast<uintptr_t>(p) & 15u)
+    return fail(QDR_EALIGN, "%s = %p is not 16-byte aligned", name, p);
+  return QDR_OK;
+}
+
+#define CHECK(expr)        \
+  do {                     \
+    int rc_ = (expr);      \
+    if (rc_) return rc_;   \
+  } while (0)
+
+qdr::Pool pool_of(const qdr_desc* d, const void* meta, const Geometry& g) {
+  qdr::Pool p;
+  p.meta = meta;
+  p.n_head = d->n_head;
+  p.n_unit = d->n_req * d->n_head;
+  p.req_bytes = g.req_bytes;
+  return p;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QDR_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+struct RankItem {
+  double tau;
+  int idx;
+};
+
+void quartile(int n, const double* tau, uint8_t* out) {
+  std::vector<RankItem> it(n);
+  for (int i = 0; i < n; ++i) it[i] = {tau[i], i};
+  std::stable_sort(it.begin(), it.end(),
+                   [](const RankItem& a, const RankItem& b) { return a.tau < b.tau; });
+  const int quarter = n / 4;
+  for (int r = 0; r < n; ++r)
+    out[it[r].idx] = (uint8_t)(r < quarter ? 4 : (r >= n - quarter ? 8 : 6));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qdr_assign_bits(int32_t gate, int32_t n_head, int32_t dk, const double* halflife,
+                    uint8_t* bits_out) {
+  if (n_head < 1 || dk < 1 || !halflife || !bits_out)
+    return fail(QDR_EINVAL, "qdr_assign_bits: bad arguments");
+  if (gate == QDR_GATE_GDN) {
+    std::vector<uint8_t> hb(n_head);
+    quartile(n_head, halflife, hb.data());
+    for (int h = 0; h < n_head; ++h) memset(bits_out + (size_t)h * dk, hb[h], (size_t)dk);
+    return ok();
+  }
+  if (gate == QDR_GATE_KDA) {
+    for (int h = 0; h < n_head; ++h)
+      quartile(dk, halflife + (size_t)h * dk, bits_out + (size_t)h * dk);
+    return ok();
+  }
+  return fail(QDR_EINVAL, "qdr_assign_bits: gate = %d", gate);
+}
+
+int qdr_state_bytes(const qdr_desc* d, size_t* packed, size_t* scales, size_t* meta,
+                    size_t* window_buf) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  const size_t n_unit = (size_t)d->n_req * d->n_head;
+  if (packed) *packed = (size_t)d->n_req * g.req_bytes;
+  if (scales) *scales = n_unit * qdr::kD * sizeof(float);
+  if (meta) *meta = sizeof(qdr::MetaHeader) + (size_t)d->n_head * sizeof(qdr::MetaHead);
+  if (window_buf) *window_buf = d->window > 0 ? n_unit * qdr::window_unit_bytes(d->window) : 0;
+  return ok();
+}
+
+int qdr_init_state(const qdr_desc* d, void* packed, float* row_scale, float* col_scale,
+                   void* meta, void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  std::vector<uint8_t> host(sizeof(qdr::MetaHeader) + (size_t)d->n_head * sizeof(qdr::MetaHead), 0);
+  auto* hdr = reinterpret_cast<qdr::MetaHeader*>(host.data());
+  hdr->magic = qdr::kMetaMagic;
+  hdr->n_head = (uint32_t)d->n_head;
+  hdr->dk = (uint32_t)d->dk;
+  hdr->dv = (uint32_t)d->dv;
+  hdr->gate = (uint32_t)d->gate;
+  hdr->req_bytes = g.req_bytes;
+  hdr->window = (uint32_t)d->window;
+  auto* mh = reinterpret_cast<qdr::MetaHead*>(host.data() + sizeof(qdr::MetaHeader));
+  for (int h = 0; h < d->n_head; ++h) {
+    mh[h].tile_off = g.off[h];
+    mh[h].tile_bytes = g.heads[h].tile_bytes;
+    memcpy(mh[h].seg_bits, g.heads[h].seg_bits, 4);
+    mh[h].identity = g.heads[h].identity ? 1u : 0u;
+    memcpy(mh[h].perm, g.heads[h].perm, qdr::kD);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the table is small; a synchronous copy keeps the host vector's lifetime simple
+  hipError_t e = hipMemcpyAsync(meta, host.data(), host.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "qdr_init_state: metadata copy");
+  return hip_status(qdr::launch_init(pool_of(d, meta, g), static_cast<uint8_t*>(packed),
+                                     row_scale, col_scale, s),
+                    "qdr_init_state: launch");
+}
+
+int qdr_quantize_state(const qdr_desc* d, const void* meta, const float* S, void* packed,
+                       float* row_scale, float* col_scale, void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(S, "S", any));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  return hip_status(qdr::launch_quantize(pool_of(d, meta, g), S, static_cast<uint8_t*>(packed),
+                                         row_scale, col_scale, static_cast<hipStream_t>(stream)),
+                    "qdr_quantize_state: launch");
+}
+
+int qdr_dequantize_state(const qdr_desc* d, const void* meta, const void* packed,
+                         const float* row_scale, const float* col_scale, float* S_out,
+                         void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(S_out, "S_out", any));
+  return hip_status(qdr::launch_dequantize(pool_of(d, meta, g),
+                                           static_cast<const uint8_t*>(packed), row_scale,
+                                           col_scale, S_out, static_cast<hipStream_t>(stream)),
+                    "qdr_dequantize_state: launch");
+}
+
+int qdr_decode_step(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
+                    float* col_scale, const float* q, const float* k, const float* v,
+                    const float* a, const float* b, float* o, void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(q, "q", any));
+  CHECK(check_ptr(k, "k", any));
+  CHECK(check_ptr(v, "v", any));
+  CHECK(check_ptr(a, "a", any));
+  CHECK(check_ptr(b, "b", any));
+  CHECK(check_ptr(o, "o", any));
+  return hip_status(qdr::launch_step(pool_of(d, meta, g), d->gate, static_cast<uint8_t*>(packed),
+                                     row_scale, col_scale, q, k, v, a, b, o,
+                                     static_cast<hipStream_t>(stream)),
+                    "qdr_decode_step: launch");
+}
+
+int qdr_decode_window(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
+                      float* col_scale, void* window_buf, int32_t t, const float* q,
+                      const float* k, const float* v, const float* a, const float* b,
+                      float* o, void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  if (d->window < 1) return fail(QDR_EUNSUPPORTED, "desc->window = %d: no window mode", d->window);
+  if (t < 0 || t >= d->window)
+    return fail(QDR_EUNSUPPORTED, "window position t = %d outside [0, %d)", t, d->window);
+  (void)meta; (void)packed; (void)row_scale; (void)col_scale; (void)window_buf;
+  (void)q; (void)k; (void)v; (void)a; (void)b; (void)o; (void)stream;
+  return fail(QDR_EUNSUPPORTED, "qdr_decode_window: not built yet");
+}
+
+const char* qdr_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

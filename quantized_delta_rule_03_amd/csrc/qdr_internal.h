@@ -1,0 +1,61 @@
+// qdr_internal.h -- shared between the C-ABI host layer and the gfx950 kernels of libqdr.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qdr {
+
+constexpr int kD = 128;          // dk = dv = 128 (STEPQuant page, Fig. 5 / Figure B2)
+constexpr int kSeg = 32;         // key positions per segment (one width per segment)
+constexpr int kThreads = 256;    // one work-group of 4 wave64 per (request, head) unit
+constexpr uint32_t kMetaMagic = 0x31524451u;  // "QDR1"
+
+// Device metadata table: a 64-byte header, then one MetaHead per head.
+struct MetaHeader {
+  uint32_t magic;
+  uint32_t n_head;
+  uint32_t dk, dv;
+  uint32_t gate;
+  uint32_t req_bytes;
+  uint32_t window;
+  uint32_t reserved[9];
+};
+static_assert(sizeof(MetaHeader) == 64, "meta header size");
+
+struct MetaHead {
+  uint32_t tile_off;    // byte offset of the head's tile inside a request
+  uint32_t tile_bytes;  // 16 * sum_j bits_j
+  uint8_t seg_bits[4];  // width of physical positions 32s..32s+31
+  uint32_t identity;    // 1 if the physical order is the logical order
+  uint8_t perm[kD];     // perm[p] = logical key channel at physical position p
+};
+static_assert(sizeof(MetaHead) == 144, "meta head size");
+
+__host__ __device__ inline const MetaHead* meta_heads(const void* meta) {
+  return reinterpret_cast<const MetaHead*>(static_cast<const uint8_t*>(meta) + sizeof(MetaHeader));
+}
+
+// Bytes of one window-buffer slot set per unit: W slots of (kappa[128], delta[128]) fp32
+// plus the running cumulative gate g[128] fp32.
+inline size_t window_unit_bytes(int W) { return (size_t)W * 2 * kD * 4 + (size_t)kD * 4; }
+
+struct Pool {
+  const void* meta;
+  int n_head;
+  int n_unit;
+  uint32_t req_bytes;
+};
+
+// Launchers (kernels.hip). All enqueue on `stream` and return hipGetLastError().
+hipError_t launch_init(const Pool& p, uint8_t* packed, float* rs, float* cs, hipStream_t s);
+hipError_t launch_quantize(const Pool& p, const float* S, uint8_t* packed, float* rs, float* cs,
+                           hipStream_t s);
+hipError_t launch_dequantize(const Pool& p, const uint8_t* packed, const float* rs,
+                             const float* cs, float* S, hipStream_t s);
+hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, float* cs,
+                       const float* q, const float* k, const float* v, const float* a,
+                       const float* b, float* o, hipStream_t s);
+
+}  // namespace qdr

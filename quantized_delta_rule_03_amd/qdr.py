@@ -1,0 +1,226 @@
+"""Thin Python binding of libqdr (C ABI in include/qdr.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP kernels of
+``libqdr.so``. PyTorch supplies device memory (``torch.empty``) and the current HIP
+stream. There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqdr.so")
+
+QDR_OK = 0
+QDR_EINVAL = -1
+QDR_EUNSUPPORTED = -2
+QDR_EALIGN = -3
+QDR_EHIP = -4
+GDN = 0
+KDA = 1
+
+SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize_state",
+           "qdr_decode_step", "qdr_decode_window", "qdr_dequantize_state", "qdr_last_error")
+
+
+class QdrError(RuntimeError):
+    def __init__(self, code: int, where: str, text: str):
+        super().__init__(f"{where} failed with {code}: {text}")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("n_head", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("gate", ctypes.c_int32),
+                ("bits", ctypes.c_void_p), ("window", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqdr.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "quantized_delta_rule_03_amd/build.py (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32 = ctypes.c_void_p, ctypes.c_int32
+        D = ctypes.POINTER(Desc)
+        sz = ctypes.POINTER(ctypes.c_size_t)
+        sigs = {
+            "qdr_assign_bits": [i32, i32, i32, P, P],
+            "qdr_state_bytes": [D, sz, sz, sz, sz],
+            "qdr_init_state": [D, P, P, P, P, P],
+            "qdr_quantize_state": [D, P, P, P, P, P, P],
+            "qdr_decode_step": [D, P, P, P, P, P, P, P, P, P, P, P],
+            "qdr_decode_window": [D, P, P, P, P, P, i32, P, P, P, P, P, P, P],
+            "qdr_dequantize_state": [D, P, P, P, P, P, P],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.qdr_last_error.argtypes = []
+        L.qdr_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().qdr_last_error().decode()
+
+
+def _check(rc: int, where: str):
+    if rc != QDR_OK:
+        raise QdrError(rc, where, last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+def assign_bits(gate: int, halflife: np.ndarray, dk: int = 128) -> np.ndarray:
+    """Lifetime quartile bit map (host): GDN halflife [n_head], KDA [n_head, dk]."""
+    hl = np.ascontiguousarray(halflife, np.float64)
+    n_head = hl.shape[0]
+    out = np.zeros((n_head, dk), np.uint8)
+    _check(lib().qdr_assign_bits(gate, n_head, dk, hl.ctypes.data, out.ctypes.data),
+           "qdr_assign_bits")
+    return out
+
+
+@dataclass
+class Layout:
+    """Descriptor plus the sizes libqdr reports for it."""
+    n_req: int
+    n_head: int
+    gate: int
+    bits: np.ndarray
+    window: int = 0
+    packed_bytes: int = 0
+    scale_bytes: int = 0
+    meta_bytes: int = 0
+    window_bytes: int = 0
+    _desc: Desc = field(default=None, repr=False)
+
+    def __post_init__(self):
+        self.bits = np.ascontiguousarray(self.bits, np.uint8).reshape(self.n_head, 128)
+        self._desc = Desc(self.n_req, self.n_head, 128, 128, self.gate,
+                          self.bits.ctypes.data, self.window)
+        s = [ctypes.c_size_t() for _ in range(4)]
+        _check(lib().qdr_state_bytes(ctypes.byref(self._desc), *[ctypes.byref(x) for x in s]),
+               "qdr_state_bytes")
+        self.packed_bytes, self.scale_bytes, self.meta_bytes, self.window_bytes = (
+            int(x.value) for x in s)
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    @property
+    def req_bytes(self):
+        return self.packed_bytes // self.n_req if self.n_req else 0
+
+
+def init_state(L: Layout, packed, row_scale, col_scale, meta, stream=None):
+    _check(lib().qdr_init_state(L.desc, _ptr(packed), _ptr(row_scale), _ptr(col_scale),
+                                _ptr(meta), _stream(stream)), "qdr_init_state")
+
+
+def quantize_state(L: Layout, meta, S, packed, row_scale, col_scale, stream=None):
+    _check(lib().qdr_quantize_state(L.desc, _ptr(meta), _ptr(S), _ptr(packed), _ptr(row_scale),
+                                    _ptr(col_scale), _stream(stream)), "qdr_quantize_state")
+
+
+def decode_step(L: Layout, meta, packed, row_scale, col_scale, q, k, v, a, b, o, stream=None):
+    _check(lib().qdr_decode_step(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                 _ptr(col_scale), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                 _ptr(o), _stream(stream)), "qdr_decode_step")
+
+
+def decode_window(L: Layout, meta, packed, row_scale, col_scale, window_buf, t, q, k, v, a, b, o,
+                  stream=None):
+    _check(lib().qdr_decode_window(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                   _ptr(col_scale), _ptr(window_buf), int(t), _ptr(q), _ptr(k),
+                                   _ptr(v), _ptr(a), _ptr(b), _ptr(o), _stream(stream)),
+           "qdr_decode_window")
+
+
+def dequantize_state(L: Layout, meta, packed, row_scale, col_scale, S_out, stream=None):
+    _check(lib().qdr_dequantize_state(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                      _ptr(col_scale), _ptr(S_out), _stream(stream)),
+           "qdr_dequantize_state")
+
+
+class StatePool:
+    """Caller-owned device buffers of one layer's quantized state (torch allocations)."""
+
+    def __init__(self, n_req: int, n_head: int, gate: int, bits: np.ndarray, window: int = 0,
+                 device="cuda"):
+        import torch
+
+        self.layout = Layout(n_req, n_head, gate, bits, window)
+        L = self.layout
+        self.device = torch.device(device)
+        self.packed = torch.empty(max(L.packed_bytes, 16), dtype=torch.uint8, device=device)
+        shape = (n_req, n_head, 128)
+        self.row_scale = torch.empty(shape, dtype=torch.float32, device=device)
+        self.col_scale = torch.empty(shape, dtype=torch.float32, device=device)
+        self.meta = torch.empty(L.meta_bytes, dtype=torch.uint8, device=device)
+        self.window_buf = (torch.empty(L.window_bytes, dtype=torch.uint8, device=device)
+                           if L.window_bytes else None)
+        init_state(L, self.packed, self.row_scale, self.col_scale, self.meta)
+
+    def quantize(self, S, stream=None):
+        quantize_state(self.layout, self.meta, S, self.packed, self.row_scale, self.col_scale,
+                       stream)
+
+    def step(self, q, k, v, a, b, o, stream=None):
+        decode_step(self.layout, self.meta, self.packed, self.row_scale, self.col_scale,
+                    q, k, v, a, b, o, stream)
+
+    def window_token(self, t, q, k, v, a, b, o, stream=None):
+        decode_window(self.layout, self.meta, self.packed, self.row_scale, self.col_scale,
+                      self.window_buf, t, q, k, v, a, b, o, stream)
+
+    def dequantize(self, S_out=None, stream=None):
+        import torch
+
+        if S_out is None:
+            S_out = torch.empty((self.layout.n_req, self.layout.n_head, 128, 128),
+                                dtype=torch.float32, device=self.device)
+        dequantize_state(self.layout, self.meta, self.packed, self.row_scale, self.col_scale,
+                         S_out, stream)
+        return S_out
+
+    def load_host(self, packed: np.ndarray, row_scale: np.ndarray, col_scale: np.ndarray):
+        """Copy a host packed state (same layout) into the device buffers."""
+        import torch
+
+        n = self.layout.packed_bytes
+        self.packed[:n].copy_(torch.from_numpy(np.ascontiguousarray(packed).reshape(-1)))
+        self.row_scale.copy_(torch.from_numpy(np.ascontiguousarray(row_scale)))
+        self.col_scale.copy_(torch.from_numpy(np.ascontiguousarray(col_scale)))
+
+    def to_host(self):
+        n = self.layout.packed_bytes
+        return (self.packed[:n].cpu().numpy().reshape(self.layout.n_req, -1),
+                self.row_scale.cpu().numpy(), self.col_scale.cpu().numpy())

@@ -7,9 +7,10 @@ it derives from drawn half-lives (a = 2^(-1/tau)) and drawn logits
 (a = exp(-softplus(x))) are inputs of the method, not steps of it.
 
 Seeding: every array comes from ``numpy.random.default_rng(SeedSequence(key))``
-with ``key = [seed, workload_id, stream, index]``; stream 0 = static draws
-(half-lives, outlier masks), 1 = decode-step inputs, 2 = pre-warm inputs. Inside a
-step the draw order is k, q, v, b, x.
+with ``key = [seed, workload_id, stream, ...]``; stream 0 = static draws
+(half-lives: [..., 0, 0]; outlier masks: [..., 0, 1, request]), 1 = decode-step
+inputs ([..., 1, step, request]), 2 = pre-warm inputs ([..., 2, step, request]).
+Inside a request's step the draw order is k, q, v, b, x.
 """
 from __future__ import annotations
 
@@ -57,9 +58,9 @@ WORKLOADS = {
 }
 
 
-def _rng(seed, wid, stream, index):
-    return np.random.default_rng(np.random.SeedSequence([int(seed), int(wid), int(stream),
-                                                         int(index)]))
+def _rng(seed, wid, stream, *index):
+    key = [int(seed), int(wid), int(stream)] + [int(i) for i in index]
+    return np.random.default_rng(np.random.SeedSequence(key))
 
 
 def _unit_normal_rows(rng, shape):
@@ -103,45 +104,52 @@ def uniform_bits(n_head: int, width: int = 8) -> np.ndarray:
 
 
 def step_inputs(w: Workload, step: int, seed: int = 0, n_req: Optional[int] = None,
-                stream: int = 1) -> dict:
-    """Inputs of decode step ``step`` for requests [0, n_req).
+                stream: int = 1, r0: int = 0) -> dict:
+    """Inputs of decode step ``step`` for requests [r0, r0 + n_req).
 
     q, k: [n_req, n_head, DK] unit-norm; v: [n_req, n_head, DV] ~ N(0,1);
     b: [n_req, n_head] ~ U(0,1); a: the gate (per-step exp(-softplus(x)) for a
-    per-step-gate workload, else the fixed gate). Draws are made for all of the
-    workload's requests so that a prefix is the same as in the full-size run.
+    per-step-gate workload, else the fixed gate). Each request draws from its own
+    seed key [seed, workload, stream, step, request], so any subset of requests gets
+    exactly the values it has in the full-size run.
     """
-    rng = _rng(seed, w.wid, stream, step)
-    full = (w.n_req, w.n_head)
-    k = _unit_normal_rows(rng, full + (DK,))
-    q = _unit_normal_rows(rng, full + (DK,))
-    v = rng.standard_normal(full + (DV,)).astype(np.float32)
-    b = rng.uniform(0.0, 1.0, size=full).astype(np.float32)
-    x = rng.standard_normal(full)
-    n = w.n_req if n_req is None else n_req
-    out = {"q": q[:n], "k": k[:n], "v": v[:n], "b": b[:n]}
+    n = (w.n_req - r0) if n_req is None else n_req
+    H = w.n_head
+    out = {"q": np.empty((n, H, DK), np.float32), "k": np.empty((n, H, DK), np.float32),
+           "v": np.empty((n, H, DV), np.float32), "b": np.empty((n, H), np.float32)}
+    x = np.empty((n, H), np.float64)
+    for i in range(n):
+        rng = _rng(seed, w.wid, stream, step, r0 + i)
+        out["k"][i] = _unit_normal_rows(rng, (H, DK))
+        out["q"][i] = _unit_normal_rows(rng, (H, DK))
+        out["v"][i] = rng.standard_normal((H, DV))
+        out["b"][i] = rng.uniform(0.0, 1.0, size=H)
+        x[i] = rng.standard_normal(H)
     if w.per_step_gate:
         # a = exp(-softplus(x)) = 1 / (1 + e^x), evaluated in fp64
-        out["a"] = np.exp(-np.logaddexp(0.0, x[:n])).astype(np.float32)
+        out["a"] = np.exp(-np.logaddexp(0.0, x)).astype(np.float32)
     else:
         out["a"] = static_gate(w, seed, n)
     return {kk: np.ascontiguousarray(vv) for kk, vv in out.items()}
 
 
-def prewarm_inputs(w: Workload, step: int, seed: int = 0, n_req: Optional[int] = None) -> dict:
+def prewarm_inputs(w: Workload, step: int, seed: int = 0, n_req: Optional[int] = None,
+                   r0: int = 0) -> dict:
     """Inputs of pre-warm step ``step`` (same distributions, stream 2)."""
-    return step_inputs(w, step, seed, n_req, stream=2)
+    return step_inputs(w, step, seed, n_req, stream=2, r0=r0)
 
 
-def outlier_masks(w: Workload, seed: int = 0, n_req: Optional[int] = None):
+def outlier_masks(w: Workload, seed: int = 0, n_req: Optional[int] = None, r0: int = 0):
     """Boolean masks selecting outlier key channels [n_req, n_head, DK] and value rows
     [n_req, n_head, DV], each entry independently with probability outlier_frac."""
-    rng = _rng(seed, w.wid, 0, 1)
-    full = (w.n_req, w.n_head)
-    key_sel = rng.uniform(size=full + (DK,)) < w.outlier_frac
-    val_sel = rng.uniform(size=full + (DV,)) < w.outlier_frac
-    n = w.n_req if n_req is None else n_req
-    return key_sel[:n], val_sel[:n]
+    n = (w.n_req - r0) if n_req is None else n_req
+    key_sel = np.empty((n, w.n_head, DK), bool)
+    val_sel = np.empty((n, w.n_head, DV), bool)
+    for i in range(n):
+        rng = _rng(seed, w.wid, 0, 1, r0 + i)
+        key_sel[i] = rng.uniform(size=(w.n_head, DK)) < w.outlier_frac
+        val_sel[i] = rng.uniform(size=(w.n_head, DV)) < w.outlier_frac
+    return key_sel, val_sel
 
 
 def device_step_inputs(w: Workload, step: int, device, seed: int = 0):

@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header
+declares, and its host-side logic (validation, sizes, bit map) behaves as documented."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from quantized_delta_rule_03_amd import qdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "qdr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdr_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = qdr.lib()
+    syms = header_symbols()
+    assert set(syms) == set(qdr.SYMBOLS), syms
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_assign_bits_matches_oracle(oref):
+    rng = np.random.default_rng(1)
+    tau = np.exp(rng.uniform(0, np.log(4096), 32))
+    assert np.array_equal(qdr.assign_bits(qdr.GDN, tau), oref.assign_bits(0, tau, 128))
+    tau2 = np.exp(rng.uniform(0, np.log(8192), (8, 128)))
+    assert np.array_equal(qdr.assign_bits(qdr.KDA, tau2), oref.assign_bits(1, tau2, 128))
+    ties = np.ones(12)
+    assert np.array_equal(qdr.assign_bits(qdr.GDN, ties), oref.assign_bits(0, ties, 128))
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_state_bytes_matches_oracle_layout(oref, gate):
+    rng = np.random.default_rng(2)
+    if gate == 0:
+        bits = qdr.assign_bits(0, np.exp(rng.uniform(0, 8, 32)))
+    else:
+        bits = qdr.assign_bits(1, np.exp(rng.uniform(0, 9, (32, 128))))
+    L = qdr.Layout(7, 32, gate, bits, window=64)
+    pool = oref.Pool(7, 32, bits)
+    assert L.packed_bytes == 7 * pool.req_bytes
+    assert L.scale_bytes == 7 * 32 * 128 * 4
+    assert L.meta_bytes == 64 + 32 * 144
+    assert L.window_bytes == 7 * 32 * (64 * 2 * 128 * 4 + 128 * 4)
+
+
+def _desc(n_req=2, n_head=4, dk=128, dv=128, gate=0, bits=None, window=0):
+    if bits is None:
+        bits = np.full((n_head, 128), 8, np.uint8)
+    d = qdr.Desc(n_req, n_head, dk, dv, gate, bits.ctypes.data if bits is not False else None,
+                 window)
+    return d, bits
+
+
+def _state_bytes(d):
+    s = [ctypes.c_size_t() for _ in range(4)]
+    return qdr.lib().qdr_state_bytes(ctypes.byref(d), *[ctypes.byref(x) for x in s])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=64), qdr.QDR_EUNSUPPORTED),
+    (dict(dv=256), qdr.QDR_EUNSUPPORTED),
+    (dict(n_head=0), qdr.QDR_EINVAL),
+    (dict(n_req=-1), qdr.QDR_EINVAL),
+    (dict(gate=7), qdr.QDR_EINVAL),
+    (dict(window=-3), qdr.QDR_EINVAL),
+])
+def test_descriptor_validation(kw, code):
+    d, keep = _desc(**kw)
+    assert _state_bytes(d) == code
+    assert qdr.last_error() != ""
+
+
+def test_bad_bit_maps():
+    bits = np.full((4, 128), 8, np.uint8)
+    bits[1, 5] = 5
+    d, keep = _desc(bits=bits)
+    assert _state_bytes(d) == qdr.QDR_EUNSUPPORTED
+    assert "bits[1][5]" in qdr.last_error()
+    bits = np.full((4, 128), 8, np.uint8)
+    bits[2, :20] = 4
+    d, keep = _desc(bits=bits)
+    assert _state_bytes(d) == qdr.QDR_EUNSUPPORTED
+    d = qdr.Desc(2, 4, 128, 128, 0, None, 0)
+    assert _state_bytes(d) == qdr.QDR_EINVAL
+
+
+def test_pointer_validation_before_any_launch():
+    """Null and misaligned device pointers are rejected on the host (no GPU touched)."""
+    d, keep = _desc()
+    L = qdr.lib()
+    P = 1 << 20  # aligned fake address, never dereferenced because validation fails first
+    rc = L.qdr_decode_step(ctypes.byref(d), P, P, P, P, P, P, P, P, None, P, None)
+    assert rc == qdr.QDR_EINVAL and "b is NULL" in qdr.last_error()
+    rc = L.qdr_decode_step(ctypes.byref(d), P, P + 4, P, P, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EALIGN and "packed" in qdr.last_error()
+    rc = L.qdr_quantize_state(ctypes.byref(d), None, P, P, P, P, None)
+    assert rc == qdr.QDR_EINVAL and "meta" in qdr.last_error()
+    rc = L.qdr_dequantize_state(ctypes.byref(d), P, P, P, P + 8, P, None)
+    assert rc == qdr.QDR_EALIGN
+
+
+def test_window_position_validation():
+    d, keep = _desc(window=0)
+    L = qdr.lib()
+    P = 1 << 20
+    rc = L.qdr_decode_window(ctypes.byref(d), P, P, P, P, P, 0, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED
+    d, keep = _desc(window=64)
+    rc = L.qdr_decode_window(ctypes.byref(d), P, P, P, P, P, 64, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED and "t = 64" in qdr.last_error()
+    rc = L.qdr_decode_window(ctypes.byref(d), P, P, P, P, P, -1, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED
+
+
+def test_errors_are_thread_local():
+    import threading
+
+    d, keep = _desc(dk=64)
+    assert _state_bytes(d) == qdr.QDR_EUNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["text"] = qdr.last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["text"] == ""
+    assert qdr.last_error() != ""
