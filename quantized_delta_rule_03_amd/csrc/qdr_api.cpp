@@ -68,7 +68,10 @@ int head_layout(const uint8_t* bits, HeadLayout* out, int h) {
 struct Geometry {
   std::vector<HeadLayout> heads;
   std::vector<uint32_t> off;
+  std::vector<uint16_t> order;  // heads by width 8, 6, 4 (uniform heads)
   uint32_t req_bytes = 0;
+  bool uniform = true;
+  int n_class[3] = {0, 0, 0};
 };
 
 int check_desc(const qdr_desc* d, Geometry* g) {
@@ -97,6 +100,20 @@ int check_desc(const qdr_desc* d, Geometry* g) {
     }
     if (off > 0xFFFFFFFFull) return fail(QDR_EINVAL, "request too large");
     g->req_bytes = (uint32_t)off;
+    static const int widths[3] = {8, 6, 4};
+    for (int h = 0; h < d->n_head; ++h) {
+      const uint8_t* sb = g->heads[h].seg_bits;
+      g->uniform = g->uniform && sb[0] == sb[1] && sb[1] == sb[2] && sb[2] == sb[3];
+    }
+    g->order.clear();
+    for (int c = 0; c < 3; ++c) {
+      g->n_class[c] = 0;
+      for (int h = 0; h < d->n_head; ++h)
+        if (g->heads[h].seg_bits[0] == widths[c] && g->heads[h].seg_bits[3] == widths[c]) {
+          g->order.push_back((uint16_t)h);
+          ++g->n_class[c];
+        }
+    }
   }
   return QDR_OK;
 }
@@ -120,6 +137,8 @@ qdr::Pool pool_of(const qdr_desc* d, const void* meta, const Geometry& g) {
   p.n_head = d->n_head;
   p.n_unit = d->n_req * d->n_head;
   p.req_bytes = g.req_bytes;
+  p.uniform = g.uniform ? 1 : 0;
+  for (int c = 0; c < 3; ++c) p.n_class[c] = g.n_class[c];
   return p;
 }
 
@@ -172,7 +191,7 @@ int qdr_state_bytes(const qdr_desc* d, size_t* packed, size_t* scales, size_t* m
   const size_t n_unit = (size_t)d->n_req * d->n_head;
   if (packed) *packed = (size_t)d->n_req * g.req_bytes;
   if (scales) *scales = n_unit * qdr::kD * sizeof(float);
-  if (meta) *meta = sizeof(qdr::MetaHeader) + (size_t)d->n_head * sizeof(qdr::MetaHead);
+  if (meta) *meta = qdr::meta_bytes(d->n_head);
   if (window_buf) *window_buf = d->window > 0 ? n_unit * qdr::window_unit_bytes(d->window) : 0;
   return ok();
 }
@@ -186,7 +205,7 @@ int qdr_init_state(const qdr_desc* d, void* packed, float* row_scale, float* col
   CHECK(check_ptr(packed, "packed", any));
   CHECK(check_ptr(row_scale, "row_scale", any));
   CHECK(check_ptr(col_scale, "col_scale", any));
-  std::vector<uint8_t> host(sizeof(qdr::MetaHeader) + (size_t)d->n_head * sizeof(qdr::MetaHead), 0);
+  std::vector<uint8_t> host(qdr::meta_bytes(d->n_head), 0);
   auto* hdr = reinterpret_cast<qdr::MetaHeader*>(host.data());
   hdr->magic = qdr::kMetaMagic;
   hdr->n_head = (uint32_t)d->n_head;
@@ -195,6 +214,8 @@ int qdr_init_state(const qdr_desc* d, void* packed, float* row_scale, float* col
   hdr->gate = (uint32_t)d->gate;
   hdr->req_bytes = g.req_bytes;
   hdr->window = (uint32_t)d->window;
+  hdr->uniform = g.uniform ? 1u : 0u;
+  for (int c = 0; c < 3; ++c) hdr->n_class[c] = (uint32_t)g.n_class[c];
   auto* mh = reinterpret_cast<qdr::MetaHead*>(host.data() + sizeof(qdr::MetaHeader));
   for (int h = 0; h < d->n_head; ++h) {
     mh[h].tile_off = g.off[h];
@@ -202,6 +223,12 @@ int qdr_init_state(const qdr_desc* d, void* packed, float* row_scale, float* col
     memcpy(mh[h].seg_bits, g.heads[h].seg_bits, 4);
     mh[h].identity = g.heads[h].identity ? 1u : 0u;
     memcpy(mh[h].perm, g.heads[h].perm, qdr::kD);
+    for (int q = 0; q < qdr::kD; ++q) mh[h].iperm[g.heads[h].perm[q]] = (uint8_t)q;
+  }
+  if (g.uniform) {
+    uint16_t* ord = reinterpret_cast<uint16_t*>(host.data() + sizeof(qdr::MetaHeader) +
+                                                (size_t)d->n_head * sizeof(qdr::MetaHead));
+    for (size_t i = 0; i < g.order.size(); ++i) ord[i] = g.order[i];
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the table is small; a synchronous copy keeps the host vector's lifetime simple

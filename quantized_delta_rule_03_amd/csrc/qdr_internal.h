@@ -20,7 +20,9 @@ struct MetaHeader {
   uint32_t gate;
   uint32_t req_bytes;
   uint32_t window;
-  uint32_t reserved[9];
+  uint32_t uniform;     // 1 if every head has a single code width
+  uint32_t n_class[3];  // uniform heads of width 8, 6, 4
+  uint32_t reserved[5];
 };
 static_assert(sizeof(MetaHeader) == 64, "meta header size");
 
@@ -30,11 +32,24 @@ struct MetaHead {
   uint8_t seg_bits[4];  // width of physical positions 32s..32s+31
   uint32_t identity;    // 1 if the physical order is the logical order
   uint8_t perm[kD];     // perm[p] = logical key channel at physical position p
+  uint8_t iperm[kD];    // iperm[j] = physical position of logical key channel j
 };
-static_assert(sizeof(MetaHead) == 144, "meta head size");
+static_assert(sizeof(MetaHead) == 272, "meta head size");
 
 __host__ __device__ inline const MetaHead* meta_heads(const void* meta) {
   return reinterpret_cast<const MetaHead*>(static_cast<const uint8_t*>(meta) + sizeof(MetaHeader));
+}
+
+// After the head records: uint16 head indices ordered by width (8, 6, 4), ties by index
+// (meaningful when every head has a single width).
+__host__ __device__ inline const uint16_t* meta_order(const void* meta, int n_head) {
+  return reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(meta) + sizeof(MetaHeader) +
+                                           (size_t)n_head * sizeof(MetaHead));
+}
+
+inline size_t meta_bytes(int n_head) {
+  return sizeof(MetaHeader) + (size_t)n_head * sizeof(MetaHead) +
+         (((size_t)n_head * 2 + 15) & ~(size_t)15);
 }
 
 // Bytes of one window-buffer slot set per unit: W slots of (kappa[128], delta[128]) fp32
@@ -46,6 +61,8 @@ struct Pool {
   int n_head;
   int n_unit;
   uint32_t req_bytes;
+  int uniform;      // every head has a single code width
+  int n_class[3];   // heads of width 8, 6, 4 (uniform case)
 };
 
 // Launchers (kernels.hip). All enqueue on `stream` and return hipGetLastError().

@@ -1,15 +1,18 @@
 // qdr_kernels.hip -- gfx950 kernels of libqdr: init, quantize, dequantize, decode step.
 //
-// Work decomposition (all kernels): one work-group of 256 threads (4 wave64) per
-// (request, head) unit. Wave w owns segment w of the tile, i.e. physical key positions
+// Work decomposition. One work-group of 256 threads (4 wave64) owns one (request, head)
+// unit at a time. Wave w owns segment w of the tile, i.e. physical key positions
 // 32w..32w+31, which all share one code width. Lane l of a wave owns value rows
 // rg + 16 r (rg = l & 15, r = 0..7) at the 8 key positions 32w + 8 jg + m (jg = l >> 4,
 // m = 0..7): 64 state entries per lane, held in VGPRs for the whole step.
-//
-// With that layout a wave-wide load of one row slot r reads 16 consecutive segment
-// rows x 4 lanes, i.e. one contiguous 64*b-byte block (512 B at 8 bits); key-row
-// (column) reductions stay inside a wave (16 lanes of one DPP row), value-row
-// reductions go through LDS across the 16 (wave, jg) partials.
+//  - A wave-wide load of one row slot r reads 16 consecutive segment rows x 4 lanes,
+//    i.e. one contiguous 64*b-byte block (512 B at 8 bits).
+//  - Key-row (column) absmax stays inside a wave: in-lane over 8 rows, then across the
+//    16 lanes of one DPP row. Value-row reductions (prediction, readout, value-column
+//    absmax) go through LDS over the 16 (wave, jg) partials of a row.
+//  - The decode step is persistent: a grid of (CUs x resident groups) work-groups walks
+//    the units, and each group issues the loads of its next unit's codes and vectors
+//    before computing the current one, so HBM reads stay in flight during the compute.
 //
 // Arithmetic contract (identical in every rounding to the scalar reference):
 //   dequant + gate   P = fl(code * cf_j) as fma(field, cf_j, -bias*cf_j) (exact),
@@ -50,27 +53,33 @@ struct Raw {
   uint32_t lo, hi;
 };
 
-template <int B>
-__device__ __forceinline__ Raw load_row(const uint8_t* seg, int row, int jg) {
+// One 8-byte load per row for every width, so that the number and kind of memory
+// instructions does not depend on the width (the lane's bytes are then selected by
+// fix_raw): 8-bit: bytes [8jg, 8jg+8); 6-bit: the aligned 8 bytes holding [6jg, 6jg+6);
+// 4-bit: bytes [8(jg>>1), 8(jg>>1)+8) of the 16-byte row (holds both jg pairs).
+__device__ __forceinline__ uint32_t row_load_off(int B, int jg) {
+  return B == 8 ? 8u * jg : (B == 6 ? (uint32_t)((jg * 6) & ~3) : 8u * (uint32_t)(jg >> 1));
+}
+
+__device__ __forceinline__ Raw load_row_any(const uint8_t* seg, int B, int row, int jg) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(seg + row * 4 * B + row_load_off(B, jg));
   Raw r;
-  if constexpr (B == 8) {
-    const uint2 x = *reinterpret_cast<const uint2*>(seg + row * 32 + jg * 8);
-    r.lo = x.x;
-    r.hi = x.y;
-  } else if constexpr (B == 4) {
-    r.lo = *reinterpret_cast<const uint32_t*>(seg + row * 16 + jg * 4);
-    r.hi = 0;
-  } else {
-    // 6 bytes at row*24 + 6*jg; read the two aligned dwords that contain them
-    const int start = row * 24 + ((jg * 6) & ~3);
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(seg + start);
-    uint32_t a0 = p[0], a1 = p[1];
-    const int sh = ((jg * 6) & 3) * 8;  // 0 or 16
-    const uint64_t x = ((uint64_t)a1 << 32 | a0) >> sh;
-    r.lo = (uint32_t)x;
-    r.hi = (uint32_t)(x >> 32);
-  }
+  r.lo = p[0];
+  r.hi = p[1];
   return r;
+}
+
+// select the lane's payload from the 8 loaded bytes
+template <int B>
+__device__ __forceinline__ Raw fix_raw(Raw x, int jg) {
+  if constexpr (B == 6) {
+    const uint32_t sh = (uint32_t)(jg & 1) * 16u;
+    return {__builtin_amdgcn_alignbit(x.hi, x.lo, sh), (x.hi >> sh) & 0xFFFFu};
+  } else if constexpr (B == 4) {
+    return {(jg & 1) ? x.hi : x.lo, 0u};
+  } else {
+    return x;
+  }
 }
 
 // field values (unsigned, offset binary) of the 8 codes as floats
@@ -83,59 +92,76 @@ __device__ __forceinline__ void decode_row(Raw raw, float f[8]) {
       f[m + 4] = (float)((raw.hi >> (8 * m)) & 0xFFu);
     }
   } else if constexpr (B == 4) {
+    const uint32_t ev = raw.lo & 0x0F0F0F0Fu, od = (raw.lo >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) f[m] = (float)((raw.lo >> (4 * m)) & 0xFu);
-  } else {
-    const uint64_t x = ((uint64_t)raw.hi << 32) | raw.lo;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) f[m] = (float)((uint32_t)(x >> (6 * m)) & 0x3Fu);
-  }
-}
-
-template <int B>
-__device__ __forceinline__ void store_row(uint8_t* seg, int row, int jg, const uint32_t fld[8]) {
-  if constexpr (B == 8) {
-    uint2 x;
-    x.x = fld[0] | (fld[1] << 8) | (fld[2] << 16) | (fld[3] << 24);
-    x.y = fld[4] | (fld[5] << 8) | (fld[6] << 16) | (fld[7] << 24);
-    *reinterpret_cast<uint2*>(seg + row * 32 + jg * 8) = x;
-  } else if constexpr (B == 4) {
-    uint32_t x = 0;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) x |= fld[m] << (4 * m);
-    *reinterpret_cast<uint32_t*>(seg + row * 16 + jg * 4) = x;
-  } else {
-    uint64_t x = 0;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) x |= (uint64_t)fld[m] << (6 * m);
-    uint8_t* dst = seg + row * 24 + jg * 6;
-    if ((jg & 1) == 0) {  // 4-byte aligned start
-      *reinterpret_cast<uint32_t*>(dst) = (uint32_t)x;
-      *reinterpret_cast<uint16_t*>(dst + 4) = (uint16_t)(x >> 32);
-    } else {              // 2-byte aligned start, dword at +2
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)x;
-      *reinterpret_cast<uint32_t*>(dst + 2) = (uint32_t)(x >> 16);
+    for (int m = 0; m < 4; ++m) {
+      f[2 * m] = (float)((ev >> (8 * m)) & 0xFFu);
+      f[2 * m + 1] = (float)((od >> (8 * m)) & 0xFFu);
     }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 5; ++m) f[m] = (float)((raw.lo >> (6 * m)) & 0x3Fu);
+    f[5] = (float)(__builtin_amdgcn_alignbit(raw.hi, raw.lo, 30) & 0x3Fu);
+    f[6] = (float)((raw.hi >> 4) & 0x3Fu);
+    f[7] = (float)((raw.hi >> 10) & 0x3Fu);
   }
 }
 
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// t[m]: fp32 bit patterns whose low B bits hold the field and bits B..22 are zero.
+// Every width issues exactly two stores per row (so that the memory-instruction count
+// does not depend on the width): 8-bit dword + dword, 6-bit dword + short (order by
+// alignment), 4-bit short + short.
 template <int B>
-__device__ __forceinline__ void load_tile_rows(const uint8_t* seg, int rg, int jg, Raw raw[8]) {
+__device__ __forceinline__ void store_row(uint8_t* seg, int row, int jg, const uint32_t t[8]) {
+  if constexpr (B == 8) {
+    // byte 0 of four words -> one word
+    const uint32_t a = perm_b32(t[1], t[0], 0x0c0c0400u);  // [t0.b0, t1.b0, 0, 0]
+    const uint32_t b = perm_b32(t[3], t[2], 0x0c0c0400u);
+    const uint32_t c = perm_b32(t[5], t[4], 0x0c0c0400u);
+    const uint32_t d = perm_b32(t[7], t[6], 0x0c0c0400u);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(seg + row * 32 + jg * 8);
+    dst[0] = perm_b32(b, a, 0x05040100u);
+    dst[1] = perm_b32(d, c, 0x05040100u);
+  } else if constexpr (B == 4) {
+    // nibble pairs: low byte of (t[2m+1] << 4 | t[2m]) holds fields 2m, 2m+1
+    const uint32_t p0 = (t[1] << 4) | t[0], p1 = (t[3] << 4) | t[2];
+    const uint32_t p2 = (t[5] << 4) | t[4], p3 = (t[7] << 4) | t[6];
+    uint16_t* dst = reinterpret_cast<uint16_t*>(seg + row * 16 + jg * 4);
+    dst[0] = (uint16_t)perm_b32(p1, p0, 0x0c0c0400u);
+    dst[1] = (uint16_t)perm_b32(p3, p2, 0x0c0c0400u);
+  } else {
+    // 24-bit groups of 4 fields; the exponent bits of t (>= bit 23) never reach bits 0..23
+    const uint32_t g0 = (t[3] << 18) | (t[2] << 12) | (t[1] << 6) | t[0];
+    const uint32_t g1 = (t[7] << 18) | (t[6] << 12) | (t[5] << 6) | t[4];
+    // even jg: dword at +0, short at +4; odd jg: short at +0, dword at +2 (no branch)
+    uint8_t* dst = seg + row * 24 + jg * 6;
+    const uint32_t par = (uint32_t)(jg & 1);
+    const uint32_t dw = perm_b32(g1, g0, par ? 0x06050402u : 0x04020100u);
+    const uint32_t hw = par ? g0 : (g1 >> 8);
+    *reinterpret_cast<uint32_t*>(dst + 2 * par) = dw;
+    *reinterpret_cast<uint16_t*>(dst + 4 - 4 * par) = (uint16_t)hw;
+  }
+}
+
+__device__ __forceinline__ void load_rows(int B, const uint8_t* seg, int rg, int jg,
+                                          Raw raw[8]) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) raw[r] = load_row<B>(seg, rg + 16 * r, jg);
+  for (int r = 0; r < 8; ++r) raw[r] = load_row_any(seg, B, rg + 16 * r, jg);
 }
 
-__device__ __forceinline__ void load_rows_dispatch(int B, const uint8_t* seg, int rg, int jg,
-                                                   Raw raw[8]) {
-  if (B == 8) load_tile_rows<8>(seg, rg, jg, raw);
-  else if (B == 6) load_tile_rows<6>(seg, rg, jg, raw);
-  else load_tile_rows<4>(seg, rg, jg, raw);
-}
-
-__device__ __forceinline__ void decode_dispatch(int B, Raw raw, float f[8]) {
-  if (B == 8) decode_row<8>(raw, f);
-  else if (B == 6) decode_row<6>(raw, f);
-  else decode_row<4>(raw, f);
+template <int BFIX>
+__device__ __forceinline__ void decode_any(int B, Raw raw, int jg, float f[8]) {
+  if constexpr (BFIX != 0) {
+    decode_row<BFIX>(fix_raw<BFIX>(raw, jg), f);
+  } else {
+    if (B == 8) decode_row<8>(raw, f);
+    else if (B == 6) decode_row<6>(fix_raw<6>(raw, jg), f);
+    else decode_row<4>(fix_raw<4>(raw, jg), f);
+  }
 }
 
 // requantize the lane's normalised entries y (8 rows x 8 positions) and store them
@@ -143,66 +169,66 @@ template <int B>
 __device__ __forceinline__ void requant_store(uint8_t* seg, int rg, int jg, const float (&y)[8][8],
                                               const float (&M)[8]) {
   const float magic = 8388608.0f + (float)(1 << (B - 1));
-  const uint32_t mask = (1u << B) - 1u;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    uint32_t fld[8];
+    uint32_t t[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) fld[m] = __float_as_uint(fmaf(y[r][m], M[r], magic)) & mask;
-    store_row<B>(seg, rg + 16 * r, jg, fld);
+    for (int m = 0; m < 8; ++m) t[m] = __float_as_uint(fmaf(y[r][m], M[r], magic));
+    store_row<B>(seg, rg + 16 * r, jg, t);
   }
 }
 
-__device__ __forceinline__ void requant_dispatch(int B, uint8_t* seg, int rg, int jg,
-                                                 const float (&y)[8][8], const float (&M)[8]) {
-  if (B == 8) requant_store<8>(seg, rg, jg, y, M);
-  else if (B == 6) requant_store<6>(seg, rg, jg, y, M);
-  else requant_store<4>(seg, rg, jg, y, M);
+template <int BFIX>
+__device__ __forceinline__ void requant_any(int B, uint8_t* seg, int rg, int jg,
+                                            const float (&y)[8][8], const float (&M)[8]) {
+  if constexpr (BFIX != 0) {
+    requant_store<BFIX>(seg, rg, jg, y, M);
+  } else {
+    if (B == 8) requant_store<8>(seg, rg, jg, y, M);
+    else if (B == 6) requant_store<6>(seg, rg, jg, y, M);
+    else requant_store<4>(seg, rg, jg, y, M);
+  }
 }
 
-__device__ __forceinline__ float shfl_xor_f(float x, int d) { return __shfl_xor(x, d, 64); }
+// max over the 16 lanes of a DPP row, for non-negative floats compared as unsigned ints
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false)); // row_ror 4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false)); // row_ror 8
+  return x;
+}
 
-// Shared tail of quantize and decode step: refit both scale axes of the lane-held
-// state s (overwritten by y) and write R (physical order) and c. Returns through
-// LDS sinvc[] the reciprocal value-column scales. Contains block barriers: every
-// thread of the block must call it.
-struct TailLds {
-  float invA[kD];
-  float invc[kD];
-  float cpart[16 * kD];
-};
-
-__device__ __forceinline__ void refit_tail(float (&s)[8][8], int w, int rg, int jg, int B,
-                                           TailLds& L, float* __restrict__ Rs_u,
-                                           float* __restrict__ Cs_u) {
-  const int p0 = 32 * w + 8 * jg;
-  // key-row absmax: in-lane over 8 rows, then across the 16 lanes rg of this jg
-  float am[8];
+// Key-row absmax of the lane-held state s over all 128 rows of this wave's segment;
+// the lanes write R (physical order) to global and 1/A to LDS for position p0 + (rg & 7).
+__device__ __forceinline__ void key_row_refit(const float (&s)[8][8], int rg, int p0, int B,
+                                              float* __restrict__ Rs_u, float* invA_lds) {
+  uint32_t am[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    float x = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) x = fmaxf(x, fabsf(s[r][m]));
-    am[m] = x;
+    float x = fmaxf(fmaxf(fabsf(s[0][m]), fabsf(s[1][m])), fabsf(s[2][m]));
+    x = fmaxf(fmaxf(x, fabsf(s[3][m])), fabsf(s[4][m]));
+    x = fmaxf(fmaxf(x, fabsf(s[5][m])), fabsf(s[6][m]));
+    x = fmaxf(x, fabsf(s[7][m]));
+    am[m] = row16_max_u32(__float_as_uint(x));
   }
+  uint32_t sel = am[0];
 #pragma unroll
-  for (int d = 1; d < 16; d <<= 1) {
-#pragma unroll
-    for (int m = 0; m < 8; ++m) am[m] = fmaxf(am[m], shfl_xor_f(am[m], d));
-  }
-  float Am = am[0];
-#pragma unroll
-  for (int m = 1; m < 8; ++m) Am = ((rg & 7) == m) ? am[m] : Am;
-  if (rg < 8) {
-    const float A = (Am == 0.0f) ? 1.0f : Am;
-    const float qmax = (float)((1 << (B - 1)) - 1);
-    Rs_u[p0 + rg] = A / qmax;
-    L.invA[p0 + rg] = 1.0f / A;
-  }
-  __syncthreads();
+  for (int m = 1; m < 8; ++m) sel = ((rg & 7) == m) ? am[m] : sel;
+  // lanes rg and rg + 8 hold the same value for position p0 + (rg & 7); both store it
+  const float Am = __uint_as_float(sel);
+  const float A = (Am == 0.0f) ? 1.0f : Am;
+  Rs_u[p0 + (rg & 7)] = A / (float)((1 << (B - 1)) - 1);
+  invA_lds[p0 + (rg & 7)] = 1.0f / A;
+}
+
+// y = s * invA in place; per-row partial value-column absmax written to cpart.
+template <int STRIDE = kD>
+__device__ __forceinline__ void normalise_rows(float (&s)[8][8], const float* invA_lds, int rg,
+                                               int p0, int slot, float* cpart) {
   float ia[8];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) ia[m] = L.invA[p0 + m];
+  for (int m = 0; m < 8; ++m) ia[m] = invA_lds[p0 + m];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     float cm = 0.0f;
@@ -212,16 +238,7 @@ __device__ __forceinline__ void refit_tail(float (&s)[8][8], int w, int rg, int 
       s[r][m] = y;
       cm = fmaxf(cm, fabsf(y));
     }
-    L.cpart[(w * 4 + jg) * kD + rg + 16 * r] = cm;
-  }
-  __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid < kD) {
-    float cm = 0.0f;
-    for (int t = 0; t < 16; ++t) cm = fmaxf(cm, L.cpart[t * kD + tid]);
-    if (cm == 0.0f) cm = 1.0f;
-    Cs_u[tid] = cm;
-    L.invc[tid] = 1.0f / cm;
+    cpart[slot * STRIDE + rg + 16 * r] = cm;
   }
 }
 
@@ -244,7 +261,7 @@ __global__ void __launch_bounds__(kThreads) k_init(const void* meta, int n_head,
 #pragma unroll
     for (int m = 0; m < 8; ++m) y[rr][m] = 0.0f;
   }
-  requant_dispatch(sg.bits, seg, rg, jg, y, M);
+  requant_any<0>(sg.bits, seg, rg, jg, y, M);
   const size_t uo = (size_t)u * kD;
   if (threadIdx.x < kD) {
     const int p = threadIdx.x;
@@ -257,10 +274,16 @@ __global__ void __launch_bounds__(kThreads) k_init(const void* meta, int n_head,
 // ------------------------------------------------------------------------------
 // quantize a caller fp32 state S [unit][dv][dk] (logical order)
 // ------------------------------------------------------------------------------
+struct QuantLds {
+  float invA[kD];
+  float invc[kD];
+  float cpart[16 * kD];
+};
+
 __global__ void __launch_bounds__(kThreads) k_quantize(const void* meta, int n_head,
                                                        uint32_t req_bytes, const float* S,
                                                        uint8_t* packed, float* Rs, float* Cs) {
-  __shared__ TailLds L;
+  __shared__ QuantLds L;
   const int u = blockIdx.x, r = u / n_head, h = u % n_head;
   const int w = wave_id(), lane = threadIdx.x & 63, rg = lane & 15, jg = lane >> 4;
   const MetaHead* mh = meta_heads(meta) + h;
@@ -277,13 +300,24 @@ __global__ void __launch_bounds__(kThreads) k_quantize(const void* meta, int n_h
 #pragma unroll
     for (int m = 0; m < 8; ++m) s[rr][m] = Su[(size_t)(rg + 16 * rr) * kD + col[m]];
   const size_t uo = (size_t)u * kD;
-  refit_tail(s, w, rg, jg, sg.bits, L, Rs + uo, Cs + uo);
+  key_row_refit(s, rg, p0, sg.bits, Rs + uo, L.invA);
+  __syncthreads();
+  normalise_rows(s, L.invA, rg, p0, w * 4 + jg, L.cpart);
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    const int i = threadIdx.x;
+    float cm = 0.0f;
+    for (int g = 0; g < 16; ++g) cm = fmaxf(cm, L.cpart[g * kD + i]);
+    if (cm == 0.0f) cm = 1.0f;
+    Cs[uo + i] = cm;
+    L.invc[i] = 1.0f / cm;
+  }
   __syncthreads();
   const float qmax = (float)((1 << (sg.bits - 1)) - 1);
   float M[8];
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) M[rr] = qmax * L.invc[rg + 16 * rr];
-  requant_dispatch(sg.bits, seg, rg, jg, s, M);
+  requant_any<0>(sg.bits, seg, rg, jg, s, M);
 }
 
 // ------------------------------------------------------------------------------
@@ -300,7 +334,7 @@ __global__ void __launch_bounds__(kThreads) k_dequantize(const void* meta, int n
   const Seg sg = seg_of(mh, w);
   const uint8_t* seg = packed + (size_t)r * req_bytes + mh->tile_off + sg.off;
   Raw raw[8];
-  load_rows_dispatch(sg.bits, seg, rg, jg, raw);
+  load_rows(sg.bits, seg, rg, jg, raw);
   const size_t uo = (size_t)u * kD;
   const int p0 = 32 * w + 8 * jg;
   const float bias = (float)(1 << (sg.bits - 1));
@@ -318,7 +352,7 @@ __global__ void __launch_bounds__(kThreads) k_dequantize(const void* meta, int n
     const int i = rg + 16 * rr;
     const float c = Cs[uo + i];
     float f[8];
-    decode_dispatch(sg.bits, raw[rr], f);
+    decode_any<0>(sg.bits, raw[rr], jg, f);
 #pragma unroll
     for (int m = 0; m < 8; ++m) Su[(size_t)i * kD + col[m]] = fmaf(f[m], R[m], nb[m]) * c;
   }
@@ -326,135 +360,579 @@ __global__ void __launch_bounds__(kThreads) k_dequantize(const void* meta, int n
 
 // ------------------------------------------------------------------------------
 // decode step
+//
+// Persistent work-groups of 4 waves walk contiguous runs of units. Wave w owns
+// segment w of the current unit: its 32 key positions x 128 rows, 64 entries per lane.
+// At the top of unit n every wave issues the global loads of its own share of unit
+// n+1 (its tile segment and a slice of the input vectors) into registers; they land
+// while unit n is computed and are written to the (single) LDS slot between the third
+// and fourth barriers of unit n, after every wave has finished reading that slot.
+//
+// Per unit:
+//   prep  (per wave)    column/row factors, and the digit planes of its segment
+//   phase 1             digit-plane sums on the matrix cores -> partials per row
+//   B1 phase 2          u, w (waves 0-1) and the readout sum (waves 2-3) per row
+//   B2 phase 3          o; dequantize + gate + update; key-row absmax in the wave;
+//                       normalise; per-row partial value-column maxima
+//   B3 phase 4          value-column scales (two waves, alternating per unit); the
+//                       next unit's inputs go to LDS
+//   B4 phase 5          requantize, pack and store the segment; store the scales
 // ------------------------------------------------------------------------------
-struct StepLds {
-  double Kd[kD];       // cf_j * k_j in fp64, physical order
-  float k[kD], q[kD], cf[kD];
-  float rf[kD], v[kD], w[kD];
-  union {
-    double upart[16 * kD];  // per (wave, jg) partial of sum_j code_ij cf_j k_j
-    struct {
-      float opart[16 * kD];
-      float spare[16 * kD];
-    } f;
-  } part;
-  TailLds tail;
+constexpr int kTileMax = 16384;  // 128 x 128 codes at 8 bits
+
+// Exact dot products on the matrix cores. The prediction needs
+//   U_i = sum_j code_ij K_j,  K_j = cf_j k_j (exact in fp64),
+// to fp64 accuracy. Per segment s, K is written in balanced base-128 fixed point
+// relative to a power of two above the segment's max |K|:
+//   K_j = 2^Es sum_{t<8} d_jt 128^-(t+1) + e_j,  d in [-64, 64],  |e_j| <= 2^(Es-57).
+// Then U_i = sum_s 2^(Es-56) sum_t 128^(7-t) D_ist with D_ist = sum_j code_ij d_jt,
+// exact int32 sums formed by v_mfma_i32_16x16x32_i8 (A = digit planes x positions,
+// B = positions x rows). The readout uses eight digit planes of Q_j = cf_j q_j the same
+// way: o_i = rf_i sum_j code_ij Q_j + w_i (k.q).
+constexpr int kPlanes = 16;  // 8 planes of K, then 8 of Q
+
+// One unit's inputs as copied from HBM (global->LDS, 16 bytes per lane).
+struct VecIn {
+  float k[kD], q[kD];  // logical key order
+  float v[kD], R[kD];  // R: key-row scales, physical order
+  float C[kD], a[kD];  // C: value-column scales; a: KDA gate, logical order
+  float b, ag, pad0, pad1;  // write strength; GDN gate
+  uint8_t perm[kD];         // physical position -> logical key channel
 };
 
+// Partial arrays: 16 slots (wave, jg) of one value per row; slot strides are padded so
+// that the four jg slots written by one instruction fall in different LDS banks.
+constexpr int kFS = kD + 4;  // float slot stride
+constexpr int kDS = kD + 2;  // double slot stride
+
+struct StepWork {
+  float cf[kD];  // column factor, physical order
+  float rf[kD];  // row factor
+  float kp[kD];  // k, physical order
+  float w[kD];
+  float invA[kD];
+  float invc[kD];
+  double osum[kD];  // rf_i-free readout sums from phase 2
+  int8_t dig[4][kPlanes][4][8];  // [segment][plane][jg][operand byte]
+  double scale_u[4], scale_o[4], kq[4];
+  union {
+    double upart[16 * kDS];  // per (wave, jg) combined digit-plane sums
+    float cpart[16 * kFS];   // per (wave, jg) partial value-column absmax
+  } part;
+};
+
+// Work order. Units are enumerated by an index k. When every head has a single code
+// width, k runs width class by width class (8, 6, 4), requests in order, the class's
+// heads in order; otherwise k = r * n_head + h.
+struct StepArgs {
+  const void* meta;
+  int n_head, n_req, n_unit;
+  uint32_t req_bytes;
+  int uniform;
+  int n_class[3];
+  uint8_t* packed;
+  float* Rs;
+  float* Cs;
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* a;
+  const float* b;
+  float* o;
+};
+
+// Position of a group's walk: request r, index hi among the nc heads of the class
+// (or all heads), whose head numbers start at order[hoff] (uniform) or are hi itself.
+struct UnitIter {
+  int r, hi, nc, hoff;
+};
+
+// One unit's addressing, wave-uniform.
+struct UnitInfo {
+  uint32_t un;    // r * n_head + h: offset of the unit's vectors and scales / 128
+  uint32_t toff;  // byte offset of the tile in the pool
+  uint32_t sb;    // byte s = width of segment s
+  uint32_t h;
+};
+
+typedef const __attribute__((address_space(4))) uint32_t* cu32_ptr;
+
+// Scalar (constant-cache) read of dword `idx` of the metadata table.
+__device__ __forceinline__ uint32_t meta_dword(const void* meta, uint32_t idx) {
+  return ((cu32_ptr)meta)[idx];
+}
+
+__device__ __forceinline__ UnitInfo unit_info(const StepArgs& A, const UnitIter& it) {
+  int h = it.hi;
+  if (A.uniform) {
+    const uint32_t pos = (uint32_t)(it.hoff + it.hi);
+    const uint32_t base = (uint32_t)(sizeof(MetaHeader) + (size_t)A.n_head * sizeof(MetaHead)) / 4;
+    const uint32_t d = meta_dword(A.meta, base + (pos >> 1));
+    h = (int)((pos & 1) ? (d >> 16) : (d & 0xFFFFu));
+  }
+  const uint32_t hb = (uint32_t)(sizeof(MetaHeader) + (size_t)h * sizeof(MetaHead)) / 4;
+  UnitInfo u;
+  u.un = (uint32_t)(it.r * A.n_head + h);
+  u.toff = (uint32_t)it.r * A.req_bytes + meta_dword(A.meta, hb);  // MetaHead::tile_off
+  u.sb = meta_dword(A.meta, hb + 2);                                // MetaHead::seg_bits
+  u.h = (uint32_t)h;
+  return u;
+}
+
+__device__ __forceinline__ void advance(UnitIter& it) {
+  if (++it.hi == it.nc) {
+    it.hi = 0;
+    ++it.r;
+  }
+}
+
+__device__ __forceinline__ Seg seg_from(uint32_t sb, int w) {
+  uint32_t off = 0;
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+    if (s < w) off += 512u * ((sb >> (8 * s)) & 0xFFu);
+  return {(int)((sb >> (8 * w)) & 0xFFu), off};
+}
+
+// Byte of an 8-position group at which position m sits in the MFMA code operand:
+// natural order for 8 and 6 bits; even positions then odd ones for 4 bits (that is
+// how the nibble pairs separate into bytes).
+__device__ __forceinline__ int operand_byte(int B, int m) {
+  return B == 4 ? ((m & 1) ? 4 + (m >> 1) : (m >> 1)) : m;
+}
+
+// One lane's share of the next unit, held in registers until it is written to LDS.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One lane's share of the next unit, held in registers until it is written to LDS.
+struct Prefetch {
+  u32x4 t0, t1, t2, t3;  // tile segment: 16 bytes of each 1 KB chunk
+  u32x4 vec;             // 16 bytes of an input vector (or of the KDA position map)
+  float sc;              // wave 3: lane 0 b, lane 1 the GDN gate
+};
+
+// Every wave issues the same instruction sequence; which arrays a wave and lane read
+// is chosen by address arithmetic and lane masks, not by branches on the wave index
+// (branches would merge the pending-load state of the prefetch registers at their
+// joins and force early waits):
+//   wave 0: k (lanes 0-31), q (32-63)    wave 1: v, R
+//   wave 2: C, a (KDA only)              wave 3: KDA position map (lanes 0-7); b, a (GDN)
+__device__ __forceinline__ bool vec_lane_active(int gate, int w, int lane) {
+  return w < 2 || (w == 2 && (gate == KDA || lane < 32)) || (w == 3 && gate == KDA && lane < 8);
+}
+
+template <int GATE, int B>
+__device__ __forceinline__ void issue_prefetch(const StepArgs& A, const UnitInfo& u, int w, int lane,
+                                               Prefetch& f) {
+  const Seg sg = seg_from(u.sb, w);
+  const int nchunk = (B ? B : sg.bits) >> 1;  // 512 * bits bytes in 1 KB chunks
+  const u32x4* src = reinterpret_cast<const u32x4*>(A.packed + u.toff + sg.off) + lane;
+  f.t0 = src[0];
+  f.t1 = src[64];
+  if (nchunk > 2) f.t2 = src[128];
+  if (nchunk > 3) f.t3 = src[192];
+  const uintptr_t pk = (uintptr_t)A.k, pq = (uintptr_t)A.q, pv = (uintptr_t)A.v;
+  const uintptr_t pr = (uintptr_t)A.Rs, pc = (uintptr_t)A.Cs, pa = (uintptr_t)A.a;
+  const uintptr_t pm = (uintptr_t)meta_heads(A.meta)[u.h].perm;
+  const uintptr_t lo = w == 0 ? pk : (w == 1 ? pv : (w == 2 ? pc : pm));
+  const uintptr_t hi = w == 0 ? pq : (w == 1 ? pr : (w == 2 ? pa : pm));
+  const uintptr_t off = w == 3 ? (uintptr_t)lane * 16
+                               : ((uintptr_t)u.un * kD + (uintptr_t)(lane & 31) * 4) * 4;
+  const uintptr_t base = lane >= 32 ? hi : lo;
+  if (vec_lane_active(GATE, w, lane)) f.vec = *reinterpret_cast<const u32x4*>(base + off);
+  if (w == 3 && lane < (GATE == GDN ? 2 : 1))
+    f.sc = *reinterpret_cast<const float*>((lane ? pa : (uintptr_t)A.b) + (uintptr_t)u.un * 4);
+}
+
+// Write a prefetched share to the LDS slot.
+template <int GATE, int B>
+__device__ __forceinline__ void commit_prefetch(const UnitInfo& u, int w, int lane, const Prefetch& f,
+                                                uint8_t* tile, VecIn& vin) {
+  const Seg sg = seg_from(u.sb, w);
+  const int nchunk = (B ? B : sg.bits) >> 1;
+  u32x4* dst = reinterpret_cast<u32x4*>(tile + sg.off) + lane;
+  dst[0] = f.t0;
+  dst[64] = f.t1;
+  if (nchunk > 2) dst[128] = f.t2;
+  if (nchunk > 3) dst[192] = f.t3;
+  // lanes 32-63 of waves 0-2 land in the array after the first one (q, R, a)
+  float* vdst = w == 0 ? vin.k : (w == 1 ? vin.v : (w == 2 ? vin.C : reinterpret_cast<float*>(vin.perm)));
+  if (vec_lane_active(GATE, w, lane)) reinterpret_cast<u32x4*>(vdst)[lane] = f.vec;
+  if (w == 3 && lane < (GATE == GDN ? 2 : 1)) (&vin.b)[lane] = f.sc;
+}
+
+// max over the 32 lanes of one half of the wave
+__device__ __forceinline__ int half_max_i32(int x) {
+  uint32_t y = (uint32_t)(x + 4096);
+  y = row16_max_u32(y);
+  y = max(y, (uint32_t)__builtin_amdgcn_ds_swizzle((int)y, 0x401F));  // lane ^ 16
+  return (int)y - 4096;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// sum over the 32 lanes of one half of the wave; lanes 0 and 32 end with the sum taken
+// in a fixed tree order
+__device__ __forceinline__ double half_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);   // quad [1,0,3,2]
+  x += dpp_f64<0x4E>(x);   // quad [2,3,0,1]
+  x += dpp_f64<0x124>(x);  // row_ror 4
+  x += dpp_f64<0x128>(x);  // row_ror 8
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_ds_swizzle((int)u, 0x401F);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(u >> 32), 0x401F);
+  const double y = __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+  return x + y;
+}
+
+// Prep of wave w's segment: lanes 0-31 take K = cf k at position 32w + lane, lanes
+// 32-63 take Q = cf q there (and the row factor of value row 32w + lane - 32).
 template <int GATE>
-__global__ void __launch_bounds__(kThreads) k_step(const void* meta, int n_head,
-                                                   uint32_t req_bytes, uint8_t* packed,
-                                                   float* Rs, float* Cs, const float* q,
-                                                   const float* k, const float* v,
-                                                   const float* a, const float* b, float* o) {
-  __shared__ StepLds L;
-  const int u = blockIdx.x, r = u / n_head, h = u % n_head;
+__device__ __forceinline__ void prep(const VecIn& vin, StepWork& W, int w, int lane, int Bw) {
+  const int half = lane >> 5, pl = lane & 31;
+  const int p = 32 * w + pl;
+  const int j = (GATE == KDA) ? (int)vin.perm[p] : p;
+  const float kk = vin.k[j], qq = vin.q[j];
+  const float cf = (GATE == KDA) ? vin.a[j] * vin.R[p] : vin.R[p];
+  if (half == 0) {
+    W.cf[p] = cf;
+    W.kp[p] = kk;
+  } else {
+    W.rf[p] = (GATE == GDN) ? vin.ag * vin.C[p] : vin.C[p];
+  }
+  const double X = (double)cf * (double)(half ? qq : kk);
+  int e = -2000;
+  if (X != 0.0) (void)frexp(X, &e);
+  const int E = half_max_i32(e) + 1;  // max |X| over the half < 2^(E-1)
+  double y = ldexp(X, -E);
+  int8_t* dst = &W.dig[w][8 * half][pl >> 3][operand_byte(Bw, pl & 7)];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    y *= 128.0;
+    const double r = rint(y);
+    y -= r;
+    dst[t * 32] = (int8_t)(int)r;  // plane stride: 4 x 8 bytes
+  }
+  const double kq = half_sum_f64(half ? 0.0 : (double)kk * (double)qq);
+  if (lane == 0) {
+    W.scale_u[w] = ldexp(1.0, E - 56);
+    W.kq[w] = kq;
+  }
+  if (lane == 32) W.scale_o[w] = ldexp(1.0, E - 56);
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// four digit-plane sums of one row -> their base-128 combination (exact in fp64)
+__device__ __forceinline__ double combine4(v4i d) {
+  const int pa = d[0] * 128 + d[1];
+  const int pb = d[2] * 128 + d[3];
+  return fma((double)pa, 16384.0, (double)pb);
+}
+
+// Codes of one row as the MFMA B operand: 8 signed bytes (8 bits) or offset-binary
+// bytes (4 and 6 bits), in the byte order of operand_byte.
+template <int B>
+__device__ __forceinline__ long code_operand(Raw raw, int jg) {
+  const Raw x = fix_raw<B>(raw, jg);
+  if constexpr (B == 8) {
+    const uint32_t lo = x.lo ^ 0x80808080u, hi = x.hi ^ 0x80808080u;
+    return (long)(((uint64_t)hi << 32) | lo);
+  } else if constexpr (B == 4) {
+    const uint32_t ev = x.lo & 0x0F0F0F0Fu, od = (x.lo >> 4) & 0x0F0F0F0Fu;
+    return (long)(((uint64_t)od << 32) | ev);
+  } else {
+    // four 6-bit fields of a 24-bit group g -> four bytes
+    const uint32_t g0 = x.lo & 0xFFFFFFu;
+    const uint32_t g1 = __builtin_amdgcn_alignbit(x.hi, x.lo, 24) & 0xFFFFFFu;
+    const uint32_t lo = (g0 & 0x3Fu) | ((g0 << 2) & 0x3F00u) | ((g0 << 4) & 0x3F0000u) |
+                        ((g0 << 6) & 0x3F000000u);
+    const uint32_t hi = (g1 & 0x3Fu) | ((g1 << 2) & 0x3F00u) | ((g1 << 4) & 0x3F0000u) |
+                        ((g1 << 6) & 0x3F000000u);
+    return (long)(((uint64_t)hi << 32) | lo);
+  }
+}
+
+__device__ __forceinline__ Raw lds_row(const uint8_t* seg, int B, int i, int jg) {
+  const uint32_t* pr = reinterpret_cast<const uint32_t*>(seg + i * 4 * B + row_load_off(B, jg));
+  return {pr[0], pr[1]};
+}
+
+// Phase 1 for one code width: the lane's code operands of its 8 rows (kept for the
+// update) and the digit-plane sums of the prediction and the readout, combined per
+// lane (4 planes of one row per 16-row block) into upart.
+template <int B>
+__device__ __forceinline__ void plane_sums(const StepWork& W, double* upart, const uint8_t* seg,
+                                           int w, int rg, int jg, long (&op)[8]) {
+  const long a_op = *reinterpret_cast<const long*>(&W.dig[w][rg][jg][0]);
+  const v4i zero = {0, 0, 0, 0};
+  // offset-binary operands (4 and 6 bits): subtract bias * (sum of digits), obtained
+  // from one product with an all-bias operand
+  double corr = 0.0;
+  if constexpr (B != 8) {
+    const long bias_op = (long)(0x0101010101010101ull * (uint64_t)(1 << (B - 1)));
+    corr = combine4(__builtin_amdgcn_mfma_i32_16x16x32_i8(a_op, bias_op, zero, 0, 0, 0));
+  }
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) op[rr] = code_operand<B>(lds_row(seg, B, rg + 16 * rr, jg), jg);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    // D[plane 4jg+t][row rg of block rr] for t = 0..3
+    const v4i d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a_op, op[rr], zero, 0, 0, 0);
+    upart[(4 * w + jg) * kDS + rg + 16 * rr] = combine4(d) - corr;
+  }
+}
+
+// Phase 3 for one code width: dequantize + gate and apply the rank-one update,
+//   S'_ij = fl(fl(code cf_j) rf_i),  S_new_ij = fma(w_i, k_j, S'_ij).
+template <int B>
+__device__ __forceinline__ void update_phase(const StepWork& W, int rg, int p0, const long (&op)[8],
+                                             float (&s)[8][8]) {
+  constexpr float bias = (float)(1 << (B - 1));
+  float cf[8], nb[8], km[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    cf[m] = W.cf[p0 + m];
+    nb[m] = -bias * cf[m];
+    km[m] = W.kp[p0 + m];
+  }
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const int i = rg + 16 * rr;
+    const float rf = W.rf[i];
+    const float wi = W.w[i];
+    const uint32_t lo = (uint32_t)op[rr], hi = (uint32_t)((uint64_t)op[rr] >> 32);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int e = operand_byte(B, m);
+      const uint32_t x = e < 4 ? lo : hi;
+      float P;
+      if constexpr (B == 8) {
+        P = (float)(int)(int8_t)(x >> (8 * (e & 3))) * cf[m];  // signed code
+      } else {
+        const float field = (float)((x >> (8 * (e & 3))) & 0xFFu);
+        P = fmaf(field, cf[m], nb[m]);  // = fl((field - bias) * cf), exact rewrite
+      }
+      s[rr][m] = fmaf(wi, km[m], P * rf);
+    }
+  }
+}
+
+// Key-row absmax of the lane-held state over all 128 rows of this wave's segment.
+// Position p0 + (rg & 7) is finished by two lanes: rg < 8 forms R = A / Qmax (kept in
+// a register for the store), rg >= 8 forms 1/A and writes it to LDS.
+__device__ __forceinline__ float key_row_refit_split(const float (&s)[8][8], int rg, int p0, int B,
+                                                     float* invA_lds) {
+  uint32_t am[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    float x = fmaxf(fmaxf(fabsf(s[0][m]), fabsf(s[1][m])), fabsf(s[2][m]));
+    x = fmaxf(fmaxf(x, fabsf(s[3][m])), fabsf(s[4][m]));
+    x = fmaxf(fmaxf(x, fabsf(s[5][m])), fabsf(s[6][m]));
+    x = fmaxf(x, fabsf(s[7][m]));
+    am[m] = row16_max_u32(__float_as_uint(x));
+  }
+  uint32_t sel = am[0];
+#pragma unroll
+  for (int m = 1; m < 8; ++m) sel = ((rg & 7) == m) ? am[m] : sel;
+  const float Am = __uint_as_float(sel);
+  const float A = (Am == 0.0f) ? 1.0f : Am;
+  const bool rlane = rg < 8;
+  const float x = (rlane ? A : 1.0f) / (rlane ? (float)((1 << (B - 1)) - 1) : A);
+  if (!rlane) invA_lds[p0 + (rg & 7)] = x;
+  return x;
+}
+
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07Fu); }
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ void block_sync() {
+  wait_lgkm();
+  __builtin_amdgcn_s_barrier();
+}
+
+// Width dispatch: B != 0 is the width of every segment; B == 0 takes the wave's own
+// (wave-uniform) width at run time.
+#define QDR_WIDTH_DISPATCH(B, Bw, CALL)   \
+  do {                                    \
+    if constexpr (B != 0) {               \
+      constexpr int BB = B;               \
+      CALL;                               \
+    } else if (Bw == 8) {                 \
+      constexpr int BB = 8;               \
+      CALL;                               \
+    } else if (Bw == 6) {                 \
+      constexpr int BB = 6;               \
+      CALL;                               \
+    } else {                              \
+      constexpr int BB = 4;               \
+      CALL;                               \
+    }                                     \
+  } while (0)
+
+// One unit. `odd` alternates the two waves that form the value-column scales.
+template <int GATE, int B>
+__device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecIn& vin, StepWork& W,
+                                          const UnitInfo& cur, const UnitInfo& nx, int odd) {
   const int tid = threadIdx.x;
   const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
-  const MetaHead* mh = meta_heads(meta) + h;
-  const Seg sg = seg_of(mh, w);
-  uint8_t* seg = packed + (size_t)r * req_bytes + mh->tile_off + sg.off;
-
-  // 1. issue the code loads first so their latency overlaps the vector set-up
-  Raw raw[8];
-  load_rows_dispatch(sg.bits, seg, rg, jg, raw);
-
-  const size_t uo = (size_t)u * kD;
-  if (tid < kD) {
-    const int p = tid;
-    const int j = mh->identity ? p : (int)mh->perm[p];
-    const float kk = k[uo + j], qq = q[uo + j], R = Rs[uo + p];
-    const float cf = (GATE == KDA) ? a[uo + j] * R : R;
-    L.k[p] = kk;
-    L.q[p] = qq;
-    L.cf[p] = cf;
-    L.Kd[p] = (double)cf * (double)kk;
-  } else {
-    const int i = tid - kD;
-    const float c = Cs[uo + i];
-    L.rf[i] = (GATE == GDN) ? a[u] * c : c;
-    L.v[i] = v[uo + i];
-  }
-  __syncthreads();
-
-  // 2. dequantize + gate, partial prediction sums (fp64)
+  Prefetch f;
+  issue_prefetch<GATE, B>(A, nx, w, lane, f);  // past the last unit: the current one again
+  const Seg sg = seg_from(cur.sb, w);
+  const int Bw = B ? B : sg.bits;
   const int p0 = 32 * w + 8 * jg;
-  const float bias = (float)(1 << (sg.bits - 1));
-  float cf[8], nb[8];
-  double Kd[8];
-  double kdsum = 0.0;
+  const size_t uo = (size_t)cur.un * kD;
+
+  prep<GATE>(vin, W, w, lane, Bw);
+  wait_lgkm();
+  __builtin_amdgcn_wave_barrier();
+
+  // 1. code operands and digit-plane sums (matrix cores)
+  long op[8];
+  QDR_WIDTH_DISPATCH(B, Bw, (plane_sums<BB>(W, W.part.upart, tile + sg.off, w, rg, jg, op)));
+  block_sync();  // B1
+
+  // 2. per row: prediction u and delta w (waves 0-1), readout sum (waves 2-3)
+  {
+    const int i = tid & (kD - 1);
+    const double* up = &W.part.upart[i];
+    if (tid < kD) {
+      double U = 0.0;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    cf[m] = L.cf[p0 + m];
-    nb[m] = -bias * cf[m];
-    Kd[m] = L.Kd[p0 + m];
-    kdsum += Kd[m];
-  }
-  float s[8][8];
+      for (int s = 0; s < 4; ++s)
+        U += W.scale_u[s] * fma(up[(4 * s) * kDS], 268435456.0, up[(4 * s + 1) * kDS]);
+      const float uu = (float)((double)W.rf[i] * U);
+      W.w[i] = vin.b * (vin.v[i] - uu);
+    } else {
+      double O = 0.0;
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const int i = rg + 16 * rr;
-    const float rf = L.rf[i];
-    float f[8];
-    decode_dispatch(sg.bits, raw[rr], f);
-    double acc = 0.0;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float P = fmaf(f[m], cf[m], nb[m]);  // = fl((field - bias) * cf), exact rewrite
-      s[rr][m] = P * rf;
-      acc = fma((double)f[m], Kd[m], acc);
+      for (int s = 0; s < 4; ++s)
+        O += W.scale_o[s] * fma(up[(4 * s + 2) * kDS], 268435456.0, up[(4 * s + 3) * kDS]);
+      W.osum[i] = O;
     }
-    acc = fma(-(double)bias, kdsum, acc);
-    L.part.upart[(w * 4 + jg) * kD + i] = acc;
   }
-  __syncthreads();
+  block_sync();  // B2
 
-  // 3. prediction u, delta w (one thread per value row)
-  if (tid < kD) {
-    double t = 0.0;
-    for (int g = 0; g < 16; ++g) t += L.part.upart[g * kD + tid];
-    const float uu = (float)((double)L.rf[tid] * t);
-    L.w[tid] = b[u] * (L.v[tid] - uu);
-  }
-  __syncthreads();
-
-  // 4. rank-one update and readout partials
-  float km[8], qm[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    km[m] = L.k[p0 + m];
-    qm[m] = L.q[p0 + m];
-  }
-#pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const int i = rg + 16 * rr;
-    const float wi = L.w[i];
-    float oacc = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      s[rr][m] = fmaf(wi, km[m], s[rr][m]);
-      oacc = fmaf(s[rr][m], qm[m], oacc);
-    }
-    L.part.f.opart[(w * 4 + jg) * kD + i] = oacc;
-  }
-
-  // 5. refit scales (writes R, c) and collect the readout
-  refit_tail(s, w, rg, jg, sg.bits, L.tail, Rs + uo, Cs + uo);
+  // 3. readout; dequantize + gate + update; key-row refit inside the wave; normalise
   if (tid >= kD) {
     const int i = tid - kD;
-    float os = 0.0f;
-    for (int g = 0; g < 16; ++g) os += L.part.f.opart[g * kD + i];
-    o[uo + i] = os;
+    const double kq = ((W.kq[0] + W.kq[1]) + W.kq[2]) + W.kq[3];
+    A.o[uo + i] = (float)fma((double)W.rf[i], W.osum[i], (double)W.w[i] * kq);
   }
-  __syncthreads();
+  float s[8][8];
+  QDR_WIDTH_DISPATCH(B, Bw, (update_phase<BB>(W, rg, p0, op, s)));
+  const float Rkeep = key_row_refit_split(s, rg, p0, Bw, W.invA);
+  wait_lgkm();
+  __builtin_amdgcn_wave_barrier();
+  normalise_rows<kFS>(s, W.invA, rg, p0, w * 4 + jg, W.part.cpart);
+  block_sync();  // B3
 
-  // 6. requantize and store in place
-  const float qmax = (float)((1 << (sg.bits - 1)) - 1);
+  // 4. value-column scales; the next unit's inputs to LDS (every wave is past its
+  //    last read of the slot)
+  float cm = 0.0f;
+  if ((tid >> 7) == odd) {
+    const int i = tid & (kD - 1);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) cm = fmaxf(cm, W.part.cpart[g * kFS + i]);
+    if (cm == 0.0f) cm = 1.0f;
+    W.invc[i] = 1.0f / cm;
+  }
+  commit_prefetch<GATE, B>(nx, w, lane, f, tile, vin);
+  block_sync();  // B4
+
+  // 5. requantize and store in place; scales
+  const float qmax = (float)((1 << (Bw - 1)) - 1);
   float M[8];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) M[rr] = qmax * L.tail.invc[rg + 16 * rr];
-  requant_dispatch(sg.bits, seg, rg, jg, s, M);
+  for (int rr = 0; rr < 8; ++rr) M[rr] = qmax * W.invc[rg + 16 * rr];
+  uint8_t* gseg = A.packed + cur.toff + sg.off;
+  QDR_WIDTH_DISPATCH(B, Bw, (requant_store<BB>(gseg, rg, jg, s, M)));
+  if (rg < 8) A.Rs[uo + p0 + rg] = Rkeep;
+  if ((tid >> 7) == odd) A.Cs[uo + (tid & (kD - 1))] = cm;
 }
+
+template <int GATE, int B>
+__device__ __forceinline__ void step_run(const StepArgs& A, uint8_t* tile, VecIn& vin, StepWork& W,
+                                         UnitIter it, int count) {
+  UnitInfo cur = unit_info(A, it);
+  for (int n = 0; n < count; ++n) {
+    advance(it);
+    const bool nx = n + 1 < count;
+    const UnitInfo u1 = nx ? unit_info(A, it) : cur;
+    step_unit<GATE, B>(A, tile, vin, W, cur, u1, n & 1);
+    cur = u1;
+  }
+}
+
+template <int GATE, bool UNIFORM>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+k_step(StepArgs A) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileMax];
+  __shared__ __attribute__((aligned(16))) VecIn vin;
+  __shared__ __attribute__((aligned(16))) StepWork W;
+  const int lane = threadIdx.x & 63;
+  // Work split. Uniform heads: the groups are partitioned among the width classes in
+  // proportion to their units, and each group takes a contiguous run of its class
+  // (one specialised loop per group). Otherwise: contiguous runs of all units.
+  int k_begin, k_end, cls = 0;
+  UnitIter it;
+  if (UNIFORM) {
+    const int G = (int)gridDim.x;
+    int g0 = 0, hoff = 0;
+    int gc[3], nc[3];
+    for (int c = 0; c < 3; ++c) nc[c] = A.n_req * A.n_class[c];
+    int left = G, nleft = A.n_unit;
+    for (int c = 0; c < 3; ++c) {
+      int g = nleft ? (int)(((long long)left * nc[c] + nleft / 2) / nleft) : 0;
+      if (nc[c] > 0 && g < 1) g = 1;
+      if (g > left) g = left;
+      if (c == 2 || nc[c] == 0) g = nc[c] > 0 ? left : 0;
+      gc[c] = g;
+      left -= g;
+      nleft -= nc[c];
+    }
+    while (cls < 2 && (int)blockIdx.x >= g0 + gc[cls]) {
+      g0 += gc[cls];
+      hoff += A.n_class[cls];
+      ++cls;
+    }
+    const int gi = (int)blockIdx.x - g0, gn = gc[cls];
+    k_begin = (int)(((long long)gi * nc[cls]) / gn);
+    k_end = (int)(((long long)(gi + 1) * nc[cls]) / gn);
+    it.nc = A.n_class[cls];
+    it.hoff = hoff;
+  } else {
+    k_begin = (int)(((long long)blockIdx.x * A.n_unit) / gridDim.x);
+    k_end = (int)(((long long)(blockIdx.x + 1) * A.n_unit) / gridDim.x);
+    it.nc = A.n_head;
+    it.hoff = 0;
+  }
+  if (k_begin >= k_end) return;  // uniform across the group
+  it.r = k_begin / it.nc;
+  it.hi = k_begin - it.r * it.nc;
+  {
+    const UnitInfo u0 = unit_info(A, it);
+    Prefetch f;
+    issue_prefetch<GATE, 0>(A, u0, wave_id(), lane, f);
+    commit_prefetch<GATE, 0>(u0, wave_id(), lane, f, tile, vin);
+    block_sync();
+  }
+  const int count = k_end - k_begin;
+  if constexpr (UNIFORM) {
+    if (cls == 0) step_run<GATE, 8>(A, tile, vin, W, it, count);
+    else if (cls == 1) step_run<GATE, 6>(A, tile, vin, W, it, count);
+    else step_run<GATE, 4>(A, tile, vin, W, it, count);
+  } else {
+    step_run<GATE, 0>(A, tile, vin, W, it, count);
+  }
+}
+
+int g_step_grid[2][2] = {{0, 0}, {0, 0}};
 
 }  // namespace
 
@@ -481,16 +959,43 @@ hipError_t launch_dequantize(const Pool& p, const uint8_t* packed, const float* 
   return hipGetLastError();
 }
 
+// Persistent grid size: resident groups per CU (occupancy query) x CUs, capped by the
+// number of units. Queried once per process and kernel variant (one device per
+// process assumed for the cache; the value only sizes the grid, correctness does not
+// depend on it).
+template <int GATE, bool UNIFORM>
+static int step_grid(int n_unit) {
+  int& g = g_step_grid[GATE][UNIFORM ? 1 : 0];
+  if (g == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<GATE, UNIFORM>,
+                                                       kThreads, 0);
+    g = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+  }
+  return n_unit < g ? n_unit : g;
+}
+
+template <int GATE, bool UNIFORM>
+static void launch_step_variant(const StepArgs& A, hipStream_t s) {
+  hipLaunchKernelGGL((k_step<GATE, UNIFORM>), dim3(step_grid<GATE, UNIFORM>(A.n_unit)),
+                     dim3(kThreads), 0, s, A);
+}
+
 hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, float* cs,
                        const float* q, const float* k, const float* v, const float* a,
                        const float* b, float* o, hipStream_t s) {
   if (p.n_unit == 0) return hipSuccess;
-  if (gate == GDN)
-    hipLaunchKernelGGL(k_step<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, p.meta, p.n_head,
-                       p.req_bytes, packed, rs, cs, q, k, v, a, b, o);
-  else
-    hipLaunchKernelGGL(k_step<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, p.meta, p.n_head,
-                       p.req_bytes, packed, rs, cs, q, k, v, a, b, o);
+  StepArgs A{p.meta, p.n_head, p.n_unit / p.n_head, p.n_unit, p.req_bytes, p.uniform,
+             {p.n_class[0], p.n_class[1], p.n_class[2]}, packed, rs, cs, q, k, v, a, b, o};
+  if (gate == GDN) {
+    if (p.uniform) launch_step_variant<GDN, true>(A, s);
+    else launch_step_variant<GDN, false>(A, s);
+  } else {
+    if (p.uniform) launch_step_variant<KDA, true>(A, s);
+    else launch_step_variant<KDA, false>(A, s);
+  }
   return hipGetLastError();
 }
 

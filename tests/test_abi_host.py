@@ -47,7 +47,7 @@ def test_state_bytes_matches_oracle_layout(oref, gate):
     pool = oref.Pool(7, 32, bits)
     assert L.packed_bytes == 7 * pool.req_bytes
     assert L.scale_bytes == 7 * 32 * 128 * 4
-    assert L.meta_bytes == 64 + 32 * 144
+    assert L.meta_bytes == 64 + 32 * 272 + 64
     assert L.window_bytes == 7 * 32 * (64 * 2 * 128 * 4 + 128 * 4)
 
 
