@@ -365,17 +365,18 @@ __global__ void __launch_bounds__(kThreads) k_dequantize(const void* meta, int n
 // segment w of the current unit: its 32 key positions x 128 rows, 64 entries per lane.
 // At the top of unit n every wave issues the global loads of its own share of unit
 // n+1 (its tile segment and a slice of the input vectors) into registers; they land
-// while unit n is computed and are written to the (single) LDS slot between the third
-// and fourth barriers of unit n, after every wave has finished reading that slot.
+// while unit n's prep and dot products run and are written to the (single) LDS slot
+// right after the second barrier of unit n, when every wave has finished reading that
+// slot and before the register peak of the update.
 //
 // Per unit:
 //   prep  (per wave)    column/row factors, and the digit planes of its segment
 //   phase 1             digit-plane sums on the matrix cores -> partials per row
 //   B1 phase 2          u, w (waves 0-1) and the readout sum (waves 2-3) per row
-//   B2 phase 3          o; dequantize + gate + update; key-row absmax in the wave;
-//                       normalise; per-row partial value-column maxima
-//   B3 phase 4          value-column scales (two waves, alternating per unit); the
-//                       next unit's inputs go to LDS
+//   B2 phase 3          the next unit's inputs to LDS; o; dequantize + gate + update;
+//                       key-row absmax in the wave; normalise; per-row partial
+//                       value-column maxima
+//   B3 phase 4          value-column scales (two waves, alternating per unit)
 //   B4 phase 5          requantize, pack and store the segment; store the scales
 // ------------------------------------------------------------------------------
 constexpr int kTileMax = 16384;  // 128 x 128 codes at 8 bits
@@ -503,6 +504,8 @@ __device__ __forceinline__ int operand_byte(int B, int m) {
 
 // One lane's share of the next unit, held in registers until it is written to LDS.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4* gu32x4_ptr;
+typedef const __attribute__((address_space(1))) float* gf32_ptr;
 
 // One lane's share of the next unit, held in registers until it is written to LDS.
 struct Prefetch {
@@ -539,9 +542,9 @@ __device__ __forceinline__ void issue_prefetch(const StepArgs& A, const UnitInfo
   const uintptr_t off = w == 3 ? (uintptr_t)lane * 16
                                : ((uintptr_t)u.un * kD + (uintptr_t)(lane & 31) * 4) * 4;
   const uintptr_t base = lane >= 32 ? hi : lo;
-  if (vec_lane_active(GATE, w, lane)) f.vec = *reinterpret_cast<const u32x4*>(base + off);
+  if (vec_lane_active(GATE, w, lane)) f.vec = *(gu32x4_ptr)(base + off);
   if (w == 3 && lane < (GATE == GDN ? 2 : 1))
-    f.sc = *reinterpret_cast<const float*>((lane ? pa : (uintptr_t)A.b) + (uintptr_t)u.un * 4);
+    f.sc = *(gf32_ptr)((lane ? pa : (uintptr_t)A.b) + (uintptr_t)u.un * 4);
 }
 
 // Write a prefetched share to the LDS slot.
@@ -636,25 +639,46 @@ __device__ __forceinline__ double combine4(v4i d) {
   return fma((double)pa, 16384.0, (double)pb);
 }
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t shr16x2(uint32_t x, uint16_t a, uint16_t b) {
+  const u16x2 v = __builtin_bit_cast(u16x2, x) >> (u16x2){a, b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Byte selectors that unpack one lane's eight 6-bit fields from the 8 bytes it loads
+// (its 6 bytes start at byte 0 for even jg, byte 2 for odd jg). For a 24-bit group
+// g = bytes (c0, c1, c2): P = (c0 c1 | c1 c2) shifted right by (6, 4) per 16-bit half
+// puts fields 1 and 2 in bytes 0 and 2; Q = (c0 0 | c2 0) shifted by (0, 2) puts
+// fields 0 and 3 there; one more byte select interleaves them.
+struct Sel6 {
+  uint32_t p0, q0, p1, q1;
+};
+
+__device__ __forceinline__ Sel6 sel6_for(int jg) {
+  const uint32_t o = (jg & 1) ? 0x02020202u : 0u;
+  return {0x02010100u + o, 0x0C020C00u + (o & 0x00FF00FFu), 0x05040403u + o,
+          0x0C050C03u + (o & 0x00FF00FFu)};
+}
+
 // Codes of one row as the MFMA B operand: 8 signed bytes (8 bits) or offset-binary
 // bytes (4 and 6 bits), in the byte order of operand_byte.
 template <int B>
-__device__ __forceinline__ long code_operand(Raw raw, int jg) {
-  const Raw x = fix_raw<B>(raw, jg);
+__device__ __forceinline__ long code_operand(Raw raw, int jg, const Sel6& sl) {
   if constexpr (B == 8) {
-    const uint32_t lo = x.lo ^ 0x80808080u, hi = x.hi ^ 0x80808080u;
+    const uint32_t lo = raw.lo ^ 0x80808080u, hi = raw.hi ^ 0x80808080u;
     return (long)(((uint64_t)hi << 32) | lo);
   } else if constexpr (B == 4) {
-    const uint32_t ev = x.lo & 0x0F0F0F0Fu, od = (x.lo >> 4) & 0x0F0F0F0Fu;
+    const uint32_t x = (jg & 1) ? raw.hi : raw.lo;
+    const uint32_t ev = x & 0x0F0F0F0Fu, od = (x >> 4) & 0x0F0F0F0Fu;
     return (long)(((uint64_t)od << 32) | ev);
   } else {
-    // four 6-bit fields of a 24-bit group g -> four bytes
-    const uint32_t g0 = x.lo & 0xFFFFFFu;
-    const uint32_t g1 = __builtin_amdgcn_alignbit(x.hi, x.lo, 24) & 0xFFFFFFu;
-    const uint32_t lo = (g0 & 0x3Fu) | ((g0 << 2) & 0x3F00u) | ((g0 << 4) & 0x3F0000u) |
-                        ((g0 << 6) & 0x3F000000u);
-    const uint32_t hi = (g1 & 0x3Fu) | ((g1 << 2) & 0x3F00u) | ((g1 << 4) & 0x3F0000u) |
-                        ((g1 << 6) & 0x3F000000u);
+    const uint32_t p0 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p0), 6, 4);
+    const uint32_t q0 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.q0), 0, 2);
+    const uint32_t p1 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p1), 6, 4);
+    const uint32_t q1 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.q1), 0, 2);
+    const uint32_t lo = __builtin_amdgcn_perm(p0, q0, 0x02060400u) & 0x3F3F3F3Fu;
+    const uint32_t hi = __builtin_amdgcn_perm(p1, q1, 0x02060400u) & 0x3F3F3F3Fu;
     return (long)(((uint64_t)hi << 32) | lo);
   }
 }
@@ -679,8 +703,17 @@ __device__ __forceinline__ void plane_sums(const StepWork& W, double* upart, con
     const long bias_op = (long)(0x0101010101010101ull * (uint64_t)(1 << (B - 1)));
     corr = combine4(__builtin_amdgcn_mfma_i32_16x16x32_i8(a_op, bias_op, zero, 0, 0, 0));
   }
+  const Sel6 sl = sel6_for(jg);
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) op[rr] = code_operand<B>(lds_row(seg, B, rg + 16 * rr, jg), jg);
+  for (int rr = 0; rr < 8; ++rr) op[rr] = code_operand<B>(lds_row(seg, B, rg + 16 * rr, jg), jg, sl);
+  // Keep the operands as built (they are reused for the update): without this the
+  // compiler re-derives each field from the packed word instead of reading its byte.
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    uint32_t lo = (uint32_t)op[rr], hi = (uint32_t)((uint64_t)op[rr] >> 32);
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    op[rr] = (long)(((uint64_t)hi << 32) | lo);
+  }
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
     // D[plane 4jg+t][row rg of block rr] for t = 0..3
@@ -716,7 +749,9 @@ __device__ __forceinline__ void update_phase(const StepWork& W, int rg, int p0, 
       if constexpr (B == 8) {
         P = (float)(int)(int8_t)(x >> (8 * (e & 3))) * cf[m];  // signed code
       } else {
-        const float field = (float)((x >> (8 * (e & 3))) & 0xFFu);
+        // fields of 4 and 6 bits are below 128: the signed-byte conversion (one SDWA
+        // instruction) reads them unchanged
+        const float field = (float)(int)(int8_t)(x >> (8 * (e & 3)));
         P = fmaf(field, cf[m], nb[m]);  // = fl((field - bias) * cf), exact rewrite
       }
       s[rr][m] = fmaf(wi, km[m], P * rf);
@@ -818,7 +853,9 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   }
   block_sync();  // B2
 
-  // 3. readout; dequantize + gate + update; key-row refit inside the wave; normalise
+  // 3. the next unit's inputs to LDS (every wave is past its last read of the slot);
+  //    readout; dequantize + gate + update; key-row refit inside the wave; normalise
+  commit_prefetch<GATE, B>(nx, w, lane, f, tile, vin);
   if (tid >= kD) {
     const int i = tid - kD;
     const double kq = ((W.kq[0] + W.kq[1]) + W.kq[2]) + W.kq[3];
@@ -832,8 +869,7 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   normalise_rows<kFS>(s, W.invA, rg, p0, w * 4 + jg, W.part.cpart);
   block_sync();  // B3
 
-  // 4. value-column scales; the next unit's inputs to LDS (every wave is past its
-  //    last read of the slot)
+  // 4. value-column scales
   float cm = 0.0f;
   if ((tid >> 7) == odd) {
     const int i = tid & (kD - 1);
@@ -842,7 +878,6 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
     if (cm == 0.0f) cm = 1.0f;
     W.invc[i] = 1.0f / cm;
   }
-  commit_prefetch<GATE, B>(nx, w, lane, f, tile, vin);
   block_sync();  // B4
 
   // 5. requantize and store in place; scales
@@ -870,7 +905,7 @@ __device__ __forceinline__ void step_run(const StepArgs& A, uint8_t* tile, VecIn
 }
 
 template <int GATE, bool UNIFORM>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(UNIFORM ? 3 : 2)))
 k_step(StepArgs A) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileMax];
   __shared__ __attribute__((aligned(16))) VecIn vin;
