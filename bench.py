@@ -26,6 +26,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-updates/s (req x head) and % of HBM roofline, 1024-req mixed 6-bit"
 HBM_PEAK_GBPS = 8000.0
+# non-packed fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+PROFILE = os.path.join(ROOT, "profiles", "k_step_gdn_serving_1024x32.md")
 
 
 def log(msg):
@@ -41,6 +44,25 @@ def algorithmic_bytes(layout, n_unit: int, gate: int) -> int:
     gates = n_unit * 4 * (128 if gate == 1 else 1) + n_unit * 4
     out = n_unit * 128 * 4
     return codes + scales + qkv + gates + out
+
+
+def profile_record():
+    """Machine-readable lines of the committed rocprofv3 summary of the step kernel, or {}
+    when they were taken on a different kernel source than the one built here."""
+    from quantized_delta_rule_03_amd import rocprof_summary
+
+    try:
+        rec = {}
+        with open(PROFILE) as f:
+            for line in f:
+                k, sep, v = line.partition(": ")
+                if sep and k.replace("_", "").isalnum() and " " not in k:
+                    rec[k] = v.strip()
+    except OSError:
+        return {}
+    if rec.get("kernel_source_sha256") != rocprof_summary.kernel_source_sha256(ROOT):
+        return {}
+    return rec
 
 
 def cpu_baseline(w, bits, threads: int, n_req: int, steps: int):
@@ -70,8 +92,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=256)
-    ap.add_argument("--cpu-steps", type=int, default=4)
+    ap.add_argument("--cpu-requests", type=int, default=1024)
+    ap.add_argument("--cpu-steps", type=int, default=8)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step has "
@@ -126,6 +148,15 @@ def main():
     log(f"step kernel: mean {kern_ms.mean()*1e3:.1f} us, median {np.median(kern_ms)*1e3:.1f} us; "
         f"{achieved:.0f} GB/s algorithmic ({100*achieved/HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
 
+    prof = profile_record()
+    traffic = float(prof["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in prof else None
+    valu = None
+    if "SQ_INSTS_VALU" in prof:
+        lane_ops = float(prof["SQ_INSTS_VALU"]) * 64
+        valu = {"lane_ops_per_launch": lane_ops, "achieved": lane_ops / avg_kern_s,
+                "peak": VALU_PEAK_LANE_OPS, "unit": "lane-ops/s",
+                "frac": lane_ops / avg_kern_s / VALU_PEAK_LANE_OPS}
+
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
@@ -153,9 +184,10 @@ def main():
         "hbm_gbps": achieved,
         "pct_hbm_roofline": 100.0 * achieved / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_step<GDN>", "bytes_per_launch": nbytes,
                      "avg_launch_us": avg_kern_s * 1e6},
+        "valu": valu,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
