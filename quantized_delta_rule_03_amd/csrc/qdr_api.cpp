@@ -301,11 +301,27 @@ int qdr_decode_window(const qdr_desc* d, const void* meta, void* packed, float* 
   Geometry g;
   CHECK(check_desc(d, &g));
   if (d->window < 1) return fail(QDR_EUNSUPPORTED, "desc->window = %d: no window mode", d->window);
+  if (d->window > qdr::kWindowMax)
+    return fail(QDR_EUNSUPPORTED, "desc->window = %d exceeds %d", d->window, qdr::kWindowMax);
   if (t < 0 || t >= d->window)
     return fail(QDR_EUNSUPPORTED, "window position t = %d outside [0, %d)", t, d->window);
-  (void)meta; (void)packed; (void)row_scale; (void)col_scale; (void)window_buf;
-  (void)q; (void)k; (void)v; (void)a; (void)b; (void)o; (void)stream;
-  return fail(QDR_EUNSUPPORTED, "qdr_decode_window: not built yet");
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(window_buf, "window_buf", any));
+  CHECK(check_ptr(q, "q", any));
+  CHECK(check_ptr(k, "k", any));
+  CHECK(check_ptr(v, "v", any));
+  CHECK(check_ptr(a, "a", any));
+  CHECK(check_ptr(b, "b", any));
+  CHECK(check_ptr(o, "o", any));
+  return hip_status(qdr::launch_window(pool_of(d, meta, g), d->gate, d->window, t,
+                                       static_cast<uint8_t*>(packed), row_scale, col_scale,
+                                       static_cast<uint8_t*>(window_buf), q, k, v, a, b, o,
+                                       static_cast<hipStream_t>(stream)),
+                    "qdr_decode_window: launch");
 }
 
 const char* qdr_last_error(void) { return g_err.c_str(); }

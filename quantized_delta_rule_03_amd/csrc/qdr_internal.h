@@ -11,6 +11,7 @@ constexpr int kD = 128;          // dk = dv = 128 (STEPQuant page, Fig. 5 / Figu
 constexpr int kSeg = 32;         // key positions per segment (one width per segment)
 constexpr int kThreads = 256;    // one work-group of 4 wave64 per (request, head) unit
 constexpr uint32_t kMetaMagic = 0x31524451u;  // "QDR1"
+constexpr int kWindowMax = 256;  // largest window (tokens) of qdr_decode_window
 
 // Device metadata table: a 64-byte header, then one MetaHead per head.
 struct MetaHeader {
@@ -54,7 +55,7 @@ inline size_t meta_bytes(int n_head) {
 
 // Bytes of one window-buffer slot set per unit: W slots of (kappa[128], delta[128]) fp32
 // plus the running cumulative gate g[128] fp32.
-inline size_t window_unit_bytes(int W) { return (size_t)W * 2 * kD * 4 + (size_t)kD * 4; }
+__host__ __device__ inline size_t window_unit_bytes(int W) { return (size_t)W * 2 * kD * 4 + (size_t)kD * 4; }
 
 struct Pool {
   const void* meta;
@@ -74,5 +75,9 @@ hipError_t launch_dequantize(const Pool& p, const uint8_t* packed, const float* 
 hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, float* cs,
                        const float* q, const float* k, const float* v, const float* a,
                        const float* b, float* o, hipStream_t s);
+// One window token (and, at t = W-1, the fold and requantization).
+hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed, float* rs,
+                         float* cs, uint8_t* buf, const float* q, const float* k, const float* v,
+                         const float* a, const float* b, float* o, hipStream_t s);
 
 }  // namespace qdr

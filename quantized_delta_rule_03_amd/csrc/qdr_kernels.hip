@@ -967,6 +967,339 @@ k_step(StepArgs A) {
   }
 }
 
+// ------------------------------------------------------------------------------
+// window mode
+//
+// The packed state S0 stays fixed for W tokens. With the cumulative gate
+// g_t = a_0 * ... * a_t (per key channel; GDN: the same for all channels) and the
+// buffered keys decayed to time t, Kt_i(t) = k_i * a_{i+1} * ... * a_t (elementwise), the
+// recurrence from S0 unrolls to
+//   S_t = S0 diag(g_t) + sum_{i<=t} w_i Kt_i(t)^T,
+//   w_t = b_t (v_t - S0 (g_t k_t) - sum_{i<t} w_i (Kt_i(t) . k_t)),
+//   o_t = S0 (g_t q_t) + sum_{i<t} w_i (Kt_i(t) . q_t) + (k_t . q_t) w_t.
+// Per token (k_window_token): S0 (g_t k_t) and S0 (g_t q_t) are exact matrix-core
+// digit-plane sums (the prediction machinery of the decode step with the column factor
+// cf_j = fl(g_tj R_j), row factor c_i); the buffered keys are decayed in place and
+// dotted with k_t and q_t, one lane per buffered token; the row sums over buffered
+// tokens run one thread per value row. At t = W-1 (k_window_fold) the buffered
+// updates are folded into the state on the matrix cores (bf16 in, fp32 accumulate,
+// each fp32 operand split into three bf16 parts so the contraction keeps fp32
+// accuracy) and the state is refit and requantized once.
+//
+// Buffer of one unit (fp32): Kt[W][128] (physical key order), Wv[W][128] (value rows),
+// g[128] (physical key order).
+// ------------------------------------------------------------------------------
+constexpr int kWinMax = kWindowMax;
+
+struct WinArgs {
+  const void* meta;
+  int n_head, W, t;
+  uint32_t req_bytes;
+  uint8_t* packed;
+  float* Rs;
+  float* Cs;
+  uint8_t* buf;
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* a;
+  const float* b;
+  float* o;
+};
+
+__device__ __forceinline__ float* win_kt(const WinArgs& A, int u) {
+  return reinterpret_cast<float*>(A.buf + (size_t)u * window_unit_bytes(A.W));
+}
+
+struct WinLds {
+  uint8_t tile[kTileMax];
+  VecIn vin;  // k, q (logical), v, R, C, a := g_t (logical), b, perm
+  StepWork W;
+  float ap[kD];  // token gate, physical order
+  float gt[kD];  // cumulative gate, physical order
+  float qp[kD];  // q, physical order
+  float ab[2][4][kWinMax];  // alpha/beta partials: [which][wave][token]
+  float al[kWinMax], be[kWinMax];
+  float sp[2][2][kD];  // row sums over buffered tokens: [alpha|beta][token parity][row]
+  float xs[kD];        // S0 (g_t k_t) per row
+};
+
+// Unit u's addressing from the metadata (scalar reads).
+__device__ __forceinline__ UnitInfo win_unit(const WinArgs& A, int u) {
+  const int r = u / A.n_head, h = u - (u / A.n_head) * A.n_head;
+  const uint32_t hb = (uint32_t)(sizeof(MetaHeader) + (size_t)h * sizeof(MetaHead)) / 4;
+  UnitInfo x;
+  x.un = (uint32_t)u;
+  x.toff = (uint32_t)r * A.req_bytes + meta_dword(A.meta, hb);
+  x.sb = meta_dword(A.meta, hb + 2);
+  x.h = (uint32_t)h;
+  return x;
+}
+
+template <int GATE>
+__global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
+  __shared__ __attribute__((aligned(16))) WinLds L;
+  const int tid = threadIdx.x;
+  const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
+  const int u = blockIdx.x;
+  const UnitInfo cur = win_unit(A, u);
+  const Seg sg = seg_from(cur.sb, w);
+  const int Bw = sg.bits;
+  const size_t uo = (size_t)u * kD;
+  const int t = A.t, W = A.W;
+  float* Kt = win_kt(A, u);
+  float* Wv = Kt + (size_t)W * kD;
+  float* gbuf = Wv + (size_t)W * kD;
+
+  // 1. the fixed state's tile segment and this token's vectors to LDS
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(A.packed + cur.toff + sg.off) + lane;
+    u32x4* dst = reinterpret_cast<u32x4*>(L.tile + sg.off) + lane;
+    for (int c = 0; c < (Bw >> 1); ++c) dst[64 * c] = src[64 * c];
+  }
+  if (tid < kD) {
+    const int p = tid;
+    const int j = meta_heads(A.meta)[cur.h].perm[p];
+    const float ap = (GATE == KDA) ? A.a[uo + j] : A.a[u];
+    const float g = (t > 0 ? gbuf[p] : 1.0f) * ap;
+    L.ap[p] = ap;
+    L.gt[p] = g;
+    L.vin.a[j] = g;
+    L.vin.perm[p] = (uint8_t)j;
+    L.vin.k[tid] = A.k[uo + tid];
+    L.vin.q[tid] = A.q[uo + tid];
+    L.vin.v[tid] = A.v[uo + tid];
+    L.vin.R[p] = A.Rs[uo + p];
+    L.vin.C[tid] = A.Cs[uo + tid];
+    if (tid == 0) L.vin.b = A.b[u];
+  }
+  __syncthreads();
+  if (tid < kD) L.qp[tid] = L.vin.q[L.vin.perm[tid]];
+
+  // 2. exact S0 (g_t k_t), S0 (g_t q_t): digit planes of cf k and cf q, cf = fl(g_t R)
+  prep<KDA>(L.vin, L.W, w, lane, Bw);
+  wait_lgkm();
+  __builtin_amdgcn_wave_barrier();
+  long op[8];
+  QDR_WIDTH_DISPATCH(0, Bw, (plane_sums<BB>(L.W, L.W.part.upart, L.tile + sg.off, w, rg, jg, op)));
+  __syncthreads();
+  {
+    const int i = tid & (kD - 1);
+    const double* up = &L.W.part.upart[i];
+    if (tid < kD) {
+      double U = 0.0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        U += L.W.scale_u[s] * fma(up[(4 * s) * kDS], 268435456.0, up[(4 * s + 1) * kDS]);
+      L.xs[i] = (float)((double)L.W.rf[i] * U);
+    } else {
+      double O = 0.0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        O += L.W.scale_o[s] * fma(up[(4 * s + 2) * kDS], 268435456.0, up[(4 * s + 3) * kDS]);
+      L.W.osum[i] = O;
+    }
+  }
+
+  // 3. buffered keys: decay by a_t in place; dot with k_t and q_t over this wave's 32
+  //    positions (one lane per buffered token)
+  for (int i = lane; i < t; i += 64) {
+    u32x4* kt = reinterpret_cast<u32x4*>(Kt + (size_t)i * kD + 32 * w);
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      u32x4 x = kt[c];
+      float e[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int p = 32 * w + 4 * c + m;
+        e[m] = __uint_as_float(x[m]) * L.ap[p];
+        sa = fmaf(e[m], L.W.kp[p], sa);
+        sb = fmaf(e[m], L.qp[p], sb);
+        x[m] = __float_as_uint(e[m]);
+      }
+      kt[c] = x;
+    }
+    L.ab[0][w][i] = sa;
+    L.ab[1][w][i] = sb;
+  }
+  __syncthreads();
+  if (tid < t) {
+    L.al[tid] = ((L.ab[0][0][tid] + L.ab[0][1][tid]) + L.ab[0][2][tid]) + L.ab[0][3][tid];
+    L.be[tid] = ((L.ab[1][0][tid] + L.ab[1][1][tid]) + L.ab[1][2][tid]) + L.ab[1][3][tid];
+  }
+  __syncthreads();
+
+  // 4. per value row: sums over buffered tokens (token parity split over the halves)
+  {
+    const int row = tid & (kD - 1), par = tid >> 7;
+    float sa = 0.0f, sb = 0.0f;
+    for (int i = par; i < t; i += 2) {
+      const float wi = Wv[(size_t)i * kD + row];
+      sa = fmaf(L.al[i], wi, sa);
+      sb = fmaf(L.be[i], wi, sb);
+    }
+    L.sp[0][par][row] = sa;
+    L.sp[1][par][row] = sb;
+  }
+  __syncthreads();
+
+  // 5. delta, readout, append
+  if (tid < kD) {
+    const int i = tid;
+    const float pred = L.xs[i] + (L.sp[0][0][i] + L.sp[0][1][i]);
+    const float wt = L.vin.b * (L.vin.v[i] - pred);
+    const double kq = ((L.W.kq[0] + L.W.kq[1]) + L.W.kq[2]) + L.W.kq[3];
+    A.o[uo + i] = (float)(fma((double)L.W.rf[i], L.W.osum[i],
+                              (double)(L.sp[1][0][i] + L.sp[1][1][i])) + (double)wt * kq);
+    Wv[(size_t)t * kD + i] = wt;
+    Kt[(size_t)t * kD + i] = L.W.kp[i];
+    gbuf[i] = L.gt[i];
+  }
+}
+
+// Split an fp32 value into three bf16 parts whose sum is exact.
+__device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
+  h = (__bf16)x;
+  const float r1 = x - (float)h;
+  m = (__bf16)r1;
+  l = (__bf16)(r1 - (float)m);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kFoldChunk = 32;  // buffered tokens per staged chunk (one MFMA k-step)
+
+struct FoldLds {
+  float kt[kFoldChunk][kD];  // decayed keys, physical order
+  float wv[kFoldChunk][kD];  // deltas, value rows
+  float invA[kD];
+  float invc[kD];
+  float cpart[16 * kFS];
+};
+
+// Fold the window into the state and requantize: S = S0 diag(g) + sum_i w_i Kt_i^T.
+template <int GATE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+k_window_fold(WinArgs A) {
+  __shared__ __attribute__((aligned(16))) FoldLds L;
+  const int tid = threadIdx.x;
+  const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
+  const int u = blockIdx.x;
+  const UnitInfo cur = win_unit(A, u);
+  const Seg sg = seg_from(cur.sb, w);
+  const int Bw = sg.bits;
+  const size_t uo = (size_t)u * kD;
+  const int W = A.W;
+  const float* Kt = win_kt(A, u);
+  const float* Wv = Kt + (size_t)W * kD;
+  const float* gbuf = Wv + (size_t)W * kD;
+  const int p0 = 32 * w + 8 * jg;
+
+  // sum_i w_i Kt_i^T on the matrix cores. Output tile (b, rr): rows rg + 16 rr, positions
+  // p0 + 4b + (0..3) of this lane; A = Kt^T (16 positions x 32 tokens), B = Wv (32 tokens
+  // x 16 rows).
+  f32x4 d[2][8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) d[b][rr] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  const int mrow = lane & 15, kg = lane >> 4;
+  for (int i0 = 0; i0 < W; i0 += kFoldChunk) {
+    __syncthreads();
+    for (int e = tid; e < kFoldChunk * kD; e += kThreads) {
+      const int i = i0 + e / kD;
+      const bool in = i < W;
+      L.kt[e / kD][e % kD] = in ? Kt[(size_t)i * kD + e % kD] : 0.0f;
+      L.wv[e / kD][e % kD] = in ? Wv[(size_t)i * kD + e % kD] : 0.0f;
+    }
+    __syncthreads();
+    bf16x8 ah[2], am[2], al[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int pos = 32 * w + 8 * (mrow >> 2) + 4 * b + (mrow & 3);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 h, m, l;
+        split3(L.kt[8 * kg + e][pos], h, m, l);
+        ah[b][e] = h;
+        am[b][e] = m;
+        al[b][e] = l;
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      bf16x8 bh, bm, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 h, m, l;
+        split3(L.wv[8 * kg + e][mrow + 16 * rr], h, m, l);
+        bh[e] = h;
+        bm[e] = m;
+        bl[e] = l;
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f32x4 x = d[b][rr];
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[b], bh, x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[b], bl, x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[b], bm, x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[b], bh, x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[b], bm, x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[b], bh, x, 0, 0, 0);
+        d[b][rr] = x;
+      }
+    }
+  }
+  // S = S0 diag(g) + fold: S'_ij = fl(fl(code cf_j) c_i), cf_j = fl(g_j R_j), in the
+  // lane layout, plus the contraction
+  float s[8][8];
+  {
+    const uint8_t* seg = A.packed + cur.toff + sg.off;
+    Raw raw[8];
+    load_rows(Bw, seg, rg, jg, raw);
+    const float bias = (float)(1 << (Bw - 1));
+    float cf[8], nb[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      cf[m] = gbuf[p0 + m] * A.Rs[uo + p0 + m];
+      nb[m] = -bias * cf[m];
+    }
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const float c = A.Cs[uo + rg + 16 * rr];
+      float f[8];
+      decode_any<0>(Bw, raw[rr], jg, f);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) s[rr][m] = fmaf(f[m], cf[m], nb[m]) * c + d[m >> 2][rr][m & 3];
+    }
+  }
+
+  // refit + requantize (the decode step's rule)
+  const float Rkeep = key_row_refit_split(s, rg, p0, Bw, L.invA);
+  wait_lgkm();
+  __builtin_amdgcn_wave_barrier();
+  normalise_rows<kFS>(s, L.invA, rg, p0, w * 4 + jg, L.cpart);
+  __syncthreads();
+  float cm = 0.0f;
+  if (tid < kD) {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) cm = fmaxf(cm, L.cpart[g * kFS + tid]);
+    if (cm == 0.0f) cm = 1.0f;
+    L.invc[tid] = 1.0f / cm;
+  }
+  __syncthreads();
+  const float qmax = (float)((1 << (Bw - 1)) - 1);
+  float M[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) M[rr] = qmax * L.invc[rg + 16 * rr];
+  uint8_t* gseg = A.packed + cur.toff + sg.off;
+  QDR_WIDTH_DISPATCH(0, Bw, (requant_store<BB>(gseg, rg, jg, s, M)));
+  if (rg < 8) A.Rs[uo + p0 + rg] = Rkeep;
+  if (tid < kD) A.Cs[uo + tid] = cm;
+}
+
 int g_step_grid[2][2] = {{0, 0}, {0, 0}};
 
 }  // namespace
@@ -1030,6 +1363,21 @@ hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, floa
   } else {
     if (p.uniform) launch_step_variant<KDA, true>(A, s);
     else launch_step_variant<KDA, false>(A, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed, float* rs,
+                         float* cs, uint8_t* buf, const float* q, const float* k, const float* v,
+                         const float* a, const float* b, float* o, hipStream_t s) {
+  if (p.n_unit == 0) return hipSuccess;
+  WinArgs A{p.meta, p.n_head, W, t, p.req_bytes, packed, rs, cs, buf, q, k, v, a, b, o};
+  if (gate == GDN) {
+    hipLaunchKernelGGL(k_window_token<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    if (t == W - 1) hipLaunchKernelGGL(k_window_fold<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+  } else {
+    hipLaunchKernelGGL(k_window_token<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    if (t == W - 1) hipLaunchKernelGGL(k_window_fold<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
   }
   return hipGetLastError();
 }

@@ -118,6 +118,12 @@ def test_window_position_validation():
     assert rc == qdr.QDR_EUNSUPPORTED and "t = 64" in qdr.last_error()
     rc = L.qdr_decode_window(ctypes.byref(d), P, P, P, P, P, -1, P, P, P, P, P, P, None)
     assert rc == qdr.QDR_EUNSUPPORTED
+    d, keep = _desc(window=300)
+    rc = L.qdr_decode_window(ctypes.byref(d), P, P, P, P, P, 3, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED and "exceeds" in qdr.last_error()
+    d, keep = _desc(window=64)
+    rc = L.qdr_decode_window(ctypes.byref(d), P, P, P, P, None, 3, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EINVAL and "window_buf" in qdr.last_error()
 
 
 def test_errors_are_thread_local():

@@ -1,0 +1,115 @@
+"""GPU parity of window mode (qdr_decode_window) against the oracle's window reference.
+
+The oracle runs each window as the exact recurrence (fp64) from the dequantized state at
+the window start and requantizes once at its end. The GPU keeps the packed state fixed
+over the window, buffers the per-token updates in fp32 and folds them in on the matrix
+cores at the last token. Bar (same as the decode step): per-token readout rel-L2 <= 1e-4;
+codes after each window, teacher-forced (oracle window started from the GPU's own state),
+within 1 LSB on <= 1e-4 of entries; free-running dequantized-state drift <= 1e-3.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parity_tools import (CODE_FLIP_FRAC, DRIFT_REL_L2, O_REL_L2, bits_for, compare_codes,
+                          gpu_to_oracle, prewarmed_state, rel_l2, to_dev)
+from quantized_delta_rule_03_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_delta_rule_03_amd import qdr
+
+    qdr.lib()
+    return torch
+
+
+def token_inputs(w, t, n_req, n_head):
+    inp = wl.step_inputs(w, t, n_req=n_req)
+    return {k: np.ascontiguousarray(v[:, :n_head]) for k, v in inp.items()}
+
+
+def run_windows(torch, w, n_req, n_head, bits, W, n_windows, S0, name):
+    from quantized_delta_rule_03_amd import qdr
+
+    gpu = qdr.StatePool(n_req, n_head, w.gate, bits, window=W)
+    ref = oracle.Pool(n_req, n_head, bits)
+    ref.quantize(S0)
+    gpu.load_host(ref.packed, ref.row_scale, ref.col_scale)
+    o = torch.empty((n_req, n_head, 128), dtype=torch.float32, device="cuda")
+    worst_o, worst_flip, worst_lsb, worst_o_free = 0.0, 0.0, 0, 0.0
+    for win in range(n_windows):
+        toks = [token_inputs(w, win * W + t, n_req, n_head) for t in range(W)]
+        stack = {k: np.stack([x[k] for x in toks]) for k in toks[0]}
+        tf = gpu_to_oracle(gpu, bits)  # teacher-forced: the GPU's state at the window start
+        o_tf = tf.window(w.gate, stack["q"], stack["k"], stack["v"], stack["a"], stack["b"])
+        o_free = ref.window(w.gate, stack["q"], stack["k"], stack["v"], stack["a"], stack["b"])
+        for t in range(W):
+            dev = to_dev(toks[t])
+            gpu.window_token(t, dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], o)
+            og = o.cpu().numpy()
+            worst_o = max(worst_o, rel_l2(og, o_tf[t]))
+            worst_o_free = max(worst_o_free, rel_l2(og, o_free[t]))
+        g = gpu_to_oracle(gpu, bits)
+        lsb, frac = compare_codes(g.packed, tf.packed, tf)
+        worst_lsb, worst_flip = max(worst_lsb, lsb), max(worst_flip, frac)
+        assert np.allclose(g.row_scale, tf.row_scale, rtol=1e-5, atol=0), name
+        assert np.allclose(g.col_scale, tf.col_scale, rtol=1e-5, atol=0), name
+    drift = rel_l2(gpu_to_oracle(gpu, bits).dequantize(), ref.dequantize())
+    print(f"[{name}] windows={n_windows} W={W} worst o rel-L2 tf={worst_o:.2e} "
+          f"free={worst_o_free:.2e} worst flips tf={worst_flip:.2e} (max {worst_lsb} LSB) "
+          f"drift={drift:.2e}", flush=True)
+    assert worst_o <= O_REL_L2, name
+    assert worst_lsb <= 1 and worst_flip <= CODE_FLIP_FRAC, name
+    assert drift <= DRIFT_REL_L2, name
+
+
+def test_window_kda_8bit_prewarmed(torch_cuda):
+    """Windowed serving shape (KDA, 8-bit, W = 64, pre-warmed outlier states) on a request
+    subset: units are independent, so subset parity is parity for those units."""
+    w = wl.WORKLOADS[4]
+    n_req = 2
+    bits = bits_for(w)
+    S0 = prewarmed_state(w, n_req)
+    run_windows(torch_cuda, w, n_req, w.n_head, bits, w.window, 2, S0, "kda 8-bit W=64")
+
+
+def test_window_gdn_mixed_widths(torch_cuda):
+    w = wl.WORKLOADS[1]
+    bits = bits_for(w)
+    run_windows(torch_cuda, w, 1, w.n_head, bits, 16, 3,
+                np.zeros((1, w.n_head, 128, 128), np.float32), "gdn mixed W=16")
+
+
+def test_window_kda_mixed_widths_prewarmed(torch_cuda):
+    w = wl.WORKLOADS[2]
+    bits = bits_for(w, n_head=8)
+    S0 = prewarmed_state(w, 1)[:, :8]
+    run_windows(torch_cuda, w, 1, 8, bits, 32, 2, np.ascontiguousarray(S0),
+                "kda mixed W=32")
+
+
+@pytest.mark.parametrize("W", [1, 40])
+def test_window_edge_lengths(torch_cuda, W):
+    """W = 1 (fold every token) and a window that is not a multiple of the fold chunk."""
+    w = wl.WORKLOADS[2]
+    bits = bits_for(w, n_head=4)
+    rng = np.random.default_rng(5)
+    S0 = (0.1 * rng.standard_normal((1, 4, 128, 128))).astype(np.float32)
+    run_windows(torch_cuda, w, 1, 4, bits, W, 2, S0, f"kda mixed W={W}")
+
+
+def test_window_zero_requests_is_noop(torch_cuda):
+    from quantized_delta_rule_03_amd import qdr
+
+    w = wl.WORKLOADS[4]
+    gpu = qdr.StatePool(0, 4, w.gate, bits_for(w, n_head=4), window=8)
+    e = torch_cuda.empty((0,), device="cuda")
+    gpu.window_token(7, e, e, e, e, e, e)
+    torch_cuda.cuda.synchronize()
