@@ -65,6 +65,82 @@ def profile_record():
     return rec
 
 
+def window_algorithmic_bytes(tile_bytes: int, n_unit: int, W: int) -> int:
+    """Bytes one window (W tokens + fold) must move: per token the fixed packed state and
+    its scales, q/k/v, the per-channel gate and b, o; the buffered (k, w) pairs of the
+    earlier tokens read and the decayed keys written back, the new pair appended, the
+    cumulative gate read and written; at the end the buffer and state read once more and
+    the requantized state and scales written."""
+    per_unit = 0
+    for t in range(W):
+        per_unit += tile_bytes + 2 * 512      # packed state + key-row and value-column scales
+        per_unit += 3 * 512 + 512 + 4 + 512   # q, k, v, a (per channel), b; o
+        per_unit += 1024 * t + 512 * t        # buffer read (keys, deltas); decayed keys written
+        per_unit += 1024 + (512 if t else 0) + 512  # append (k, w); gate read + written
+    per_unit += tile_bytes + 1024 + 1024 * W + 512  # fold: state, scales, buffer, gate read
+    per_unit += tile_bytes + 1024                   # requantized state and scales written
+    return per_unit * n_unit
+
+
+def bench_window(args, torch, qdr, wl, dev):
+    """Window mode (config: 256 requests x 32 KDA heads, 8-bit, W = 64): time whole windows
+    of W token launches (the last one with the fold)."""
+    w = wl.WORKLOADS[4]
+    bits = wl.uniform_bits(w.n_head, 8)
+    W = w.window
+    pool = qdr.StatePool(w.n_req, w.n_head, w.gate, bits, window=W, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    pool.quantize(0.1 * torch.randn((w.n_req, w.n_head, 128, 128), generator=g, device=dev))
+    a = torch.from_numpy(wl.static_gate(w, args.seed)).to(dev)
+    n_win = max(1, args.steps // W)
+    log(f"generating {W} tokens of inputs on the device")
+    inputs = [wl.device_step_inputs(w, t, dev, args.seed) for t in range(W)]
+    o = torch.empty((w.n_req, w.n_head, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def window():
+        for t in range(W):
+            x = inputs[t]
+            pool.window_token(t, x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
+
+    window()
+    torch.cuda.synchronize()
+    log(f"warmup window done; timing {n_win} windows of {W} tokens")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_win)]
+    t0 = time.perf_counter()
+    for i in range(n_win):
+        ev[i][0].record(stream)
+        window()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    win_s = float(np.mean([s.elapsed_time(e) for s, e in ev])) / 1e3
+    n_unit = w.n_unit
+    nbytes = window_algorithmic_bytes(pool.layout.packed_bytes // w.n_req // w.n_head, n_unit, W)
+    achieved = nbytes / win_s / 1e9
+    tokens = n_win * W
+    log(f"window: {win_s * 1e6 / W:.1f} us per token (fold included); {achieved:.0f} GB/s "
+        f"algorithmic ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    return {
+        "metric": "token-updates/s (req x head), window mode W=64, 256-req KDA 8-bit",
+        "value": n_unit * tokens / wall,
+        "unit": "token-updates/s",
+        "n_gpus": 1, "steps": tokens, "warmup": W, "ms_per_step": wall * 1e3 / tokens,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_req": w.n_req, "n_head": w.n_head, "dk": 128,
+                   "dv": 128, "gate": "KDA per-channel, half-life log-uniform [1, 8192]",
+                   "bits": "8 (uniform)", "window": W, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "k_window_token<KDA> + k_window_fold<KDA>",
+                     "bytes_per_window": nbytes, "avg_window_us": win_s * 1e6},
+        "cpu_baseline": None,
+    }
+
+
 def cpu_baseline(w, bits, threads: int, n_req: int, steps: int):
     import oracle
     from quantized_delta_rule_03_amd import workloads as wl
@@ -94,6 +170,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=1024)
     ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--workload", choices=["serving", "window"], default="serving",
+                    help="serving: the decode-step metric (default); window: window mode")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step has "
@@ -108,6 +186,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "window":
+        print(json.dumps(bench_window(args, torch, qdr, wl, dev)), flush=True)
+        return
     w = wl.WORKLOADS[3]
     bits = qdr.assign_bits(w.gate, wl.halflives(w, args.seed))
     pool = qdr.StatePool(w.n_req, w.n_head, w.gate, bits, device=dev)

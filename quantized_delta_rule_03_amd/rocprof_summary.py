@@ -36,8 +36,11 @@ def counters(path, match):
     return out
 
 
+KERNELS = ("k_step<",)
+
+
 def is_step(name):
-    return "k_step<" in name
+    return any(k in name for k in KERNELS)
 
 
 def is_copy(name):
@@ -56,11 +59,15 @@ def kernel_source_sha256(root):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("dir")
-    ap.add_argument("--copy-bytes", type=float, required=True,
+    ap.add_argument("--copy-bytes", type=float, default=None,
                     help="bytes read (= bytes written) per calibration dispatch")
+    ap.add_argument("--kernels", default="k_step<",
+                    help="comma-separated kernel-name fragments to summarise")
     ap.add_argument("--cmd", action="append", default=[], help="command lines, for the record")
     ap.add_argument("--title", default="k_step, serving workload")
     args = ap.parse_args()
+    global KERNELS
+    KERNELS = tuple(args.kernels.split(","))
     d = args.dir
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -81,6 +88,12 @@ def main():
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
     lines.append("")
 
+    if not os.path.exists(os.path.join(d, "fetch_counter_collection.csv")):
+        lines.append("## Machine-readable")
+        lines.append("")
+        lines.append(f"kernel_source_sha256: {kernel_source_sha256(root)}")
+        print("\n".join(lines))
+        return
     fetch = counters(os.path.join(d, "fetch_counter_collection.csv"), is_step)["FETCH_SIZE"]
     write = counters(os.path.join(d, "write_counter_collection.csv"), is_step)["WRITE_SIZE"]
     cf = counters(os.path.join(d, "cfetch_counter_collection.csv"), is_copy)["FETCH_SIZE"]
