@@ -208,8 +208,8 @@ void oref_dequantize(int dv, int dk, const int8_t *codes, const float *R, const 
                      float *S) {
     for (int i = 0; i < dv; ++i)
         for (int j = 0; j < dk; ++j) {
-            float p = (float)codes[(size_t)i * dk + j] * R[j];
-            S[(size_t)i * dk + j] = p * c[i];
+            float step = R[j] * c[i]; /* the entry's quantization step */
+            S[(size_t)i * dk + j] = (float)codes[(size_t)i * dk + j] * step;
         }
 }
 
@@ -220,7 +220,7 @@ void oref_dequantize(int dv, int dk, const int8_t *codes, const float *R, const 
  *   S' = S diag(a) (KDA) or a S (GDN),  u = S' k,  w = b (v - u),  o = S_new q.
  * S' is the dequantized state with the gate folded into a scale:
  *   GDN: cf_j = R_j, rf_i = fl(a c_i);  KDA: cf_j = fl(a_j R_j), rf_i = c_i;
- *   S'_ij = fl(fl(code_ij cf_j) rf_i).
+ *   S'_ij = fl(code_ij fl(cf_j rf_i))  (the code times its entry's gated step).
  * u_i is the exact dequantized-and-gated row times k, accumulated in fp64 and rounded
  * once: u_i = fl32(rf_i * sum_j code_ij (cf_j k_j)).
  * S_new_ij = fma(w_i, k_j, S'_ij) (one rounding); o_i = fl32(sum_j S_new_ij q_j) in fp64.
@@ -248,8 +248,8 @@ void oref_step(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, flo
     /* S_new = S' + w k^T */
     for (int i = 0; i < dv; ++i)
         for (int j = 0; j < dk; ++j) {
-            float p = (float)codes[(size_t)i * dk + j] * cf[j];
-            float sp = p * rf[i];
+            float step = cf[j] * rf[i];
+            float sp = (float)codes[(size_t)i * dk + j] * step;
             Sn[(size_t)i * dk + j] = fmaf(w[i], k[j], sp);
         }
     /* o = S_new q */

@@ -72,7 +72,8 @@ int oref_unpack(int dv, int dk, const uint8_t *bits, const uint8_t *tile, int8_t
 void oref_quantize(int dv, int dk, const uint8_t *bits, const float *S, int8_t *codes,
                    float *R, float *c);
 
-/* Dequantized state S_hat[i][j] = fl(fl(code*R_j) * c_i). */
+/* Dequantized state S_hat[i][j] = fl(code * fl(R_j * c_i)): the code times the step of
+ * its entry, the product of its key-row and value-column scales. */
 void oref_dequantize(int dv, int dk, const int8_t *codes, const float *R, const float *c,
                      float *S);
 
