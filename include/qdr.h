@@ -120,7 +120,7 @@ int qdr_quantize_state(const qdr_desc *desc, const void *meta, const float *S,
  *   S <- S diag(a) (I - b k k^T) + b v k^T   (GDN: diag(a) = a I)
  * (dev.to page, running-sum section; gate families per the DASC abstract), read out
  * o = S q from the updated fp32 state, then refit the scales and requantize (same rule
- * as qdr_quantize_state). Arithmetic: S'_ij = fl(fl(code*cf_j)*rf_i) with GDN
+ * as qdr_quantize_state). Arithmetic: S'_ij = fl(code * fl(cf_j*rf_i)) with GDN
  * cf_j = R_j, rf_i = fl(a c_i) and KDA cf_j = fl(a_j R_j), rf_i = c_i;
  * u_i = fl32(rf_i * sum_j code_ij (cf_j k_j)) accumulated in fp64;
  * w_i = fl(b fl(v_i - u_i)); S_new_ij = fma(w_i, k_j, S'_ij).
@@ -142,7 +142,7 @@ int qdr_decode_window(const qdr_desc *desc, const void *meta, void *packed,
                       const float *q, const float *k, const float *v, const float *a,
                       const float *b, float *o, void *stream);
 
-/* Read back the dequantized state S_hat_ij = fl(fl(code_ij*R_j)*c_i) as
+/* Read back the dequantized state S_hat_ij = fl(code_ij * fl(R_j*c_i)) as
  * S_out [n_req][n_head][dv][dk] (logical key order). Errors: all codes. */
 int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *packed,
                          const float *row_scale, const float *col_scale, float *S_out,

@@ -15,8 +15,7 @@
 //    before computing the current one, so HBM reads stay in flight during the compute.
 //
 // Arithmetic contract (identical in every rounding to the scalar reference):
-//   dequant + gate   P = fl(code * cf_j) as fma(field, cf_j, -bias*cf_j) (exact),
-//                    S' = fl(P * rf_i)
+//   dequant + gate   S' = fl(code * G_ij), G_ij = fl(cf_j * rf_i) (the entry's gated step)
 //   prediction       u_i = fl32(rf_i * sum_j code_ij (cf_j k_j)) in fp64
 //   delta            w_i = fl(b * fl(v_i - u_i)),  S_new = fma(w_i, k_j, S')
 //   readout          o_i = sum_j S_new_ij q_j (fp32, fixed order)
@@ -321,7 +320,8 @@ __global__ void __launch_bounds__(kThreads) k_quantize(const void* meta, int n_h
 }
 
 // ------------------------------------------------------------------------------
-// dequantize: S_hat[i][j] = fl(fl(code * R_j) * c_i), logical order
+// dequantize: S_hat[i][j] = fl(code * fl(R_j * c_i)), logical order (the code times the
+// step of its entry)
 // ------------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads) k_dequantize(const void* meta, int n_head,
                                                          uint32_t req_bytes,
@@ -338,12 +338,11 @@ __global__ void __launch_bounds__(kThreads) k_dequantize(const void* meta, int n
   const size_t uo = (size_t)u * kD;
   const int p0 = 32 * w + 8 * jg;
   const float bias = (float)(1 << (sg.bits - 1));
-  float R[8], nb[8];
+  float R[8];
   int col[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     R[m] = Rs[uo + p0 + m];
-    nb[m] = -bias * R[m];
     col[m] = mh->identity ? p0 + m : (int)mh->perm[p0 + m];
   }
   float* Su = S + (size_t)u * kD * kD;
@@ -354,7 +353,7 @@ __global__ void __launch_bounds__(kThreads) k_dequantize(const void* meta, int n
     float f[8];
     decode_any<0>(sg.bits, raw[rr], jg, f);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) Su[(size_t)i * kD + col[m]] = fmaf(f[m], R[m], nb[m]) * c;
+    for (int m = 0; m < 8; ++m) Su[(size_t)i * kD + col[m]] = (f[m] - bias) * (R[m] * c);
   }
 }
 
@@ -623,14 +622,17 @@ __device__ __forceinline__ void prep(const VecIn& vin, StepWork& W, int w, int l
     dst[t * 32] = (int8_t)(int)r;  // plane stride: 4 x 8 bytes
   }
   const double kq = half_sum_f64(half ? 0.0 : (double)kk * (double)qq);
+  // the code operands are s*code with s = 1, 16, 4 for 8, 4, 6 bits
+  const int ls = Bw == 8 ? 0 : (Bw == 4 ? 4 : 2);
   if (lane == 0) {
-    W.scale_u[w] = ldexp(1.0, E - 56);
+    W.scale_u[w] = ldexp(1.0, E - 56 - ls);
     W.kq[w] = kq;
   }
-  if (lane == 32) W.scale_o[w] = ldexp(1.0, E - 56);
+  if (lane == 32) W.scale_o[w] = ldexp(1.0, E - 56 - ls);
 }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // four digit-plane sums of one row -> their base-128 combination (exact in fp64)
 __device__ __forceinline__ double combine4(v4i d) {
@@ -646,11 +648,16 @@ __device__ __forceinline__ uint32_t shr16x2(uint32_t x, uint16_t a, uint16_t b) 
   return __builtin_bit_cast(uint32_t, v);
 }
 
+__device__ __forceinline__ uint32_t shl16x2(uint32_t x, uint16_t a, uint16_t b) {
+  const u16x2 v = __builtin_bit_cast(u16x2, x) << (u16x2){a, b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Byte selectors that unpack one lane's eight 6-bit fields from the 8 bytes it loads
 // (its 6 bytes start at byte 0 for even jg, byte 2 for odd jg). For a 24-bit group
-// g = bytes (c0, c1, c2): P = (c0 c1 | c1 c2) shifted right by (6, 4) per 16-bit half
-// puts fields 1 and 2 in bytes 0 and 2; Q = (c0 0 | c2 0) shifted by (0, 2) puts
-// fields 0 and 3 there; one more byte select interleaves them.
+// g = bytes (c0, c1, c2): P = (c0 c1 | c1 c2) shifted right by (4, 2) per 16-bit half
+// puts fields 1 and 2 in bits 2-7 of bytes 0 and 2; Q = (c0 0 | c2 0) shifted left by
+// (2, 0) puts fields 0 and 3 there; one more byte select interleaves them.
 struct Sel6 {
   uint32_t p0, q0, p1, q1;
 };
@@ -661,24 +668,31 @@ __device__ __forceinline__ Sel6 sel6_for(int jg) {
           0x0C050C03u + (o & 0x00FF00FFu)};
 }
 
-// Codes of one row as the MFMA B operand: 8 signed bytes (8 bits) or offset-binary
-// bytes (4 and 6 bits), in the byte order of operand_byte.
+// Codes of one row as signed bytes s*code in the byte order of operand_byte, where
+// s = 1, 16, 4 for 8, 4, 6 bits: each field is moved to the top of its byte and its
+// offset-binary bias removed. These are the MFMA B operand of the dot products and,
+// converted with one signed-byte instruction, the codes of the update.
+template <int B>
+__device__ __forceinline__ constexpr int code_scale() {
+  return B == 8 ? 1 : (B == 4 ? 16 : 4);
+}
+
 template <int B>
 __device__ __forceinline__ long code_operand(Raw raw, int jg, const Sel6& sl) {
   if constexpr (B == 8) {
     const uint32_t lo = raw.lo ^ 0x80808080u, hi = raw.hi ^ 0x80808080u;
     return (long)(((uint64_t)hi << 32) | lo);
   } else if constexpr (B == 4) {
-    const uint32_t x = (jg & 1) ? raw.hi : raw.lo;
-    const uint32_t ev = x & 0x0F0F0F0Fu, od = (x >> 4) & 0x0F0F0F0Fu;
+    const uint32_t x = ((jg & 1) ? raw.hi : raw.lo) ^ 0x88888888u;  // two's complement nibbles
+    const uint32_t ev = (x << 4) & 0xF0F0F0F0u, od = x & 0xF0F0F0F0u;
     return (long)(((uint64_t)od << 32) | ev);
   } else {
-    const uint32_t p0 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p0), 6, 4);
-    const uint32_t q0 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.q0), 0, 2);
-    const uint32_t p1 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p1), 6, 4);
-    const uint32_t q1 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.q1), 0, 2);
-    const uint32_t lo = __builtin_amdgcn_perm(p0, q0, 0x02060400u) & 0x3F3F3F3Fu;
-    const uint32_t hi = __builtin_amdgcn_perm(p1, q1, 0x02060400u) & 0x3F3F3F3Fu;
+    const uint32_t p0 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p0), 4, 2);
+    const uint32_t q0 = shl16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.q0), 2, 0);
+    const uint32_t p1 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p1), 4, 2);
+    const uint32_t q1 = shl16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.q1), 2, 0);
+    const uint32_t lo = (__builtin_amdgcn_perm(p0, q0, 0x02060400u) & 0xFCFCFCFCu) ^ 0x80808080u;
+    const uint32_t hi = (__builtin_amdgcn_perm(p1, q1, 0x02060400u) & 0xFCFCFCFCu) ^ 0x80808080u;
     return (long)(((uint64_t)hi << 32) | lo);
   }
 }
@@ -690,19 +704,13 @@ __device__ __forceinline__ Raw lds_row(const uint8_t* seg, int B, int i, int jg)
 
 // Phase 1 for one code width: the lane's code operands of its 8 rows (kept for the
 // update) and the digit-plane sums of the prediction and the readout, combined per
-// lane (4 planes of one row per 16-row block) into upart.
+// lane (4 planes of one row per 16-row block) into upart. The operands carry the
+// factor code_scale<B>(), which the segment's sum scales remove.
 template <int B>
 __device__ __forceinline__ void plane_sums(const StepWork& W, double* upart, const uint8_t* seg,
                                            int w, int rg, int jg, long (&op)[8]) {
   const long a_op = *reinterpret_cast<const long*>(&W.dig[w][rg][jg][0]);
   const v4i zero = {0, 0, 0, 0};
-  // offset-binary operands (4 and 6 bits): subtract bias * (sum of digits), obtained
-  // from one product with an all-bias operand
-  double corr = 0.0;
-  if constexpr (B != 8) {
-    const long bias_op = (long)(0x0101010101010101ull * (uint64_t)(1 << (B - 1)));
-    corr = combine4(__builtin_amdgcn_mfma_i32_16x16x32_i8(a_op, bias_op, zero, 0, 0, 0));
-  }
   const Sel6 sl = sel6_for(jg);
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) op[rr] = code_operand<B>(lds_row(seg, B, rg + 16 * rr, jg), jg, sl);
@@ -718,21 +726,21 @@ __device__ __forceinline__ void plane_sums(const StepWork& W, double* upart, con
   for (int rr = 0; rr < 8; ++rr) {
     // D[plane 4jg+t][row rg of block rr] for t = 0..3
     const v4i d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a_op, op[rr], zero, 0, 0, 0);
-    upart[(4 * w + jg) * kDS + rg + 16 * rr] = combine4(d) - corr;
+    upart[(4 * w + jg) * kDS + rg + 16 * rr] = combine4(d);
   }
 }
 
 // Phase 3 for one code width: dequantize + gate and apply the rank-one update,
-//   S'_ij = fl(fl(code cf_j) rf_i),  S_new_ij = fma(w_i, k_j, S'_ij).
+//   S'_ij = fl(code_ij G_ij), G_ij = fl(cf_j rf_i),  S_new_ij = fma(w_i, k_j, S'_ij).
+// The code operand holds s*code, so the column factor enters as cf / s (exact).
 template <int B>
 __device__ __forceinline__ void update_phase(const StepWork& W, int rg, int p0, const long (&op)[8],
                                              float (&s)[8][8]) {
-  constexpr float bias = (float)(1 << (B - 1));
-  float cf[8], nb[8], km[8];
+  constexpr float inv_s = 1.0f / (float)code_scale<B>();
+  float cfs[8], km[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    cf[m] = W.cf[p0 + m];
-    nb[m] = -bias * cf[m];
+    cfs[m] = W.cf[p0 + m] * inv_s;
     km[m] = W.kp[p0 + m];
   }
 #pragma unroll
@@ -745,16 +753,8 @@ __device__ __forceinline__ void update_phase(const StepWork& W, int rg, int p0, 
     for (int m = 0; m < 8; ++m) {
       const int e = operand_byte(B, m);
       const uint32_t x = e < 4 ? lo : hi;
-      float P;
-      if constexpr (B == 8) {
-        P = (float)(int)(int8_t)(x >> (8 * (e & 3))) * cf[m];  // signed code
-      } else {
-        // fields of 4 and 6 bits are below 128: the signed-byte conversion (one SDWA
-        // instruction) reads them unchanged
-        const float field = (float)(int)(int8_t)(x >> (8 * (e & 3)));
-        P = fmaf(field, cf[m], nb[m]);  // = fl((field - bias) * cf), exact rewrite
-      }
-      s[rr][m] = fmaf(wi, km[m], P * rf);
+      const float code = (float)(int)(int8_t)(x >> (8 * (e & 3)));  // s * code
+      s[rr][m] = fmaf(wi, km[m], code * (cfs[m] * rf));
     }
   }
 }
@@ -1167,7 +1167,6 @@ __device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l)
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFoldChunk = 32;  // buffered tokens per staged chunk (one MFMA k-step)
 
@@ -1252,7 +1251,7 @@ k_window_fold(WinArgs A) {
       }
     }
   }
-  // S = S0 diag(g) + fold: S'_ij = fl(fl(code cf_j) c_i), cf_j = fl(g_j R_j), in the
+  // S = S0 diag(g) + fold: S'_ij = fl(code fl(cf_j c_i)), cf_j = fl(g_j R_j), in the
   // lane layout, plus the contraction
   float s[8][8];
   {
@@ -1260,19 +1259,16 @@ k_window_fold(WinArgs A) {
     Raw raw[8];
     load_rows(Bw, seg, rg, jg, raw);
     const float bias = (float)(1 << (Bw - 1));
-    float cf[8], nb[8];
+    float cf[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      cf[m] = gbuf[p0 + m] * A.Rs[uo + p0 + m];
-      nb[m] = -bias * cf[m];
-    }
+    for (int m = 0; m < 8; ++m) cf[m] = gbuf[p0 + m] * A.Rs[uo + p0 + m];
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       const float c = A.Cs[uo + rg + 16 * rr];
       float f[8];
       decode_any<0>(Bw, raw[rr], jg, f);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) s[rr][m] = fmaf(f[m], cf[m], nb[m]) * c + d[m >> 2][rr][m & 3];
+      for (int m = 0; m < 8; ++m) s[rr][m] = (f[m] - bias) * (cf[m] * c) + d[m >> 2][rr][m & 3];
     }
   }
 
