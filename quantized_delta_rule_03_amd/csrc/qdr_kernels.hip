@@ -1012,7 +1012,6 @@ __device__ __forceinline__ float* win_kt(const WinArgs& A, int u) {
 }
 
 struct WinLds {
-  uint8_t tile[kTileMax];
   VecIn vin;  // k, q (logical), v, R, C, a := g_t (logical), b, perm
   StepWork W;
   float ap[kD];  // token gate, physical order
@@ -1051,12 +1050,7 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   float* Wv = Kt + (size_t)W * kD;
   float* gbuf = Wv + (size_t)W * kD;
 
-  // 1. the fixed state's tile segment and this token's vectors to LDS
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(A.packed + cur.toff + sg.off) + lane;
-    u32x4* dst = reinterpret_cast<u32x4*>(L.tile + sg.off) + lane;
-    for (int c = 0; c < (Bw >> 1); ++c) dst[64 * c] = src[64 * c];
-  }
+  // 1. this token's vectors to LDS
   if (tid < kD) {
     const int p = tid;
     const int j = meta_heads(A.meta)[cur.h].perm[p];
@@ -1081,7 +1075,9 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   wait_lgkm();
   __builtin_amdgcn_wave_barrier();
   long op[8];
-  QDR_WIDTH_DISPATCH(0, Bw, (plane_sums<BB>(L.W, L.W.part.upart, L.tile + sg.off, w, rg, jg, op)));
+  // (the fixed state's rows are read straight from HBM: each is used once per token)
+  QDR_WIDTH_DISPATCH(0, Bw, (plane_sums<BB>(L.W, L.W.part.upart, A.packed + cur.toff + sg.off, w, rg,
+                                            jg, op)));
   __syncthreads();
   {
     const int i = tid & (kD - 1);
@@ -1130,17 +1126,30 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   }
   __syncthreads();
 
-  // 4. per value row: sums over buffered tokens (token parity split over the halves)
+  // 4. per value row: sums over buffered tokens (token parity split over the halves;
+  //    four independent partial sums per thread keep several loads in flight, combined
+  //    in a fixed order)
   {
     const int row = tid & (kD - 1), par = tid >> 7;
-    float sa = 0.0f, sb = 0.0f;
-    for (int i = par; i < t; i += 2) {
-      const float wi = Wv[(size_t)i * kD + row];
-      sa = fmaf(L.al[i], wi, sa);
-      sb = fmaf(L.be[i], wi, sb);
+    float sa[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int i = par;
+    for (; i + 6 < t; i += 8) {
+      float wv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) wv[u] = Wv[(size_t)(i + 2 * u) * kD + row];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sa[u] = fmaf(L.al[i + 2 * u], wv[u], sa[u]);
+        sb[u] = fmaf(L.be[i + 2 * u], wv[u], sb[u]);
+      }
     }
-    L.sp[0][par][row] = sa;
-    L.sp[1][par][row] = sb;
+    for (int u = 0; i < t; i += 2, ++u) {
+      const float wi = Wv[(size_t)i * kD + row];
+      sa[u] = fmaf(L.al[i], wi, sa[u]);
+      sb[u] = fmaf(L.be[i], wi, sb[u]);
+    }
+    L.sp[0][par][row] = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+    L.sp[1][par][row] = (sb[0] + sb[1]) + (sb[2] + sb[3]);
   }
   __syncthreads();
 
