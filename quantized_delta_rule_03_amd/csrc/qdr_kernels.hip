@@ -111,9 +111,9 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
 }
 
 // t[m]: fp32 bit patterns whose low B bits hold the field and bits B..22 are zero.
-// Every width issues exactly two stores per row (so that the memory-instruction count
-// does not depend on the width): 8-bit dword + dword, 6-bit dword + short (order by
-// alignment), 4-bit short + short.
+// One store per row for 8 bits (8 bytes) and 4 bits (4 bytes): the 4 lanes of a row
+// cover it and a wave-wide store writes 16 consecutive rows as one contiguous block.
+// 6 bits (6 bytes per lane, alternating 4-byte and 2-byte alignment): dword + short.
 template <int B>
 __device__ __forceinline__ void store_row(uint8_t* seg, int row, int jg, const uint32_t t[8]) {
   if constexpr (B == 8) {
@@ -122,16 +122,14 @@ __device__ __forceinline__ void store_row(uint8_t* seg, int row, int jg, const u
     const uint32_t b = perm_b32(t[3], t[2], 0x0c0c0400u);
     const uint32_t c = perm_b32(t[5], t[4], 0x0c0c0400u);
     const uint32_t d = perm_b32(t[7], t[6], 0x0c0c0400u);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(seg + row * 32 + jg * 8);
-    dst[0] = perm_b32(b, a, 0x05040100u);
-    dst[1] = perm_b32(d, c, 0x05040100u);
+    *reinterpret_cast<uint2*>(seg + row * 32 + jg * 8) =
+        make_uint2(perm_b32(b, a, 0x05040100u), perm_b32(d, c, 0x05040100u));
   } else if constexpr (B == 4) {
     // nibble pairs: low byte of (t[2m+1] << 4 | t[2m]) holds fields 2m, 2m+1
     const uint32_t p0 = (t[1] << 4) | t[0], p1 = (t[3] << 4) | t[2];
     const uint32_t p2 = (t[5] << 4) | t[4], p3 = (t[7] << 4) | t[6];
-    uint16_t* dst = reinterpret_cast<uint16_t*>(seg + row * 16 + jg * 4);
-    dst[0] = (uint16_t)perm_b32(p1, p0, 0x0c0c0400u);
-    dst[1] = (uint16_t)perm_b32(p3, p2, 0x0c0c0400u);
+    *reinterpret_cast<uint32_t*>(seg + row * 16 + jg * 4) =
+        perm_b32(perm_b32(p3, p2, 0x0c0c0400u), perm_b32(p1, p0, 0x0c0c0400u), 0x05040100u);
   } else {
     // 24-bit groups of 4 fields; the exponent bits of t (>= bit 23) never reach bits 0..23
     const uint32_t g0 = (t[3] << 18) | (t[2] << 12) | (t[1] << 6) | t[0];
