@@ -169,7 +169,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=1024)
-    ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--cpu-steps", type=int, default=24)
     ap.add_argument("--workload", choices=["serving", "window"], default="serving",
                     help="serving: the decode-step metric (default); window: window mode")
     args = ap.parse_args()

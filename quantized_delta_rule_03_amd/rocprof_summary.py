@@ -65,6 +65,8 @@ def main():
                     help="comma-separated kernel-name fragments to summarise")
     ap.add_argument("--cmd", action="append", default=[], help="command lines, for the record")
     ap.add_argument("--title", default="k_step, serving workload")
+    ap.add_argument("--bench-log", default=None,
+                    help="stderr of the traced bench run: its [bench] lines are quoted")
     args = ap.parse_args()
     global KERNELS
     KERNELS = tuple(args.kernels.split(","))
@@ -75,6 +77,14 @@ def main():
     lines += [f"    {c}" for c in args.cmd]
     lines.append("")
 
+    if args.bench_log:
+        with open(args.bench_log) as f:
+            quoted = [ln.rstrip() for ln in f if ln.startswith("[bench]")]
+        if quoted:
+            lines.append("Traced run, as bench.py reported it (HIP events on the launch stream):")
+            lines.append("")
+            lines += [f"    {ln}" for ln in quoted]
+            lines.append("")
     stats = [r for r in _rows(os.path.join(d, "trace_kernel_stats.csv")) if is_step(r["Name"])]
     lines.append("## Kernel trace (rocprofv3 --kernel-trace --stats)")
     lines.append("")
