@@ -757,29 +757,49 @@ __device__ __forceinline__ void update_phase(const StepWork& W, int rg, int p0, 
   }
 }
 
-// Key-row absmax of the lane-held state over all 128 rows of this wave's segment.
-// Position p0 + (rg & 7) is finished by two lanes: rg < 8 forms R = A / Qmax (kept in
-// a register for the store), rg >= 8 forms 1/A and writes it to LDS.
-__device__ __forceinline__ float key_row_refit_split(const float (&s)[8][8], int rg, int p0, int B,
-                                                     float* invA_lds) {
-  uint32_t am[8];
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t keep, uint32_t send) {
+  return max(keep, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, CTRL, 0xF, 0xF, false));
+}
+
+// Key-row absmax of the lane-held state over all 128 rows of this wave's segment, as a
+// reduce-scatter over the 16 lanes of a DPP row (non-negative floats compared as
+// unsigned): lanes rg, rg^1 split the 8 positions 4/4, then rg, rg^2 split 2/2, then
+// the 4 quads combine (rotations by 4 and 8). Lane rg ends holding positions
+// 4 (rg & 1) + 2 ((rg >> 1) & 1) + {0, 1}; it finishes position
+// pos = 4 (rg & 1) + 2 ((rg >> 1) & 1) + ((rg >> 2) & 1), forming R = A / Qmax when
+// rg < 8 (returned, with pos, for the store) and 1/A otherwise (written to LDS).
+__device__ __forceinline__ float key_row_refit_rs(const float (&s)[8][8], int rg, int p0, int B,
+                                                  float* invA_lds, int& pos) {
+  uint32_t x[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    float x = fmaxf(fmaxf(fabsf(s[0][m]), fabsf(s[1][m])), fabsf(s[2][m]));
-    x = fmaxf(fmaxf(x, fabsf(s[3][m])), fabsf(s[4][m]));
-    x = fmaxf(fmaxf(x, fabsf(s[5][m])), fabsf(s[6][m]));
-    x = fmaxf(x, fabsf(s[7][m]));
-    am[m] = row16_max_u32(__float_as_uint(x));
+    float v = fmaxf(fmaxf(fabsf(s[0][m]), fabsf(s[1][m])), fabsf(s[2][m]));
+    v = fmaxf(fmaxf(v, fabsf(s[3][m])), fabsf(s[4][m]));
+    v = fmaxf(fmaxf(v, fabsf(s[5][m])), fabsf(s[6][m]));
+    x[m] = __float_as_uint(fmaxf(v, fabsf(s[7][m])));
   }
-  uint32_t sel = am[0];
+  const bool b0 = rg & 1, b1 = (rg >> 1) & 1, b2 = (rg >> 2) & 1;
+  uint32_t y[4];
 #pragma unroll
-  for (int m = 1; m < 8; ++m) sel = ((rg & 7) == m) ? am[m] : sel;
-  const float Am = __uint_as_float(sel);
+  for (int i = 0; i < 4; ++i)  // quad [1,0,3,2]
+    y[i] = dpp_max_u32<0xB1>(b0 ? x[i + 4] : x[i], b0 ? x[i] : x[i + 4]);
+  uint32_t z[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)  // quad [2,3,0,1]
+    z[k] = dpp_max_u32<0x4E>(b1 ? y[k + 2] : y[k], b1 ? y[k] : y[k + 2]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    z[k] = dpp_max_u32<0x124>(z[k], z[k]);  // row_ror 4
+    z[k] = dpp_max_u32<0x128>(z[k], z[k]);  // row_ror 8
+  }
+  pos = 4 * (int)b0 + 2 * (int)b1 + (int)b2;
+  const float Am = __uint_as_float(b2 ? z[1] : z[0]);
   const float A = (Am == 0.0f) ? 1.0f : Am;
   const bool rlane = rg < 8;
-  const float x = (rlane ? A : 1.0f) / (rlane ? (float)((1 << (B - 1)) - 1) : A);
-  if (!rlane) invA_lds[p0 + (rg & 7)] = x;
-  return x;
+  const float r = (rlane ? A : 1.0f) / (rlane ? (float)((1 << (B - 1)) - 1) : A);
+  if (!rlane) invA_lds[p0 + pos] = r;
+  return r;
 }
 
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07Fu); }
@@ -861,7 +881,8 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   }
   float s[8][8];
   QDR_WIDTH_DISPATCH(B, Bw, (update_phase<BB>(W, rg, p0, op, s)));
-  const float Rkeep = key_row_refit_split(s, rg, p0, Bw, W.invA);
+  int rpos;
+  const float Rkeep = key_row_refit_rs(s, rg, p0, Bw, W.invA, rpos);
   wait_lgkm();
   __builtin_amdgcn_wave_barrier();
   normalise_rows<kFS>(s, W.invA, rg, p0, w * 4 + jg, W.part.cpart);
@@ -885,7 +906,7 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   for (int rr = 0; rr < 8; ++rr) M[rr] = qmax * W.invc[rg + 16 * rr];
   uint8_t* gseg = A.packed + cur.toff + sg.off;
   QDR_WIDTH_DISPATCH(B, Bw, (requant_store<BB>(gseg, rg, jg, s, M)));
-  if (rg < 8) A.Rs[uo + p0 + rg] = Rkeep;
+  if (rg < 8) A.Rs[uo + p0 + rpos] = Rkeep;
   if ((tid >> 7) == odd) A.Cs[uo + (tid & (kD - 1))] = cm;
 }
 
@@ -1280,7 +1301,8 @@ k_window_fold(WinArgs A) {
   }
 
   // refit + requantize (the decode step's rule)
-  const float Rkeep = key_row_refit_split(s, rg, p0, Bw, L.invA);
+  int rpos;
+  const float Rkeep = key_row_refit_rs(s, rg, p0, Bw, L.invA, rpos);
   wait_lgkm();
   __builtin_amdgcn_wave_barrier();
   normalise_rows<kFS>(s, L.invA, rg, p0, w * 4 + jg, L.cpart);
@@ -1299,7 +1321,7 @@ k_window_fold(WinArgs A) {
   for (int rr = 0; rr < 8; ++rr) M[rr] = qmax * L.invc[rg + 16 * rr];
   uint8_t* gseg = A.packed + cur.toff + sg.off;
   QDR_WIDTH_DISPATCH(0, Bw, (requant_store<BB>(gseg, rg, jg, s, M)));
-  if (rg < 8) A.Rs[uo + p0 + rg] = Rkeep;
+  if (rg < 8) A.Rs[uo + p0 + rpos] = Rkeep;
   if (tid < kD) A.Cs[uo + tid] = cm;
 }
 
