@@ -142,6 +142,22 @@ int qdr_decode_window(const qdr_desc *desc, const void *meta, void *packed,
                       const float *q, const float *k, const float *v, const float *a,
                       const float *b, float *o, void *stream);
 
+/* T known tokens for every unit in one call (teacher-forced replay, prefill, multi-token
+ * verification): the chunked form of window mode (LeapQuant abstract: outputs from the
+ * fixed low-bit state plus high-precision updates, one quantization at the end). The
+ * result is that of T consecutive tokens of qdr_decode_window with W = T: the state is
+ * dequantized once, the gated delta recurrence of qdr_decode_step runs over the T tokens
+ * in fp32 (no requantization inside), o_t = S_t q_t for every token, and the state is
+ * refit and requantized once after token T-1 (same scale rule). In place on
+ * (packed, row_scale, col_scale).
+ * Token-major inputs: q, k: [T][n_req][n_head][dk] (logical key order);
+ * v, o: [T][n_req][n_head][dv]; a: GDN [T][n_req][n_head], KDA [T][n_req][n_head][dk];
+ * b: [T][n_req][n_head]. desc->window is not used; no window buffer. Gates may take any
+ * value in [0, 1]. T = 0 is a no-op. Errors: all codes; QDR_EINVAL if T < 0. */
+int qdr_decode_chunk(const qdr_desc *desc, const void *meta, void *packed, float *row_scale,
+                     float *col_scale, int32_t T, const float *q, const float *k,
+                     const float *v, const float *a, const float *b, float *o, void *stream);
+
 /* Read back the dequantized state S_hat_ij = fl(code_ij * fl(R_j*c_i)) as
  * S_out [n_req][n_head][dv][dk] (logical key order). Errors: all codes. */
 int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *packed,

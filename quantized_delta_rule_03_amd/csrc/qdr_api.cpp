@@ -324,6 +324,29 @@ int qdr_decode_window(const qdr_desc* d, const void* meta, void* packed, float* 
                     "qdr_decode_window: launch");
 }
 
+int qdr_decode_chunk(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
+                     float* col_scale, int32_t T, const float* q, const float* k, const float* v,
+                     const float* a, const float* b, float* o, void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  if (T < 0) return fail(QDR_EINVAL, "T = %d is negative", T);
+  const bool any = d->n_req > 0 && T > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(q, "q", any));
+  CHECK(check_ptr(k, "k", any));
+  CHECK(check_ptr(v, "v", any));
+  CHECK(check_ptr(a, "a", any));
+  CHECK(check_ptr(b, "b", any));
+  CHECK(check_ptr(o, "o", any));
+  return hip_status(qdr::launch_chunk(pool_of(d, meta, g), d->gate, T,
+                                      static_cast<uint8_t*>(packed), row_scale, col_scale, q, k,
+                                      v, a, b, o, static_cast<hipStream_t>(stream)),
+                    "qdr_decode_chunk: launch");
+}
+
 const char* qdr_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

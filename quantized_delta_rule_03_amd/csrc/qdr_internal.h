@@ -80,4 +80,9 @@ hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed,
                          float* cs, uint8_t* buf, const float* q, const float* k, const float* v,
                          const float* a, const float* b, float* o, hipStream_t s);
 
+// T tokens of every unit in one call; token-major inputs [T][unit][...].
+hipError_t launch_chunk(const Pool& p, int gate, int T, uint8_t* packed, float* rs, float* cs,
+                        const float* q, const float* k, const float* v, const float* a,
+                        const float* b, float* o, hipStream_t s);
+
 }  // namespace qdr

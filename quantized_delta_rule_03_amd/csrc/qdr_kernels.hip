@@ -1043,15 +1043,20 @@ struct WinLds {
 };
 
 // Unit u's addressing from the metadata (scalar reads).
-__device__ __forceinline__ UnitInfo win_unit(const WinArgs& A, int u) {
-  const int r = u / A.n_head, h = u - (u / A.n_head) * A.n_head;
+__device__ __forceinline__ UnitInfo win_unit_of(const void* meta, int n_head, uint32_t req_bytes,
+                                                int u) {
+  const int r = u / n_head, h = u - (u / n_head) * n_head;
   const uint32_t hb = (uint32_t)(sizeof(MetaHeader) + (size_t)h * sizeof(MetaHead)) / 4;
   UnitInfo x;
   x.un = (uint32_t)u;
-  x.toff = (uint32_t)r * A.req_bytes + meta_dword(A.meta, hb);
-  x.sb = meta_dword(A.meta, hb + 2);
+  x.toff = (uint32_t)r * req_bytes + meta_dword(meta, hb);
+  x.sb = meta_dword(meta, hb + 2);
   x.h = (uint32_t)h;
   return x;
+}
+
+__device__ __forceinline__ UnitInfo win_unit(const WinArgs& A, int u) {
+  return win_unit_of(A.meta, A.n_head, A.req_bytes, u);
 }
 
 template <int GATE>
@@ -1325,6 +1330,376 @@ k_window_fold(WinArgs A) {
   if (tid < kD) A.Cs[uo + tid] = cm;
 }
 
+// ------------------------------------------------------------------------------
+// chunk mode: T known tokens of every unit in one call
+//
+// The state is dequantized once into fp32 registers and carried through the tokens in
+// sub-blocks of kCB. For a sub-block that starts after token r, with the state S_r at
+// its start and the running gate products gam_t = a_{r+1} ... a_t (per key channel),
+//   delta_t = b_t (v_t - S_r (gam_t k_t) - sum_{i<t} A_ti delta_i),
+//   o_t     = S_r (gam_t q_t) + sum_{i<=t} B_ti delta_i,
+//   A_ti = sum_j k_ij k_tj a_{i+1,j} ... a_{t,j}   (i < t),  B_ti: the same with q_t,
+//   S_{end} = S_r diag(gam_end) + sum_t delta_t (k_t a_{t+1} ... a_end)^T.
+// Every decay factor is a running product of gates, never a ratio of cumulative
+// products, so gate values anywhere in [0, 1] are safe. S_r (gam k), S_r (gam q) and the
+// state update run on the matrix cores with each fp32 operand split into three bf16
+// parts (six partial products, fp32 accumulation); the sub-block Grams A, B and the
+// triangular solve are fp32 VALU. The state is refit and requantized once, after the
+// last token (the scale rule of the decode step).
+//
+// Layout: wave w holds value rows 32w + 16h + rg (h = 0, 1) at key positions
+// 32s + 8jg + e (segment s = 0..3, e = 0..7), so sums over key positions stay inside a
+// wave.
+// ------------------------------------------------------------------------------
+constexpr int kCB = 16;  // tokens per sub-block
+
+struct ChunkArgs {
+  const void* meta;
+  int n_head, n_unit, T;
+  uint32_t req_bytes;
+  uint8_t* packed;
+  float* Rs;
+  float* Cs;
+  const float* q;  // [T][n_unit][128]
+  const float* k;
+  const float* v;
+  const float* a;  // GDN [T][n_unit]; KDA [T][n_unit][128]
+  const float* b;  // [T][n_unit]
+  float* o;        // [T][n_unit][128]
+};
+
+struct ChunkLds {
+  float kp[kCB][kD];  // keys, physical order
+  float qp[kCB][kD];  // queries, physical order; then the deltas [token][row]
+  float ap[kCB][kD];  // gates, physical order; then S_r (gam k) [token][row]
+  float vv[kCB][kD];  // values [token][row]
+  float gm[kCB][kD];  // gam_t, physical order; then S_r (gam q) [token][row]
+  float kt[kCB][kD];  // k_t a_{t+1} ... a_end, physical order
+  float gA[kCB][kCB + 1];
+  float gB[kCB][kCB + 1];
+  float gend[kD];
+  float bb[kCB];
+};
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// sum over the 16 lanes of a DPP row in a fixed tree (lane-dependent association: read
+// the result from one fixed lane)
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return x;
+}
+
+// c += A B with A = ah + am + al and B = bh + bm + bl (bf16 parts of fp32 operands):
+// the six products down to 2^-16 relative, smallest first.
+__device__ __forceinline__ f32x4 mfma6_k32(bf16x8 ah, bf16x8 am, bf16x8 al, bf16x8 bh, bf16x8 bm,
+                                          bf16x8 bl, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bm, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bm, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma6_k16(bf16x4 ah, bf16x4 am, bf16x4 al, bf16x4 bh, bf16x4 bm,
+                                          bf16x4 bl, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bm, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bm, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+}
+
+// requantize and store one row's 8 normalised entries y (scale M = Qmax / c_i)
+template <int B>
+__device__ __forceinline__ void requant_row(uint8_t* seg, int row, int jg, const float (&y)[8],
+                                            float M) {
+  const float magic = 8388608.0f + (float)(1 << (B - 1));
+  uint32_t t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = __float_as_uint(fmaf(y[e], M, magic));
+  store_row<B>(seg, row, jg, t);
+}
+
+template <int GATE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) k_chunk(ChunkArgs A) {
+  __shared__ __attribute__((aligned(16))) ChunkLds L;
+  const int tid = threadIdx.x;
+  const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
+  const int u = blockIdx.x;
+  const UnitInfo cur = win_unit_of(A.meta, A.n_head, A.req_bytes, u);
+  const MetaHead* mh = meta_heads(A.meta) + cur.h;
+  const size_t uo = (size_t)u * kD;
+  const size_t ts = (size_t)A.n_unit * kD;  // token stride of q, k, v, o (and KDA a)
+  const int T = A.T;
+
+  // dequantize: S_ij = fl(code fl(R_j c_i)) (the decode step's readback)
+  float S[2][4][8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const Seg sg = seg_from(cur.sb, s);
+    const uint8_t* seg = A.packed + cur.toff + sg.off;
+    const float bias = (float)(1 << (sg.bits - 1));
+    float R[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) R[e] = A.Rs[uo + 32 * s + 8 * jg + e];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * w + 16 * h + rg;
+      float f[8];
+      decode_any<0>(sg.bits, load_row_any(seg, sg.bits, row, jg), jg, f);
+      const float c = A.Cs[uo + row];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) S[h][s][e] = (f[e] - bias) * (R[e] * c);
+    }
+  }
+  const int pl = tid & (kD - 1);  // physical position of this thread's loads
+  const int jl = mh->identity ? pl : (int)mh->perm[pl];
+
+  for (int t0 = 0; t0 < T; t0 += kCB) {
+    // 1. the sub-block's inputs (tokens past T: k = q = v = 0, a = 1, b = 0)
+#pragma unroll
+    for (int n = 0; n < kCB / 2; ++n) {
+      const int t = 2 * n + (tid >> 7);
+      const bool in = t0 + t < T;
+      const size_t base = (size_t)(t0 + t) * ts + uo;
+      L.kp[t][pl] = in ? A.k[base + jl] : 0.0f;
+      L.qp[t][pl] = in ? A.q[base + jl] : 0.0f;
+      L.vv[t][pl] = in ? A.v[base + pl] : 0.0f;
+      L.ap[t][pl] = in ? ((GATE == KDA) ? A.a[base + jl] : A.a[(size_t)(t0 + t) * A.n_unit + u])
+                       : 1.0f;
+    }
+    if (tid < kCB) L.bb[tid] = (t0 + tid < T) ? A.b[(size_t)(t0 + tid) * A.n_unit + u] : 0.0f;
+    __syncthreads();
+
+    // 2. running gate products (threads 0-127, one key position each) and the Grams
+    if (tid < kD) {
+      float g = 1.0f;
+#pragma unroll
+      for (int t = 0; t < kCB; ++t) {
+        g *= L.ap[t][tid];
+        L.gm[t][tid] = g;
+      }
+      L.gend[tid] = g;
+      float sfx = 1.0f;
+#pragma unroll
+      for (int t = kCB - 1; t >= 0; --t) {
+        L.kt[t][tid] = L.kp[t][tid] * sfx;
+        sfx *= L.ap[t][tid];
+      }
+    }
+    {
+      // lane (i = tid >> 4, g = tid & 15) over key positions 8g..8g+7
+      const int i = tid >> 4, g8 = 8 * (tid & 15);
+      float x[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[c] = L.kp[i][g8 + c];
+#pragma unroll 1
+      for (int t = 0; t < kCB; ++t) {
+        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (t > i) x[c] *= L.ap[t][g8 + c];  // x = k_i a_{i+1} ... a_t
+          sa = fmaf(x[c], L.kp[t][g8 + c], sa);
+          sb = fmaf(x[c], L.qp[t][g8 + c], sb);
+        }
+        sa = row16_sum((t > i) ? sa : 0.0f);
+        sb = row16_sum((t >= i) ? sb : 0.0f);
+        if ((tid & 15) == 0) {
+          L.gA[t][i] = sa;
+          L.gB[t][i] = sb;
+        }
+      }
+    }
+    __syncthreads();
+
+    // 3. S_r (gam_t k_t), S_r (gam_t q_t) on the matrix cores: A = tokens x positions,
+    //    B = the lane's own state entries (positions x rows)
+    f32x4 P[2], Q[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      P[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      Q[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int m = lane & 15, pb0 = 32 * s + 8 * jg;
+      bf16x8 kh, km, kl, qh, qm, ql;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gg = L.gm[m][pb0 + e];
+        __bf16 x0, x1, x2;
+        split3(L.kp[m][pb0 + e] * gg, x0, x1, x2);
+        kh[e] = x0;
+        km[e] = x1;
+        kl[e] = x2;
+        split3(L.qp[m][pb0 + e] * gg, x0, x1, x2);
+        qh[e] = x0;
+        qm[e] = x1;
+        ql[e] = x2;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 bh, bm, bl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16 x0, x1, x2;
+          split3(S[h][s][e], x0, x1, x2);
+          bh[e] = x0;
+          bm[e] = x1;
+          bl[e] = x2;
+        }
+        P[h] = mfma6_k32(kh, km, kl, bh, bm, bl, P[h]);
+        Q[h] = mfma6_k32(qh, qm, ql, bh, bm, bl, Q[h]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * w + 16 * h + rg;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        L.ap[4 * jg + e][row] = P[h][e];
+        L.gm[4 * jg + e][row] = Q[h][e];
+      }
+    }
+    __syncthreads();
+
+    // 4. per value row: the deltas (forward substitution) and the readouts
+    if (tid < kD) {
+      const int row = tid;
+      float d[kCB];
+#pragma unroll
+      for (int t = 0; t < kCB; ++t) {
+        float pred = L.ap[t][row];
+#pragma unroll
+        for (int i = 0; i < t; ++i) pred = fmaf(L.gA[t][i], d[i], pred);
+        d[t] = L.bb[t] * (L.vv[t][row] - pred);
+        L.qp[t][row] = d[t];
+      }
+#pragma unroll
+      for (int t = 0; t < kCB; ++t) {
+        float acc = L.gm[t][row];
+#pragma unroll
+        for (int i = 0; i <= t; ++i) acc = fmaf(L.gB[t][i], d[i], acc);
+        if (t0 + t < T) A.o[(size_t)(t0 + t) * ts + uo + row] = acc;
+      }
+    }
+    __syncthreads();
+
+    // 5. S <- S diag(gam_end) + sum_t delta_t kt_t^T on the matrix cores:
+    //    A = positions x tokens, B = tokens x rows, C = the lane's state entries
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ge = L.gend[32 * s + 8 * jg + e];
+        S[0][s][e] *= ge;
+        S[1][s][e] *= ge;
+      }
+    bf16x4 dh[2], dm[2], dl[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * w + 16 * h + rg;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        __bf16 x0, x1, x2;
+        split3(L.qp[4 * jg + e][row], x0, x1, x2);
+        dh[h][e] = x0;
+        dm[h][e] = x1;
+        dl[h][e] = x2;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq) {
+        const int m = lane & 15;
+        const int pos = 32 * s + 8 * (m >> 2) + 4 * bq + (m & 3);
+        bf16x4 ah, am, al;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          __bf16 x0, x1, x2;
+          split3(L.kt[4 * jg + e][pos], x0, x1, x2);
+          ah[e] = x0;
+          am[e] = x1;
+          al[e] = x2;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 c = {S[h][s][4 * bq], S[h][s][4 * bq + 1], S[h][s][4 * bq + 2], S[h][s][4 * bq + 3]};
+          c = mfma6_k16(ah, am, al, dh[h], dm[h], dl[h], c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[h][s][4 * bq + e] = c[e];
+        }
+      }
+    __syncthreads();
+  }
+
+  // refit + requantize (the decode step's rule). Key-row absmax: the lane's two rows, the
+  // 16 lanes of its DPP row (same positions), then the four waves.
+  float* kmax = &L.vv[0][0];    // [4][128]
+  float* invA = &L.kp[0][0];    // [128]
+  float* invc = &L.kp[1][0];    // [128]
+  float* cpart = &L.kp[2][0];   // [4][128]
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t mx = row16_max_u32(__float_as_uint(fmaxf(fabsf(S[0][s][e]), fabsf(S[1][s][e]))));
+      if (rg == 0) kmax[w * kD + 32 * s + 8 * jg + e] = __uint_as_float(mx);
+    }
+  __syncthreads();
+  if (tid < kD) {
+    const int p = tid;
+    const float Am = fmaxf(fmaxf(kmax[p], kmax[kD + p]), fmaxf(kmax[2 * kD + p], kmax[3 * kD + p]));
+    const float Aa = (Am == 0.0f) ? 1.0f : Am;
+    const int bits = (int)((cur.sb >> (8 * (p >> 5))) & 0xFFu);
+    A.Rs[uo + p] = Aa / (float)((1 << (bits - 1)) - 1);
+    invA[p] = 1.0f / Aa;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float cm = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = S[h][s][e] * invA[32 * s + 8 * jg + e];
+        S[h][s][e] = y;
+        cm = fmaxf(cm, fabsf(y));
+      }
+    cpart[jg * kD + 32 * w + 16 * h + rg] = cm;
+  }
+  __syncthreads();
+  if (tid < kD) {
+    const int i = tid;
+    float cm = fmaxf(fmaxf(cpart[i], cpart[kD + i]), fmaxf(cpart[2 * kD + i], cpart[3 * kD + i]));
+    if (cm == 0.0f) cm = 1.0f;
+    A.Cs[uo + i] = cm;
+    invc[i] = 1.0f / cm;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const Seg sg = seg_from(cur.sb, s);
+    uint8_t* seg = A.packed + cur.toff + sg.off;
+    const float qmax = (float)((1 << (sg.bits - 1)) - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * w + 16 * h + rg;
+      const float M = qmax * invc[row];
+      QDR_WIDTH_DISPATCH(0, sg.bits, (requant_row<BB>(seg, row, jg, S[h][s], M)));
+    }
+  }
+}
+
 int g_step_grid[2][2] = {{0, 0}, {0, 0}};
 
 }  // namespace
@@ -1404,6 +1779,16 @@ hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed,
     hipLaunchKernelGGL(k_window_token<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
     if (t == W - 1) hipLaunchKernelGGL(k_window_fold<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk(const Pool& p, int gate, int T, uint8_t* packed, float* rs, float* cs,
+                        const float* q, const float* k, const float* v, const float* a,
+                        const float* b, float* o, hipStream_t s) {
+  if (p.n_unit == 0 || T == 0) return hipSuccess;
+  ChunkArgs A{p.meta, p.n_head, p.n_unit, T, p.req_bytes, packed, rs, cs, q, k, v, a, b, o};
+  if (gate == GDN) hipLaunchKernelGGL(k_chunk<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+  else hipLaunchKernelGGL(k_chunk<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ GDN = 0
 KDA = 1
 
 SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize_state",
-           "qdr_decode_step", "qdr_decode_window", "qdr_dequantize_state", "qdr_last_error")
+           "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk", "qdr_dequantize_state",
+           "qdr_last_error")
 
 
 class QdrError(RuntimeError):
@@ -62,6 +63,7 @@ def lib():
             "qdr_quantize_state": [D, P, P, P, P, P, P],
             "qdr_decode_step": [D, P, P, P, P, P, P, P, P, P, P, P],
             "qdr_decode_window": [D, P, P, P, P, P, i32, P, P, P, P, P, P, P],
+            "qdr_decode_chunk": [D, P, P, P, P, i32, P, P, P, P, P, P, P],
             "qdr_dequantize_state": [D, P, P, P, P, P, P],
         }
         for name, args in sigs.items():
@@ -164,6 +166,12 @@ def decode_window(L: Layout, meta, packed, row_scale, col_scale, window_buf, t, 
            "qdr_decode_window")
 
 
+def decode_chunk(L: Layout, meta, packed, row_scale, col_scale, T, q, k, v, a, b, o, stream=None):
+    _check(lib().qdr_decode_chunk(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                  _ptr(col_scale), int(T), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                  _ptr(b), _ptr(o), _stream(stream)), "qdr_decode_chunk")
+
+
 def dequantize_state(L: Layout, meta, packed, row_scale, col_scale, S_out, stream=None):
     _check(lib().qdr_dequantize_state(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
                                       _ptr(col_scale), _ptr(S_out), _stream(stream)),
@@ -200,6 +208,11 @@ class StatePool:
     def window_token(self, t, q, k, v, a, b, o, stream=None):
         decode_window(self.layout, self.meta, self.packed, self.row_scale, self.col_scale,
                       self.window_buf, t, q, k, v, a, b, o, stream)
+
+    def chunk(self, q, k, v, a, b, o, stream=None):
+        """T tokens at once; inputs token-major [T, n_req, n_head, ...] (T = b.shape[0])."""
+        decode_chunk(self.layout, self.meta, self.packed, self.row_scale, self.col_scale,
+                     int(b.shape[0]), q, k, v, a, b, o, stream)
 
     def dequantize(self, S_out=None, stream=None):
         import torch

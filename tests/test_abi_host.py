@@ -126,6 +126,18 @@ def test_window_position_validation():
     assert rc == qdr.QDR_EINVAL and "window_buf" in qdr.last_error()
 
 
+def test_chunk_validation():
+    d, keep = _desc()
+    L = qdr.lib()
+    P = 1 << 20
+    rc = L.qdr_decode_chunk(ctypes.byref(d), P, P, P, P, -1, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EINVAL and "T = -1" in qdr.last_error()
+    rc = L.qdr_decode_chunk(ctypes.byref(d), P, P, P, P, 16, P, P, P, P, P, None, None)
+    assert rc == qdr.QDR_EINVAL and "o is NULL" in qdr.last_error()
+    rc = L.qdr_decode_chunk(ctypes.byref(d), P, P, P, P, 16, P, P + 4, P, P, P, P, None)
+    assert rc == qdr.QDR_EALIGN and "k" in qdr.last_error()
+
+
 def test_errors_are_thread_local():
     import threading
 
