@@ -1335,23 +1335,30 @@ k_window_fold(WinArgs A) {
 //
 // The state is dequantized once into fp32 registers and carried through the tokens in
 // sub-blocks of kCB. For a sub-block that starts after token r, with the state S_r at
-// its start and the running gate products gam_t = a_{r+1} ... a_t (per key channel),
+// its start and the gate products gam_t = a_{r+1} ... a_t (per key channel),
 //   delta_t = b_t (v_t - S_r (gam_t k_t) - sum_{i<t} A_ti delta_i),
 //   o_t     = S_r (gam_t q_t) + sum_{i<=t} B_ti delta_i,
 //   A_ti = sum_j k_ij k_tj a_{i+1,j} ... a_{t,j}   (i < t),  B_ti: the same with q_t,
-//   S_{end} = S_r diag(gam_end) + sum_t delta_t (k_t a_{t+1} ... a_end)^T.
-// Every decay factor is a running product of gates, never a ratio of cumulative
-// products, so gate values anywhere in [0, 1] are safe. S_r (gam k), S_r (gam q) and the
-// state update run on the matrix cores with each fp32 operand split into three bf16
-// parts (six partial products, fp32 accumulation); the sub-block Grams A, B and the
-// triangular solve are fp32 VALU. The state is refit and requantized once, after the
-// last token (the scale rule of the decode step).
+//   S_end = S_r diag(gam_end) + sum_t delta_t (k_t a_{t+1} ... a_end)^T.
+// With x_t = b_t (v_t - S_r (gam_t k_t)) and L = diag(b) A: delta = (I + L)^-1 x and
+// o = S_r (gam q) + B (I + L)^-1 x.
+// The Grams are (k gam)(k / gam)^T and (q gam)(k / gam)^T on the matrix cores while
+// every gam_end >= 2^-60 (then k / gam stays far inside the fp32 range); a sub-block
+// with a smaller gate product takes them from running products of the gates read from
+// memory instead (exact for any gates in [0, 1]). S_r (gam k), S_r (gam q), the Grams
+// and the state update run on the matrix cores with each fp32 operand split into three
+// bf16 parts (six partial products, fp32 accumulation). The state is refit and
+// requantized once, after the last token (the scale rule of the decode step).
 //
 // Layout: wave w holds value rows 32w + 16h + rg (h = 0, 1) at key positions
-// 32s + 8jg + e (segment s = 0..3, e = 0..7), so sums over key positions stay inside a
-// wave.
+// 32s + 8jg + e (segment s = 0..3, e = 0..7). A sub-block has two work-group barriers:
+// one between the two halves of the gate products, one after the shared operands are in
+// LDS; everything after that (Grams, products, solve, readout, update) is private to
+// the wave, which owns its rows.
 // ------------------------------------------------------------------------------
-constexpr int kCB = 16;  // tokens per sub-block
+constexpr int kCB = 16;       // tokens per sub-block
+constexpr int kRP = kD + 8;   // bf16 pitch of [token][position] operand rows
+constexpr int kTP = kCB + 4;  // bf16 pitch of [position][token] operand rows
 
 struct ChunkArgs {
   const void* meta;
@@ -1369,29 +1376,26 @@ struct ChunkArgs {
 };
 
 struct ChunkLds {
-  float kp[kCB][kD];  // keys, physical order
-  float qp[kCB][kD];  // queries, physical order; then the deltas [token][row]
-  float ap[kCB][kD];  // gates, physical order; then S_r (gam k) [token][row]
-  float vv[kCB][kD];  // values [token][row]
-  float gm[kCB][kD];  // gam_t, physical order; then S_r (gam q) [token][row]
-  float kt[kCB][kD];  // k_t a_{t+1} ... a_end, physical order
-  float gA[kCB][kCB + 1];
-  float gB[kCB][kCB + 1];
+  __bf16 kpl[3][kCB][kRP];  // k_t gam_t in three bf16 parts, physical order
+  __bf16 qpl[3][kCB][kRP];  // q_t gam_t
+  __bf16 kmi[3][kCB][kRP];  // k_t / gam_t
+  __bf16 ktl[3][kD][kTP];   // k_t a_{t+1} ... a_end, [position][token]
+  float xw[4][kCB][32];     // per wave: x_t of its rows
+  float gw[4][2][kCB][kCB]; // per wave: A, B; then (I + L)^-T, (B (I + L)^-1)^T
+  float ex[2][kD];          // gate products over the two token halves
   float gend[kD];
   float bb[kCB];
 };
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// One thread's share of a sub-block's inputs, loaded one sub-block ahead: tokens
+// 8 (tid >> 7) + n at key position tid & 127 (k, q, a) and the value entries of its
+// lane's readout slots (v).
+struct ChunkPf {
+  float k[8], q[8], a[8], v[8];
+  float b;
+};
 
-// sum over the 16 lanes of a DPP row in a fixed tree (lane-dependent association: read
-// the result from one fixed lane)
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-  return x;
-}
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // c += A B with A = ah + am + al and B = bh + bm + bl (bf16 parts of fp32 operands):
 // the six products down to 2^-16 relative, smallest first.
@@ -1426,8 +1430,13 @@ __device__ __forceinline__ void requant_row(uint8_t* seg, int row, int jg, const
   store_row<B>(seg, row, jg, t);
 }
 
+__device__ __forceinline__ void wave_sync_lds() {
+  wait_lgkm();
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int GATE>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) k_chunk(ChunkArgs A) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) k_chunk(ChunkArgs A) {
   __shared__ __attribute__((aligned(16))) ChunkLds L;
   const int tid = threadIdx.x;
   const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
@@ -1458,90 +1467,121 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       for (int e = 0; e < 8; ++e) S[h][s][e] = (f[e] - bias) * (R[e] * c);
     }
   }
-  const int pl = tid & (kD - 1);  // physical position of this thread's loads
+  const int pl = tid & (kD - 1), half = tid >> 7;
   const int jl = mh->identity ? pl : (int)mh->perm[pl];
+  // indices are clamped into range; tokens past T read as k = q = v = 0, a = 1, b = 0
+  auto issue = [&](int t0, ChunkPf& f) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int tt = t0 + 8 * half + n;
+      const bool in = tt < T;
+      const size_t ti = (size_t)(in ? tt : T - 1);
+      const size_t base = ti * ts + uo;
+      const float kk = A.k[base + jl], qq = A.q[base + jl];
+      const float aa = (GATE == KDA) ? A.a[base + jl] : A.a[ti * A.n_unit + u];
+      f.k[n] = in ? kk : 0.0f;
+      f.q[n] = in ? qq : 0.0f;
+      f.a[n] = in ? aa : 1.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = t0 + 4 * jg + r;
+        const bool in = tt < T;
+        const float vv = A.v[(size_t)(in ? tt : T - 1) * ts + uo + 32 * w + 16 * h + rg];
+        f.v[4 * h + r] = in ? vv : 0.0f;
+      }
+    const int tb = t0 + (tid & (kCB - 1));
+    const float bv = A.b[(size_t)(tb < T ? tb : T - 1) * A.n_unit + u];
+    f.b = tb < T ? bv : 0.0f;
+  };
+  ChunkPf pf;
+  issue(0, pf);
 
   for (int t0 = 0; t0 < T; t0 += kCB) {
-    // 1. the sub-block's inputs (tokens past T: k = q = v = 0, a = 1, b = 0)
-#pragma unroll
-    for (int n = 0; n < kCB / 2; ++n) {
-      const int t = 2 * n + (tid >> 7);
-      const bool in = t0 + t < T;
-      const size_t base = (size_t)(t0 + t) * ts + uo;
-      L.kp[t][pl] = in ? A.k[base + jl] : 0.0f;
-      L.qp[t][pl] = in ? A.q[base + jl] : 0.0f;
-      L.vv[t][pl] = in ? A.v[base + pl] : 0.0f;
-      L.ap[t][pl] = in ? ((GATE == KDA) ? A.a[base + jl] : A.a[(size_t)(t0 + t) * A.n_unit + u])
-                       : 1.0f;
-    }
-    if (tid < kCB) L.bb[tid] = (t0 + tid < T) ? A.b[(size_t)(t0 + tid) * A.n_unit + u] : 0.0f;
-    __syncthreads();
-
-    // 2. running gate products (threads 0-127, one key position each) and the Grams
-    if (tid < kD) {
+    // A1. gate products over this thread's 8 tokens; the two halves exchange totals
+    float gl[8], sl[8];
+    {
       float g = 1.0f;
 #pragma unroll
-      for (int t = 0; t < kCB; ++t) {
-        g *= L.ap[t][tid];
-        L.gm[t][tid] = g;
+      for (int n = 0; n < 8; ++n) {
+        g *= pf.a[n];
+        gl[n] = g;
       }
-      L.gend[tid] = g;
-      float sfx = 1.0f;
+      float sf = 1.0f;
 #pragma unroll
-      for (int t = kCB - 1; t >= 0; --t) {
-        L.kt[t][tid] = L.kp[t][tid] * sfx;
-        sfx *= L.ap[t][tid];
+      for (int n = 7; n >= 0; --n) {
+        sl[n] = sf;
+        sf *= pf.a[n];
       }
+      L.ex[half][pl] = g;
     }
-    {
-      // lane (i = tid >> 4, g = tid & 15) over key positions 8g..8g+7
-      const int i = tid >> 4, g8 = 8 * (tid & 15);
-      float x[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) x[c] = L.kp[i][g8 + c];
-#pragma unroll 1
-      for (int t = 0; t < kCB; ++t) {
-        float sa = 0.0f, sb = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          if (t > i) x[c] *= L.ap[t][g8 + c];  // x = k_i a_{i+1} ... a_t
-          sa = fmaf(x[c], L.kp[t][g8 + c], sa);
-          sb = fmaf(x[c], L.qp[t][g8 + c], sb);
-        }
-        sa = row16_sum((t > i) ? sa : 0.0f);
-        sb = row16_sum((t >= i) ? sb : 0.0f);
-        if ((tid & 15) == 0) {
-          L.gA[t][i] = sa;
-          L.gB[t][i] = sb;
-        }
-      }
-    }
-    __syncthreads();
+    block_sync();
 
-    // 3. S_r (gam_t k_t), S_r (gam_t q_t) on the matrix cores: A = tokens x positions,
-    //    B = the lane's own state entries (positions x rows)
-    f32x4 P[2], Q[2];
+    // A2. shared operands: k gam, q gam, k / gam ([token][position]) and k decayed to
+    //     the sub-block end ([position][token]), each as three bf16 parts
+    {
+      const float G0 = L.ex[0][pl], H1 = L.ex[1][pl];
+      if (half == 0) L.gend[pl] = G0 * H1;
+      __bf16 kt3[3][8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      P[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-      Q[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      for (int n = 0; n < 8; ++n) {
+        const int t = 8 * half + n;
+        const float gam = half ? G0 * gl[n] : gl[n];
+        const float sig = half ? sl[n] : sl[n] * H1;
+        __bf16 x0, x1, x2;
+        split3(pf.k[n] * gam, x0, x1, x2);
+        L.kpl[0][t][pl] = x0;
+        L.kpl[1][t][pl] = x1;
+        L.kpl[2][t][pl] = x2;
+        split3(pf.q[n] * gam, x0, x1, x2);
+        L.qpl[0][t][pl] = x0;
+        L.qpl[1][t][pl] = x1;
+        L.qpl[2][t][pl] = x2;
+        split3(pf.k[n] * __builtin_amdgcn_rcpf(gam), x0, x1, x2);
+        L.kmi[0][t][pl] = x0;
+        L.kmi[1][t][pl] = x1;
+        L.kmi[2][t][pl] = x2;
+        split3(pf.k[n] * sig, kt3[0][n], kt3[1][n], kt3[2][n]);
+      }
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        bf16x8 x;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) x[n] = kt3[c][n];
+        *reinterpret_cast<bf16x8*>(&L.ktl[c][pl][8 * half]) = x;
+      }
+      if (tid < kCB) L.bb[tid] = pf.b;
     }
+    float vcur[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) vcur[n] = pf.v[n];
+    block_sync();
+
+    // B1. per wave: Grams and S_r (gam k), S_r (gam q) on the matrix cores
+    bool safe;
+    {
+      const float g0 = L.gend[lane], g1 = L.gend[64 + lane];
+      safe = __builtin_amdgcn_ballot_w64(!(g0 >= 0x1p-60f && g1 >= 0x1p-60f)) == 0;
+    }
+    f32x4 DA = {0.0f, 0.0f, 0.0f, 0.0f}, DB = DA, P[2] = {DA, DA}, Q[2] = {DA, DA};
+    const int m = lane & 15;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int m = lane & 15, pb0 = 32 * s + 8 * jg;
-      bf16x8 kh, km, kl, qh, qm, ql;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gg = L.gm[m][pb0 + e];
-        __bf16 x0, x1, x2;
-        split3(L.kp[m][pb0 + e] * gg, x0, x1, x2);
-        kh[e] = x0;
-        km[e] = x1;
-        kl[e] = x2;
-        split3(L.qp[m][pb0 + e] * gg, x0, x1, x2);
-        qh[e] = x0;
-        qm[e] = x1;
-        ql[e] = x2;
+      const int pb0 = 32 * s + 8 * jg;
+      bf16x8 kh = *reinterpret_cast<const bf16x8*>(&L.kpl[0][m][pb0]);
+      bf16x8 km = *reinterpret_cast<const bf16x8*>(&L.kpl[1][m][pb0]);
+      bf16x8 kl = *reinterpret_cast<const bf16x8*>(&L.kpl[2][m][pb0]);
+      bf16x8 qh = *reinterpret_cast<const bf16x8*>(&L.qpl[0][m][pb0]);
+      bf16x8 qm = *reinterpret_cast<const bf16x8*>(&L.qpl[1][m][pb0]);
+      bf16x8 ql = *reinterpret_cast<const bf16x8*>(&L.qpl[2][m][pb0]);
+      if (safe) {
+        const bf16x8 ih = *reinterpret_cast<const bf16x8*>(&L.kmi[0][m][pb0]);
+        const bf16x8 im = *reinterpret_cast<const bf16x8*>(&L.kmi[1][m][pb0]);
+        const bf16x8 il = *reinterpret_cast<const bf16x8*>(&L.kmi[2][m][pb0]);
+        DA = mfma6_k32(kh, km, kl, ih, im, il, DA);
+        DB = mfma6_k32(qh, qm, ql, ih, im, il, DB);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -1558,42 +1598,101 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         Q[h] = mfma6_k32(qh, qm, ql, bh, bm, bl, Q[h]);
       }
     }
-    __syncthreads();
+    if (!safe) {
+      // running products of the gates from memory: lane (i = rg, t = 4jg + r)
+      const int i = rg, ti = t0 + i;
+#pragma unroll 1
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * jg + r, tt = t0 + t;
+        float sa = 0.0f, sb = 0.0f;
+        if (t >= i && tt < T) {
+          for (int j = 0; j < kD; ++j) {
+            float x = A.k[(size_t)ti * ts + uo + j];
+            for (int q = i + 1; q <= t; ++q)
+              x *= (GATE == KDA) ? A.a[(size_t)(t0 + q) * ts + uo + j]
+                                 : A.a[(size_t)(t0 + q) * A.n_unit + u];
+            sa = fmaf(x, A.k[(size_t)tt * ts + uo + j], sa);
+            sb = fmaf(x, A.q[(size_t)tt * ts + uo + j], sb);
+          }
+        }
+        DA[r] = sa;
+        DB[r] = sb;
+      }
+    }
+    if (t0 + kCB < T) issue(t0 + kCB, pf);
+    // D[t = 4jg + r][i = rg]: A for i < t, B for i <= t
+    float(*gA)[kCB] = L.gw[w][0];
+    float(*gB)[kCB] = L.gw[w][1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * jg + r;
+      gA[t][rg] = (rg < t) ? DA[r] : 0.0f;
+      gB[t][rg] = (rg <= t) ? DB[r] : 0.0f;
+    }
+    // B2. x_t = b_t (v_t - S_r (gam_t k_t)) for the lane's tokens 4jg + r
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * jg + r;
+        L.xw[w][t][16 * h + rg] = L.bb[t] * (vcur[4 * h + r] - P[h][r]);
+      }
+    wave_sync_lds();
+
+    // B3. lanes 0-15: column c of (I + L)^-1 and of B (I + L)^-1, stored transposed
+    if (lane < kCB) {
+      const int c = lane;
+      float y[kCB], z[kCB];
+#pragma unroll
+      for (int t = 0; t < kCB; ++t) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < t; ++i) acc = fmaf(gA[t][i], y[i], acc);
+        y[t] = (t == c) ? 1.0f : ((t < c) ? 0.0f : -L.bb[t] * acc);
+      }
+#pragma unroll
+      for (int t = 0; t < kCB; ++t) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i <= t; ++i) acc = fmaf(gB[t][i], y[i], acc);
+        z[t] = acc;
+      }
+      wait_lgkm();
+#pragma unroll
+      for (int t = 0; t < kCB; ++t) {
+        gA[c][t] = y[t];
+        gB[c][t] = z[t];
+      }
+    }
+    wave_sync_lds();
+
+    // B4. deltas (kept for the update) and readouts for the lane's tokens and rows
+    f32x4 dd[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 32 * w + 16 * h + rg;
+      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f}, acc = Q[h];
+#pragma unroll 4
+      for (int i = 0; i < kCB; ++i) {
+        const float x = L.xw[w][i][16 * h + rg];
+        const f32x4 ti = *reinterpret_cast<const f32x4*>(&gA[i][4 * jg]);
+        const f32x4 bi = *reinterpret_cast<const f32x4*>(&gB[i][4 * jg]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        L.ap[4 * jg + e][row] = P[h][e];
-        L.gm[4 * jg + e][row] = Q[h][e];
+        for (int r = 0; r < 4; ++r) {
+          d[r] = fmaf(ti[r], x, d[r]);
+          acc[r] = fmaf(bi[r], x, acc[r]);
+        }
+      }
+      dd[h] = d;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * jg + r;
+        if (t0 + t < T) A.o[(size_t)(t0 + t) * ts + uo + row] = acc[r];
       }
     }
-    __syncthreads();
 
-    // 4. per value row: the deltas (forward substitution) and the readouts
-    if (tid < kD) {
-      const int row = tid;
-      float d[kCB];
-#pragma unroll
-      for (int t = 0; t < kCB; ++t) {
-        float pred = L.ap[t][row];
-#pragma unroll
-        for (int i = 0; i < t; ++i) pred = fmaf(L.gA[t][i], d[i], pred);
-        d[t] = L.bb[t] * (L.vv[t][row] - pred);
-        L.qp[t][row] = d[t];
-      }
-#pragma unroll
-      for (int t = 0; t < kCB; ++t) {
-        float acc = L.gm[t][row];
-#pragma unroll
-        for (int i = 0; i <= t; ++i) acc = fmaf(L.gB[t][i], d[i], acc);
-        if (t0 + t < T) A.o[(size_t)(t0 + t) * ts + uo + row] = acc;
-      }
-    }
-    __syncthreads();
-
-    // 5. S <- S diag(gam_end) + sum_t delta_t kt_t^T on the matrix cores:
-    //    A = positions x tokens, B = tokens x rows, C = the lane's state entries
+    // B5. S <- S diag(gam_end) + sum_t delta_t kt_t^T on the matrix cores:
+    //     A = positions x tokens (LDS), B = tokens x rows (the lane's deltas), C = state
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -1604,32 +1703,23 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       }
     bf16x4 dh[2], dm[2], dl[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 32 * w + 16 * h + rg;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int r = 0; r < 4; ++r) {
         __bf16 x0, x1, x2;
-        split3(L.qp[4 * jg + e][row], x0, x1, x2);
-        dh[h][e] = x0;
-        dm[h][e] = x1;
-        dl[h][e] = x2;
+        split3(dd[h][r], x0, x1, x2);
+        dh[h][r] = x0;
+        dm[h][r] = x1;
+        dl[h][r] = x2;
       }
-    }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int bq = 0; bq < 2; ++bq) {
-        const int m = lane & 15;
         const int pos = 32 * s + 8 * (m >> 2) + 4 * bq + (m & 3);
-        bf16x4 ah, am, al;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          __bf16 x0, x1, x2;
-          split3(L.kt[4 * jg + e][pos], x0, x1, x2);
-          ah[e] = x0;
-          am[e] = x1;
-          al[e] = x2;
-        }
+        const bf16x4 ah = *reinterpret_cast<const bf16x4*>(&L.ktl[0][pos][4 * jg]);
+        const bf16x4 am = *reinterpret_cast<const bf16x4*>(&L.ktl[1][pos][4 * jg]);
+        const bf16x4 al = *reinterpret_cast<const bf16x4*>(&L.ktl[2][pos][4 * jg]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           f32x4 c = {S[h][s][4 * bq], S[h][s][4 * bq + 1], S[h][s][4 * bq + 2], S[h][s][4 * bq + 3]};
@@ -1638,15 +1728,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
           for (int e = 0; e < 4; ++e) S[h][s][4 * bq + e] = c[e];
         }
       }
-    __syncthreads();
   }
+  block_sync();
 
   // refit + requantize (the decode step's rule). Key-row absmax: the lane's two rows, the
   // 16 lanes of its DPP row (same positions), then the four waves.
-  float* kmax = &L.vv[0][0];    // [4][128]
-  float* invA = &L.kp[0][0];    // [128]
-  float* invc = &L.kp[1][0];    // [128]
-  float* cpart = &L.kp[2][0];   // [4][128]
+  float* scr = reinterpret_cast<float*>(&L.kpl[0][0][0]);
+  float* kmax = scr;             // [4][128]
+  float* invA = scr + 4 * kD;    // [128]
+  float* invc = scr + 5 * kD;    // [128]
+  float* cpart = scr + 6 * kD;   // [4][128]
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -1654,7 +1745,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       const uint32_t mx = row16_max_u32(__float_as_uint(fmaxf(fabsf(S[0][s][e]), fabsf(S[1][s][e]))));
       if (rg == 0) kmax[w * kD + 32 * s + 8 * jg + e] = __uint_as_float(mx);
     }
-  __syncthreads();
+  block_sync();
   if (tid < kD) {
     const int p = tid;
     const float Am = fmaxf(fmaxf(kmax[p], kmax[kD + p]), fmaxf(kmax[2 * kD + p], kmax[3 * kD + p]));
@@ -1663,7 +1754,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     A.Rs[uo + p] = Aa / (float)((1 << (bits - 1)) - 1);
     invA[p] = 1.0f / Aa;
   }
-  __syncthreads();
+  block_sync();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float cm = 0.0f;
@@ -1677,7 +1768,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       }
     cpart[jg * kD + 32 * w + 16 * h + rg] = cm;
   }
-  __syncthreads();
+  block_sync();
   if (tid < kD) {
     const int i = tid;
     float cm = fmaxf(fmaxf(cpart[i], cpart[kD + i]), fmaxf(cpart[2 * kD + i], cpart[3 * kD + i]));
@@ -1685,7 +1776,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     A.Cs[uo + i] = cm;
     invc[i] = 1.0f / cm;
   }
-  __syncthreads();
+  block_sync();
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const Seg sg = seg_from(cur.sb, s);
