@@ -1340,8 +1340,8 @@ k_window_fold(WinArgs A) {
 //   o_t     = S_r (gam_t q_t) + sum_{i<=t} B_ti delta_i,
 //   A_ti = sum_j k_ij k_tj a_{i+1,j} ... a_{t,j}   (i < t),  B_ti: the same with q_t,
 //   S_end = S_r diag(gam_end) + sum_t delta_t (k_t a_{t+1} ... a_end)^T.
-// With x_t = b_t (v_t - S_r (gam_t k_t)) and L = diag(b) A: delta = (I + L)^-1 x and
-// o = S_r (gam q) + B (I + L)^-1 x.
+// With x_t = b_t (v_t - S_r (gam_t k_t)) and L = diag(b) A: (I + L) delta = x (forward
+// substitution) and o = S_r (gam q) + B delta.
 // The Grams are (k gam)(k / gam)^T and (q gam)(k / gam)^T on the matrix cores while
 // every gam_end >= 2^-60 (then k / gam stays far inside the fp32 range); a sub-block
 // with a smaller gate product takes them from running products of the gates read from
@@ -1381,7 +1381,7 @@ struct ChunkLds {
   __bf16 kmi[3][kCB][kRP];  // k_t / gam_t
   __bf16 ktl[3][kD][kTP];   // k_t a_{t+1} ... a_end, [position][token]
   float xw[4][kCB][32];     // per wave: x_t of its rows
-  float gw[4][2][kCB][kCB]; // per wave: A, B; then (I + L)^-T, (B (I + L)^-1)^T
+  float gw[4][2][kCB][kCB]; // per wave: -L = -diag(b) A and B, [t][i]
   float ex[2][kD];          // gate products over the two token halves
   float gend[kD];
   float bb[kCB];
@@ -1620,13 +1620,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       }
     }
     if (t0 + kCB < T) issue(t0 + kCB, pf);
-    // D[t = 4jg + r][i = rg]: A for i < t, B for i <= t
-    float(*gA)[kCB] = L.gw[w][0];
+    // D[t = 4jg + r][i = rg]: -b_t A_ti for i < t, B_ti for i <= t
+    float(*nL)[kCB] = L.gw[w][0];
     float(*gB)[kCB] = L.gw[w][1];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * jg + r;
-      gA[t][rg] = (rg < t) ? DA[r] : 0.0f;
+      nL[t][rg] = (rg < t) ? -L.bb[t] * DA[r] : 0.0f;
       gB[t][rg] = (rg <= t) ? DB[r] : 0.0f;
     }
     // B2. x_t = b_t (v_t - S_r (gam_t k_t)) for the lane's tokens 4jg + r
@@ -1639,54 +1639,36 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       }
     wave_sync_lds();
 
-    // B3. lanes 0-15: column c of (I + L)^-1 and of B (I + L)^-1, stored transposed
-    if (lane < kCB) {
-      const int c = lane;
-      float y[kCB], z[kCB];
+    // B3. deltas: (I + L) delta = x by forward substitution, one lane per row of the
+    //     wave (column-oriented: the updates of one step are independent)
+    if (lane < 32) {
+      float d[kCB];
 #pragma unroll
-      for (int t = 0; t < kCB; ++t) {
-        float acc = 0.0f;
+      for (int t = 0; t < kCB; ++t) d[t] = L.xw[w][t][lane];
 #pragma unroll
-        for (int i = 0; i < t; ++i) acc = fmaf(gA[t][i], y[i], acc);
-        y[t] = (t == c) ? 1.0f : ((t < c) ? 0.0f : -L.bb[t] * acc);
-      }
+      for (int i = 0; i < kCB - 1; ++i)
 #pragma unroll
-      for (int t = 0; t < kCB; ++t) {
-        float acc = 0.0f;
+        for (int t = i + 1; t < kCB; ++t) d[t] = fmaf(nL[t][i], d[i], d[t]);
 #pragma unroll
-        for (int i = 0; i <= t; ++i) acc = fmaf(gB[t][i], y[i], acc);
-        z[t] = acc;
-      }
-      wait_lgkm();
-#pragma unroll
-      for (int t = 0; t < kCB; ++t) {
-        gA[c][t] = y[t];
-        gB[c][t] = z[t];
-      }
+      for (int t = 0; t < kCB; ++t) L.xw[w][t][lane] = d[t];
     }
     wave_sync_lds();
 
-    // B4. deltas (kept for the update) and readouts for the lane's tokens and rows
+    // B4. readouts o = S_r (gam q) + B delta on the matrix cores (A = B, B = deltas,
+    //     C = S_r (gam q) in the output layout); the lane's deltas for the update
     f32x4 dd[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 32 * w + 16 * h + rg;
-      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f}, acc = Q[h];
-#pragma unroll 4
-      for (int i = 0; i < kCB; ++i) {
-        const float x = L.xw[w][i][16 * h + rg];
-        const f32x4 ti = *reinterpret_cast<const f32x4*>(&gA[i][4 * jg]);
-        const f32x4 bi = *reinterpret_cast<const f32x4*>(&gB[i][4 * jg]);
+      f32x4 acc = Q[h];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          d[r] = fmaf(ti[r], x, d[r]);
-          acc[r] = fmaf(bi[r], x, acc[r]);
-        }
-      }
-      dd[h] = d;
+      for (int ks = 0; ks < 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(gB[m][4 * ks + jg], L.xw[w][4 * ks + jg][16 * h + rg],
+                                                   acc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * jg + r;
+        dd[h][r] = L.xw[w][t][16 * h + rg];
         if (t0 + t < T) A.o[(size_t)(t0 + t) * ts + uo + row] = acc[r];
       }
     }
