@@ -10,6 +10,10 @@ region (inputs already resident in HBM); ``roofline`` prices the step kernel's
 algorithmic bytes per launch against MI355X's 8 TB/s HBM peak, from HIP events around
 every timed launch on the launch stream; ``cpu_baseline`` times the scalar CPU oracle
 on host threads over a bounded sample of the same workload.
+
+``--workload window`` and ``--workload chunk`` time the windowed serving shape (256
+requests x 32 KDA heads, 8-bit, windows of 64 tokens) in window mode (one call per
+token) and in chunk mode (one call per window) instead.
 """
 from __future__ import annotations
 
@@ -141,6 +145,76 @@ def bench_window(args, torch, qdr, wl, dev):
     }
 
 
+def chunk_algorithmic_bytes(tile_bytes: int, n_unit: int, T: int) -> int:
+    """Bytes one chunk call (T tokens) must move: the packed state and its scales read
+    once and written once; per token q, k, v, the per-channel gate and b read and o
+    written."""
+    per_unit = 2 * (tile_bytes + 2 * 512) + T * (3 * 512 + 512 + 4 + 512)
+    return per_unit * n_unit
+
+
+def bench_chunk(args, torch, qdr, wl, dev):
+    """Chunk mode on the windowed serving shape (256 requests x 32 KDA heads, 8-bit): one
+    qdr_decode_chunk call takes the window's T = 64 tokens at once."""
+    w = wl.WORKLOADS[4]
+    bits = wl.uniform_bits(w.n_head, 8)
+    T = w.window
+    pool = qdr.StatePool(w.n_req, w.n_head, w.gate, bits, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    pool.quantize(0.1 * torch.randn((w.n_req, w.n_head, 128, 128), generator=g, device=dev))
+    a1 = torch.from_numpy(wl.static_gate(w, args.seed)).to(dev)
+    n_chunk = max(1, args.steps // T)
+    log(f"generating {T} tokens of inputs on the device")
+    toks = [wl.device_step_inputs(w, t, dev, args.seed) for t in range(T)]
+    x = {k: torch.stack([t[k] for t in toks]).contiguous() for k in toks[0]}
+    a = a1.unsqueeze(0).expand((T,) + tuple(a1.shape)).contiguous()
+    del toks
+    o = torch.empty((T, w.n_req, w.n_head, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def chunk():
+        pool.chunk(x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        chunk()
+    torch.cuda.synchronize()
+    log(f"warmup done; timing {n_chunk} chunks of {T} tokens")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_chunk)]
+    t0 = time.perf_counter()
+    for i in range(n_chunk):
+        ev[i][0].record(stream)
+        chunk()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    chunk_s = float(np.mean([s.elapsed_time(e) for s, e in ev])) / 1e3
+    n_unit = w.n_unit
+    nbytes = chunk_algorithmic_bytes(pool.layout.packed_bytes // w.n_req // w.n_head, n_unit, T)
+    achieved = nbytes / chunk_s / 1e9
+    tokens = n_chunk * T
+    log(f"chunk: {chunk_s * 1e6:.1f} us per {T}-token call, {chunk_s * 1e6 / T:.2f} us per token; "
+        f"{achieved:.0f} GB/s algorithmic ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    return {
+        "metric": "token-updates/s (req x head), chunk mode T=64, 256-req KDA 8-bit",
+        "value": n_unit * tokens / wall,
+        "unit": "token-updates/s",
+        "n_gpus": 1, "steps": tokens, "warmup": max(1, args.warmup) * T,
+        "ms_per_step": wall * 1e3 / tokens,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name + " (chunk)", "n_req": w.n_req, "n_head": w.n_head,
+                   "dk": 128, "dv": 128, "gate": "KDA per-channel, half-life log-uniform [1, 8192]",
+                   "bits": "8 (uniform)", "tokens_per_call": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "k_chunk<KDA>", "bytes_per_call": nbytes,
+                     "avg_call_us": chunk_s * 1e6},
+        "cpu_baseline": None,
+    }
+
+
 def cpu_baseline(w, bits, threads: int, n_req: int, steps: int):
     import oracle
     from quantized_delta_rule_03_amd import workloads as wl
@@ -170,8 +244,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=1024)
     ap.add_argument("--cpu-steps", type=int, default=24)
-    ap.add_argument("--workload", choices=["serving", "window"], default="serving",
-                    help="serving: the decode-step metric (default); window: window mode")
+    ap.add_argument("--workload", choices=["serving", "window", "chunk"], default="serving",
+                    help="serving: the decode-step metric (default); window: window mode "
+                         "(one call per token); chunk: chunk mode (one call per window)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step has "
@@ -188,6 +263,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "window":
         print(json.dumps(bench_window(args, torch, qdr, wl, dev)), flush=True)
+        return
+    if args.workload == "chunk":
+        print(json.dumps(bench_chunk(args, torch, qdr, wl, dev)), flush=True)
         return
     w = wl.WORKLOADS[3]
     bits = qdr.assign_bits(w.gate, wl.halflives(w, args.seed))

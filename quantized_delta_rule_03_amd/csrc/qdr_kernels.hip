@@ -1358,7 +1358,7 @@ k_window_fold(WinArgs A) {
 // ------------------------------------------------------------------------------
 constexpr int kCB = 16;       // tokens per sub-block
 constexpr int kRP = kD + 8;   // bf16 pitch of [token][position] operand rows
-constexpr int kTP = kCB + 4;  // bf16 pitch of [position][token] operand rows
+constexpr int kTP = kCB + 8;  // bf16 pitch of [position][token] operand rows (16-B aligned)
 
 struct ChunkArgs {
   const void* meta;
@@ -1380,12 +1380,21 @@ struct ChunkLds {
   __bf16 qpl[3][kCB][kRP];  // q_t gam_t
   __bf16 kmi[3][kCB][kRP];  // k_t / gam_t
   __bf16 ktl[3][kD][kTP];   // k_t a_{t+1} ... a_end, [position][token]
-  float xw[4][kCB][32];     // per wave: x_t of its rows
-  float gw[4][2][kCB][kCB]; // per wave: -L = -diag(b) A and B, [t][i]
+  float gp[4][2][kCB][kCB]; // Gram partials over each wave's segment, [t][i]
   float ex[2][kD];          // gate products over the two token halves
   float gend[kD];
   float bb[kCB];
 };
+// After the third barrier of a sub-block the operand arrays are dead; each wave then
+// keeps its private arrays there.
+struct ChunkPriv {
+  float g[2][kCB][kCB];  // -L = -diag(b) A and B, [t][i]
+};
+struct ChunkX {
+  float x[kCB][32];  // x_t, then delta_t, of the wave's 32 rows
+};
+static_assert(4 * sizeof(ChunkPriv) <= sizeof(ChunkLds::kpl), "private Grams fit");
+static_assert(4 * sizeof(ChunkX) <= sizeof(ChunkLds::kmi), "private deltas fit");
 
 // One thread's share of a sub-block's inputs, loaded one sub-block ahead: tokens
 // 8 (tid >> 7) + n at key position tid & 127 (k, q, a) and the value entries of its
@@ -1394,8 +1403,6 @@ struct ChunkPf {
   float k[8], q[8], a[8], v[8];
   float b;
 };
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // c += A B with A = ah + am + al and B = bh + bm + bl (bf16 parts of fp32 operands):
 // the six products down to 2^-16 relative, smallest first.
@@ -1407,16 +1414,6 @@ __device__ __forceinline__ f32x4 mfma6_k32(bf16x8 ah, bf16x8 am, bf16x8 al, bf16
   c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bh, c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bm, c, 0, 0, 0);
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma6_k16(bf16x4 ah, bf16x4 am, bf16x4 al, bf16x4 bh, bf16x4 bm,
-                                          bf16x4 bl, f32x4 c) {
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bm, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bh, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bm, c, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
 }
 
 // requantize and store one row's 8 normalised entries y (scale M = Qmax / c_i)
@@ -1559,7 +1556,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     for (int n = 0; n < 8; ++n) vcur[n] = pf.v[n];
     block_sync();
 
-    // B1. per wave: Grams and S_r (gam k), S_r (gam q) on the matrix cores
+    // B1. per wave: S_r (gam k), S_r (gam q) and the Gram partials over the wave's own
+    //     segment on the matrix cores
     bool safe;
     {
       const float g0 = L.gend[lane], g1 = L.gend[64 + lane];
@@ -1576,7 +1574,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       bf16x8 qh = *reinterpret_cast<const bf16x8*>(&L.qpl[0][m][pb0]);
       bf16x8 qm = *reinterpret_cast<const bf16x8*>(&L.qpl[1][m][pb0]);
       bf16x8 ql = *reinterpret_cast<const bf16x8*>(&L.qpl[2][m][pb0]);
-      if (safe) {
+      if (s == w && safe) {
         const bf16x8 ih = *reinterpret_cast<const bf16x8*>(&L.kmi[0][m][pb0]);
         const bf16x8 im = *reinterpret_cast<const bf16x8*>(&L.kmi[1][m][pb0]);
         const bf16x8 il = *reinterpret_cast<const bf16x8*>(&L.kmi[2][m][pb0]);
@@ -1599,14 +1597,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       }
     }
     if (!safe) {
-      // running products of the gates from memory: lane (i = rg, t = 4jg + r)
+      // running products of the gates from memory over logical channels 32w..32w+31:
+      // lane (i = rg, t = 4jg + r)
       const int i = rg, ti = t0 + i;
 #pragma unroll 1
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * jg + r, tt = t0 + t;
         float sa = 0.0f, sb = 0.0f;
         if (t >= i && tt < T) {
-          for (int j = 0; j < kD; ++j) {
+          for (int j = 32 * w; j < 32 * w + 32; ++j) {
             float x = A.k[(size_t)ti * ts + uo + j];
             for (int q = i + 1; q <= t; ++q)
               x *= (GATE == KDA) ? A.a[(size_t)(t0 + q) * ts + uo + j]
@@ -1620,22 +1619,33 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       }
     }
     if (t0 + kCB < T) issue(t0 + kCB, pf);
-    // D[t = 4jg + r][i = rg]: -b_t A_ti for i < t, B_ti for i <= t
-    float(*nL)[kCB] = L.gw[w][0];
-    float(*gB)[kCB] = L.gw[w][1];
+    // partials D[t = 4jg + r][i = rg]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 4 * jg + r;
-      nL[t][rg] = (rg < t) ? -L.bb[t] * DA[r] : 0.0f;
-      gB[t][rg] = (rg <= t) ? DB[r] : 0.0f;
+      L.gp[w][0][4 * jg + r][rg] = DA[r];
+      L.gp[w][1][4 * jg + r][rg] = DB[r];
     }
-    // B2. x_t = b_t (v_t - S_r (gam_t k_t)) for the lane's tokens 4jg + r
+    block_sync();
+
+    // B2. the wave's Grams (-b_t A_ti for i < t, B_ti for i <= t; partials summed in a
+    //     fixed order) and x_t = b_t (v_t - S_r (gam_t k_t)) for the lane's tokens
+    float(*nL)[kCB] = reinterpret_cast<ChunkPriv*>(&L.kpl[0][0][0])[w].g[0];
+    float(*gB)[kCB] = reinterpret_cast<ChunkPriv*>(&L.kpl[0][0][0])[w].g[1];
+    float(*xw)[32] = reinterpret_cast<ChunkX*>(&L.kmi[0][0][0])[w].x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane + 64 * k, t = e >> 4, i = e & 15;
+      const float sa = ((L.gp[0][0][t][i] + L.gp[1][0][t][i]) + L.gp[2][0][t][i]) + L.gp[3][0][t][i];
+      const float sb = ((L.gp[0][1][t][i] + L.gp[1][1][t][i]) + L.gp[2][1][t][i]) + L.gp[3][1][t][i];
+      nL[t][i] = (i < t) ? -L.bb[t] * sa : 0.0f;
+      gB[t][i] = (i <= t) ? sb : 0.0f;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * jg + r;
-        L.xw[w][t][16 * h + rg] = L.bb[t] * (vcur[4 * h + r] - P[h][r]);
+        xw[t][16 * h + rg] = L.bb[t] * (vcur[4 * h + r] - P[h][r]);
       }
     wave_sync_lds();
 
@@ -1644,37 +1654,37 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     if (lane < 32) {
       float d[kCB];
 #pragma unroll
-      for (int t = 0; t < kCB; ++t) d[t] = L.xw[w][t][lane];
+      for (int t = 0; t < kCB; ++t) d[t] = xw[t][lane];
 #pragma unroll
       for (int i = 0; i < kCB - 1; ++i)
 #pragma unroll
         for (int t = i + 1; t < kCB; ++t) d[t] = fmaf(nL[t][i], d[i], d[t]);
 #pragma unroll
-      for (int t = 0; t < kCB; ++t) L.xw[w][t][lane] = d[t];
+      for (int t = 0; t < kCB; ++t) xw[t][lane] = d[t];
     }
     wave_sync_lds();
 
     // B4. readouts o = S_r (gam q) + B delta on the matrix cores (A = B, B = deltas,
-    //     C = S_r (gam q) in the output layout); the lane's deltas for the update
-    f32x4 dd[2];
+    //     C = S_r (gam q) in the output layout)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 32 * w + 16 * h + rg;
       f32x4 acc = Q[h];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(gB[m][4 * ks + jg], L.xw[w][4 * ks + jg][16 * h + rg],
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(gB[m][4 * ks + jg], xw[4 * ks + jg][16 * h + rg],
                                                    acc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * jg + r;
-        dd[h][r] = L.xw[w][t][16 * h + rg];
         if (t0 + t < T) A.o[(size_t)(t0 + t) * ts + uo + row] = acc[r];
       }
     }
 
-    // B5. S <- S diag(gam_end) + sum_t delta_t kt_t^T on the matrix cores:
-    //     A = positions x tokens (LDS), B = tokens x rows (the lane's deltas), C = state
+    // B5. S <- S diag(gam_end) + sum_t delta_t kt_t^T on the matrix cores. The k index
+    //     runs over two copies of the 16 tokens so that one 16x16x32 step adds two of
+    //     the six part products: A = positions x [part X | part Y] (LDS), B = the
+    //     lane's deltas of tokens 8 (jg & 1) + e, C = state.
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -1683,29 +1693,38 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
         S[0][s][e] *= ge;
         S[1][s][e] *= ge;
       }
-    bf16x4 dh[2], dm[2], dl[2];
+    const bool lo_k = jg < 2;
+    const int tk = 8 * (jg & 1);
+    bf16x8 d1[2], d2[2], d3[2];  // B operands of the three steps
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 dh, dm, dl;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int e = 0; e < 8; ++e) {
         __bf16 x0, x1, x2;
-        split3(dd[h][r], x0, x1, x2);
-        dh[h][r] = x0;
-        dm[h][r] = x1;
-        dl[h][r] = x2;
+        split3(xw[tk + e][16 * h + rg], x0, x1, x2);
+        dh[e] = x0;
+        dm[e] = x1;
+        dl[e] = x2;
       }
+      d1[h] = dh;                // [dh ; dh]
+      d2[h] = dm;                // [dm ; dm]
+      d3[h] = lo_k ? dh : dl;    // [dh ; dl]
+    }
+    const int p12 = lo_k ? 0 : 1, p3 = lo_k ? 2 : 0;  // A parts: [h | m], [l | h]
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int bq = 0; bq < 2; ++bq) {
         const int pos = 32 * s + 8 * (m >> 2) + 4 * bq + (m & 3);
-        const bf16x4 ah = *reinterpret_cast<const bf16x4*>(&L.ktl[0][pos][4 * jg]);
-        const bf16x4 am = *reinterpret_cast<const bf16x4*>(&L.ktl[1][pos][4 * jg]);
-        const bf16x4 al = *reinterpret_cast<const bf16x4*>(&L.ktl[2][pos][4 * jg]);
+        const bf16x8 a12 = *reinterpret_cast<const bf16x8*>(&L.ktl[p12][pos][tk]);
+        const bf16x8 a3 = *reinterpret_cast<const bf16x8*>(&L.ktl[p3][pos][tk]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           f32x4 c = {S[h][s][4 * bq], S[h][s][4 * bq + 1], S[h][s][4 * bq + 2], S[h][s][4 * bq + 3]};
-          c = mfma6_k16(ah, am, al, dh[h], dm[h], dl[h], c);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, d3[h], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a12, d2[h], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a12, d1[h], c, 0, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[h][s][4 * bq + e] = c[e];
         }
