@@ -1581,20 +1581,30 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
         DA = mfma6_k32(kh, km, kl, ih, im, il, DA);
         DB = mfma6_k32(qh, qm, ql, ih, im, il, DB);
       }
+      bf16x8 bh[2], bm[2], bl[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 bh, bm, bl;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           __bf16 x0, x1, x2;
           split3(S[h][s][e], x0, x1, x2);
-          bh[e] = x0;
-          bm[e] = x1;
-          bl[e] = x2;
+          bh[h][e] = x0;
+          bm[h][e] = x1;
+          bl[h][e] = x2;
         }
-        P[h] = mfma6_k32(kh, km, kl, bh, bm, bl, P[h]);
-        Q[h] = mfma6_k32(qh, qm, ql, bh, bm, bl, Q[h]);
-      }
+      // the six part products, smallest first, over four independent accumulators
+#define QDR_P4(AP, BP)                                                   \
+  P[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k##AP, BP[0], P[0], 0, 0, 0); \
+  P[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k##AP, BP[1], P[1], 0, 0, 0); \
+  Q[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q##AP, BP[0], Q[0], 0, 0, 0); \
+  Q[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q##AP, BP[1], Q[1], 0, 0, 0);
+      QDR_P4(l, bh)
+      QDR_P4(h, bl)
+      QDR_P4(m, bm)
+      QDR_P4(m, bh)
+      QDR_P4(h, bm)
+      QDR_P4(h, bh)
+#undef QDR_P4
     }
     if (!safe) {
       // running products of the gates from memory over logical channels 32w..32w+31:
@@ -1713,22 +1723,44 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
     const int p12 = lo_k ? 0 : 1, p3 = lo_k ? 2 : 0;  // A parts: [h | m], [l | h]
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 a12[2], a3[2];
 #pragma unroll
       for (int bq = 0; bq < 2; ++bq) {
         const int pos = 32 * s + 8 * (m >> 2) + 4 * bq + (m & 3);
-        const bf16x8 a12 = *reinterpret_cast<const bf16x8*>(&L.ktl[p12][pos][tk]);
-        const bf16x8 a3 = *reinterpret_cast<const bf16x8*>(&L.ktl[p3][pos][tk]);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x4 c = {S[h][s][4 * bq], S[h][s][4 * bq + 1], S[h][s][4 * bq + 2], S[h][s][4 * bq + 3]};
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, d3[h], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a12, d2[h], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a12, d1[h], c, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) S[h][s][4 * bq + e] = c[e];
-        }
+        a12[bq] = *reinterpret_cast<const bf16x8*>(&L.ktl[p12][pos][tk]);
+        a3[bq] = *reinterpret_cast<const bf16x8*>(&L.ktl[p3][pos][tk]);
       }
+      f32x4 c[2][2];
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          c[bq][h] = (f32x4){S[h][s][4 * bq], S[h][s][4 * bq + 1], S[h][s][4 * bq + 2],
+                             S[h][s][4 * bq + 3]};
+      // three steps over four independent accumulators
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          c[bq][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3[bq], d3[h], c[bq][h], 0, 0, 0);
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          c[bq][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a12[bq], d2[h], c[bq][h], 0, 0, 0);
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          c[bq][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a12[bq], d1[h], c[bq][h], 0, 0, 0);
+#pragma unroll
+      for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[h][s][4 * bq + e] = c[bq][h][e];
+    }
   }
   block_sync();
 
