@@ -33,6 +33,7 @@ HBM_PEAK_GBPS = 8000.0
 # non-packed fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 PROFILE = os.path.join(ROOT, "profiles", "k_step_gdn_serving_1024x32.md")
+PROFILE_CHUNK = os.path.join(ROOT, "profiles", "k_chunk_kda_256x32_t64.md")
 
 
 def log(msg):
@@ -50,14 +51,14 @@ def algorithmic_bytes(layout, n_unit: int, gate: int) -> int:
     return codes + scales + qkv + gates + out
 
 
-def profile_record():
-    """Machine-readable lines of the committed rocprofv3 summary of the step kernel, or {}
-    when they were taken on a different kernel source than the one built here."""
+def profile_record(path=PROFILE):
+    """Machine-readable lines of a committed rocprofv3 summary (default: the step kernel),
+    or {} when they were taken on a different kernel source than the one built here."""
     from quantized_delta_rule_03_amd import rocprof_summary
 
     try:
         rec = {}
-        with open(PROFILE) as f:
+        with open(path) as f:
             for line in f:
                 k, sep, v = line.partition(": ")
                 if sep and k.replace("_", "").isalnum() and " " not in k:
@@ -164,7 +165,7 @@ def bench_chunk(args, torch, qdr, wl, dev):
     g.manual_seed(args.seed)
     pool.quantize(0.1 * torch.randn((w.n_req, w.n_head, 128, 128), generator=g, device=dev))
     a1 = torch.from_numpy(wl.static_gate(w, args.seed)).to(dev)
-    n_chunk = max(1, args.steps // T)
+    n_chunk = max(16, args.steps // T)  # at least 16 calls (about 13 ms) in the timed region
     log(f"generating {T} tokens of inputs on the device")
     toks = [wl.device_step_inputs(w, t, dev, args.seed) for t in range(T)]
     x = {k: torch.stack([t[k] for t in toks]).contiguous() for k in toks[0]}
@@ -196,6 +197,8 @@ def bench_chunk(args, torch, qdr, wl, dev):
     tokens = n_chunk * T
     log(f"chunk: {chunk_s * 1e6:.1f} us per {T}-token call, {chunk_s * 1e6 / T:.2f} us per token; "
         f"{achieved:.0f} GB/s algorithmic ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    prof = profile_record(PROFILE_CHUNK)
+    traffic = float(prof["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in prof else None
     return {
         "metric": "token-updates/s (req x head), chunk mode T=64, 256-req KDA 8-bit",
         "value": n_unit * tokens / wall,
@@ -208,7 +211,7 @@ def bench_chunk(args, torch, qdr, wl, dev):
                    "dk": 128, "dv": 128, "gate": "KDA per-channel, half-life log-uniform [1, 8192]",
                    "bits": "8 (uniform)", "tokens_per_call": T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_chunk<KDA>", "bytes_per_call": nbytes,
                      "avg_call_us": chunk_s * 1e6},
         "cpu_baseline": None,

@@ -1,4 +1,5 @@
-"""Summarise rocprofv3 CSV output for the decode-step kernel as a short markdown file.
+"""Summarise rocprofv3 CSV output for one kernel (default: the decode step) as a short
+markdown file.
 
 Inputs (all written by rocprofv3 ``--output-format csv`` into one directory):
   <dir>/trace_kernel_stats.csv            --kernel-trace --stats of bench.py
@@ -72,6 +73,7 @@ def main():
     KERNELS = tuple(args.kernels.split(","))
     d = args.dir
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    label = KERNELS[0].rstrip("<")
 
     lines = [f"# {args.title}", "", "Commands (run from the repository root):", ""]
     lines += [f"    {c}" for c in args.cmd]
@@ -118,12 +120,12 @@ def main():
     lines.append("|---|---|---|")
     lines.append(f"| calibration copy ({args.copy_bytes / 2**20:.0f} MiB read + written) | "
                  f"{statistics.mean(cf):.0f} | {statistics.mean(cw):.0f} |")
-    lines.append(f"| k_step (mean of {len(fetch)} / {len(write)} dispatches) | "
+    lines.append(f"| {label} (mean of {len(fetch)} / {len(write)} dispatches) | "
                  f"{statistics.mean(fetch):.0f} | {statistics.mean(write):.0f} |")
     lines.append("")
     lines.append(f"Scale factors (known bytes / counter bytes of the copy): fetch {f_fetch:.3f}, "
                  f"write {f_write:.3f}.")
-    lines.append(f"k_step HBM traffic per launch: {fetch_b / 1e6:.1f} MB read + "
+    lines.append(f"{label} HBM traffic per launch: {fetch_b / 1e6:.1f} MB read + "
                  f"{write_b / 1e6:.1f} MB written = {(fetch_b + write_b) / 1e6:.1f} MB.")
     lines.append("")
 
@@ -133,7 +135,7 @@ def main():
         for name, vals in counters(os.path.join(d, f), is_step).items():
             means[name] = statistics.mean(vals)
     if means:
-        lines.append("## Other counters (mean per k_step dispatch)")
+        lines.append(f"## Other counters (mean per {label} dispatch)")
         lines.append("")
         for name in sorted(means):
             lines.append(f"- {name}: {means[name]:.4g}")
