@@ -54,15 +54,20 @@ def lib():
             "oref_pack": (i32, [i32, i32, P, P, P]),
             "oref_unpack": (i32, [i32, i32, P, P, P]),
             "oref_quantize": (None, [i32, i32, P, P, P, P, P]),
+            "oref_quantize_rule": (None, [i32, i32, P, P, P, P, P, i32]),
             "oref_dequantize": (None, [i32, i32, P, P, P, P]),
             "oref_step": (None, [i32, i32, i32, P, P, P, P, P, P, P, P, f32, P, P]),
+            "oref_step_rule": (None, [i32, i32, i32, P, P, P, P, P, P, P, P, f32, P, P, i32]),
             "oref_window": (None, [i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, P, P]),
             "oref_recur_fp64": (None, [i32, i32, i32, P, P, P, P, P, f32, P]),
             "oref_request_bytes": (i64, [i32, i32, i32, P]),
             "oref_quantize_pool": (i32, [i32, i32, i32, i32, P, P, P, P, P]),
+            "oref_quantize_pool_rule": (i32, [i32, i32, i32, i32, P, P, P, P, P, i32]),
             "oref_dequantize_pool": (i32, [i32, i32, i32, i32, P, P, P, P, P]),
             "oref_step_pool": (i32, [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
                                      i64, i64]),
+            "oref_step_pool_rule": (i32, [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                          P, i64, i64, i32]),
             "oref_window_pool": (i32, [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, P, P,
                                        P, P, i64, i64]),
         }
@@ -130,7 +135,10 @@ def unpack(tile: np.ndarray, bits: np.ndarray, dv: int = 128) -> np.ndarray:
     return codes
 
 
-def quantize(S: np.ndarray, bits: np.ndarray):
+RULE_STEP, RULE_KEYROW, RULE_TENSOR = 0, 1, 2  # scale rules (see qdr_oracle.h)
+
+
+def quantize(S: np.ndarray, bits: np.ndarray, rule: int = RULE_STEP):
     """fp32 state [dv, dk] -> (codes int8 [dv, dk], R [dk], c [dv])."""
     S = _c(S, np.float32)
     b = _c(bits, np.uint8)
@@ -138,7 +146,7 @@ def quantize(S: np.ndarray, bits: np.ndarray):
     codes = np.zeros((dv, dk), np.int8)
     R = np.zeros(dk, np.float32)
     c = np.zeros(dv, np.float32)
-    lib().oref_quantize(dv, dk, _p(b), _p(S), _p(codes), _p(R), _p(c))
+    lib().oref_quantize_rule(dv, dk, _p(b), _p(S), _p(codes), _p(R), _p(c), int(rule))
     return codes, R, c
 
 
@@ -152,7 +160,7 @@ def dequantize(codes: np.ndarray, R: np.ndarray, c: np.ndarray) -> np.ndarray:
     return S
 
 
-def step(codes, R, c, bits, gate, q, k, v, a, b, return_state=False):
+def step(codes, R, c, bits, gate, q, k, v, a, b, return_state=False, rule: int = RULE_STEP):
     """One decode step on one unit. Returns (codes, R, c, o[, S_new])."""
     codes = _c(codes, np.int8).copy()
     R = _c(R, np.float32).copy()
@@ -164,8 +172,8 @@ def step(codes, R, c, bits, gate, q, k, v, a, b, return_state=False):
     a = _c(np.atleast_1d(a), np.float32)
     o = np.zeros(dv, np.float32)
     S_new = np.zeros((dv, dk), np.float32) if return_state else None
-    lib().oref_step(dv, dk, gate, _p(bb), _p(codes), _p(R), _p(c), _p(q), _p(k), _p(v),
-                    _p(a), float(b), _p(o), _p(S_new))
+    lib().oref_step_rule(dv, dk, gate, _p(bb), _p(codes), _p(R), _p(c), _p(q), _p(k), _p(v),
+                         _p(a), float(b), _p(o), _p(S_new), int(rule))
     if return_state:
         return codes, R, c, o, S_new
     return codes, R, c, o
@@ -209,8 +217,9 @@ def recur_fp64(S: np.ndarray, gate, q, k, v, a, b):
 class Pool:
     """Host copy of a packed state pool: packed[n_req, req_bytes], scales, bit map."""
 
-    def __init__(self, n_req, n_head, bits, dv=128, dk=128):
+    def __init__(self, n_req, n_head, bits, dv=128, dk=128, rule=RULE_STEP):
         self.n_req, self.n_head, self.dv, self.dk = n_req, n_head, dv, dk
+        self.rule = int(rule)
         self.bits = _c(bits, np.uint8).reshape(n_head, dk)
         rb = lib().oref_request_bytes(n_head, dv, dk, _p(self.bits))
         if rb < 0:
@@ -231,9 +240,9 @@ class Pool:
     def quantize(self, S: np.ndarray):
         S = _c(S, np.float32)
         assert S.shape == (self.n_req, self.n_head, self.dv, self.dk)
-        rc = lib().oref_quantize_pool(self.n_req, self.n_head, self.dv, self.dk,
-                                      _p(self.bits), _p(S), _p(self.packed),
-                                      _p(self.row_scale), _p(self.col_scale))
+        rc = lib().oref_quantize_pool_rule(self.n_req, self.n_head, self.dv, self.dk,
+                                           _p(self.bits), _p(S), _p(self.packed),
+                                           _p(self.row_scale), _p(self.col_scale), self.rule)
         if rc:
             raise RuntimeError("oref_quantize_pool failed")
 
@@ -253,10 +262,10 @@ class Pool:
         o = np.zeros((self.n_req, self.n_head, self.dv), np.float32)
         q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
         a, b = _c(a, np.float32), _c(b, np.float32)
-        rc = lib().oref_step_pool(self.n_req, self.n_head, self.dv, self.dk, gate,
-                                  _p(self.bits), _p(self.packed), _p(self.row_scale),
-                                  _p(self.col_scale), _p(q), _p(k), _p(v), _p(a), _p(b),
-                                  _p(o), u0, u1)
+        rc = lib().oref_step_pool_rule(self.n_req, self.n_head, self.dv, self.dk, gate,
+                                       _p(self.bits), _p(self.packed), _p(self.row_scale),
+                                       _p(self.col_scale), _p(q), _p(k), _p(v), _p(a), _p(b),
+                                       _p(o), u0, u1, self.rule)
         if rc:
             raise RuntimeError("oref_step_pool failed")
         return o
@@ -273,10 +282,11 @@ class Pool:
         cuts = np.linspace(0, n_unit, max(1, min(threads, n_unit)) + 1).astype(int)
 
         def run(i):
-            return lib().oref_step_pool(self.n_req, self.n_head, self.dv, self.dk, gate,
-                                        _p(self.bits), _p(self.packed), _p(self.row_scale),
-                                        _p(self.col_scale), _p(q), _p(k), _p(v), _p(a),
-                                        _p(b), _p(o), int(cuts[i]), int(cuts[i + 1]))
+            return lib().oref_step_pool_rule(self.n_req, self.n_head, self.dv, self.dk, gate,
+                                             _p(self.bits), _p(self.packed),
+                                             _p(self.row_scale), _p(self.col_scale), _p(q),
+                                             _p(k), _p(v), _p(a), _p(b), _p(o),
+                                             int(cuts[i]), int(cuts[i + 1]), self.rule)
 
         with ThreadPoolExecutor(len(cuts) - 1) as ex:
             rcs = list(ex.map(run, range(len(cuts) - 1)))

@@ -169,24 +169,39 @@ int oref_unpack(int dv, int dk, const uint8_t *bits, const uint8_t *tile, int8_t
  *   c_i = max_j |y_ij| (1 if 0),  code_ij = RNE(y_ij * (Qmax_j * (1/c_i))),
  * with the last product exact (fp64) before the single round-half-even.
  * ---------------------------------------------------------------------------- */
-void oref_quantize(int dv, int dk, const uint8_t *bits, const float *S, int8_t *codes,
-                   float *R, float *c) {
+void oref_quantize_rule(int dv, int dk, const uint8_t *bits, const float *S, int8_t *codes,
+                        float *R, float *c, int rule) {
+    float *A = (float *)malloc(sizeof(float) * (size_t)dk);
     float *invA = (float *)malloc(sizeof(float) * (size_t)dk);
+    /* key rows (columns j): absmax over the value rows */
     for (int j = 0; j < dk; ++j) {
-        float A = 0.0f;
+        float m = 0.0f;
         for (int i = 0; i < dv; ++i) {
-            float m = fabsf(S[(size_t)i * dk + j]);
-            if (m > A) A = m;
+            float x = fabsf(S[(size_t)i * dk + j]);
+            if (x > m) m = x;
         }
-        if (A == 0.0f) A = 1.0f;
-        R[j] = A / (float)qmax_of(bits[j]);
-        invA[j] = 1.0f / A;
+        A[j] = m;
+    }
+    /* per-tensor INT8 ([DEV] "Uniform per-tensor INT8"): one range for the whole state */
+    if (rule == OREF_RULE_TENSOR) {
+        float m = 0.0f;
+        for (int j = 0; j < dk; ++j)
+            if (A[j] > m) m = A[j];
+        for (int j = 0; j < dk; ++j) A[j] = m;
+    }
+    for (int j = 0; j < dk; ++j) {
+        if (A[j] == 0.0f) A[j] = 1.0f;
+        R[j] = A[j] / (float)qmax_of(bits[j]);
+        invA[j] = 1.0f / A[j];
     }
     for (int i = 0; i < dv; ++i) {
+        /* value-column scale ([ABS] STEPQuant abstract); the INT8 baselines keep c = 1 */
         float cm = 0.0f;
-        for (int j = 0; j < dk; ++j) {
-            float y = S[(size_t)i * dk + j] * invA[j];
-            if (fabsf(y) > cm) cm = fabsf(y);
+        if (rule == OREF_RULE_STEP) {
+            for (int j = 0; j < dk; ++j) {
+                float y = S[(size_t)i * dk + j] * invA[j];
+                if (fabsf(y) > cm) cm = fabsf(y);
+            }
         }
         if (cm == 0.0f) cm = 1.0f;
         c[i] = cm;
@@ -201,7 +216,13 @@ void oref_quantize(int dv, int dk, const uint8_t *bits, const float *S, int8_t *
             codes[(size_t)i * dk + j] = (int8_t)t;
         }
     }
+    free(A);
     free(invA);
+}
+
+void oref_quantize(int dv, int dk, const uint8_t *bits, const float *S, int8_t *codes,
+                   float *R, float *c) {
+    oref_quantize_rule(dv, dk, bits, S, codes, R, c, OREF_RULE_STEP);
 }
 
 void oref_dequantize(int dv, int dk, const int8_t *codes, const float *R, const float *c,
@@ -226,9 +247,9 @@ void oref_dequantize(int dv, int dk, const int8_t *codes, const float *R, const 
  * S_new_ij = fma(w_i, k_j, S'_ij) (one rounding); o_i = fl32(sum_j S_new_ij q_j) in fp64.
  * The new state is then refit and requantized (oref_quantize).
  * ---------------------------------------------------------------------------- */
-void oref_step(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
-               float *c, const float *q, const float *k, const float *v, const float *a,
-               float b, float *o, float *S_new_out) {
+void oref_step_rule(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
+                    float *c, const float *q, const float *k, const float *v, const float *a,
+                    float b, float *o, float *S_new_out, int rule) {
     float *cf = (float *)malloc(sizeof(float) * (size_t)dk);
     float *rf = (float *)malloc(sizeof(float) * (size_t)dv);
     float *w = (float *)malloc(sizeof(float) * (size_t)dv);
@@ -259,12 +280,18 @@ void oref_step(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, flo
         o[i] = (float)acc;
     }
     if (S_new_out) memcpy(S_new_out, Sn, sizeof(float) * (size_t)dv * dk);
-    oref_quantize(dv, dk, bits, Sn, codes, R, c);
+    oref_quantize_rule(dv, dk, bits, Sn, codes, R, c, rule);
 
     free(cf);
     free(rf);
     free(w);
     free(Sn);
+}
+
+void oref_step(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
+               float *c, const float *q, const float *k, const float *v, const float *a,
+               float b, float *o, float *S_new_out) {
+    oref_step_rule(dv, dk, gate, bits, codes, R, c, q, k, v, a, b, o, S_new_out, OREF_RULE_STEP);
 }
 
 /* ------------------------------------------------------------------------------
@@ -362,8 +389,9 @@ static void scales_to_physical(int dk, const uint8_t *perm, const float *logical
     for (int p = 0; p < dk; ++p) phys[p] = logical[perm[p]];
 }
 
-int oref_quantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
-                       const float *S, uint8_t *packed, float *row_scale, float *col_scale) {
+int oref_quantize_pool_rule(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                            const float *S, uint8_t *packed, float *row_scale, float *col_scale,
+                            int rule) {
     pool_geom g;
     if (geom_init(&g, n_head, dv, dk, bits)) { geom_free(&g); return -1; }
     int8_t *codes = (int8_t *)malloc((size_t)dv * dk);
@@ -372,7 +400,7 @@ int oref_quantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bit
         for (int h = 0; h < n_head; ++h) {
             size_t u = (size_t)r * n_head + h;
             const uint8_t *bh = bits + (size_t)h * dk;
-            oref_quantize(dv, dk, bh, S + u * dv * dk, codes, R, col_scale + u * dv);
+            oref_quantize_rule(dv, dk, bh, S + u * dv * dk, codes, R, col_scale + u * dv, rule);
             scales_to_physical(dk, g.perm + (size_t)h * dk, R, row_scale + u * dk);
             oref_pack(dv, dk, bh, codes, packed + (size_t)r * g.req_bytes + g.head_off[h]);
         }
@@ -380,6 +408,12 @@ int oref_quantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bit
     free(R);
     geom_free(&g);
     return 0;
+}
+
+int oref_quantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                       const float *S, uint8_t *packed, float *row_scale, float *col_scale) {
+    return oref_quantize_pool_rule(n_req, n_head, dv, dk, bits, S, packed, row_scale, col_scale,
+                                   OREF_RULE_STEP);
 }
 
 int oref_dequantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
@@ -403,10 +437,10 @@ int oref_dequantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *b
     return 0;
 }
 
-int oref_step_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
-                   uint8_t *packed, float *row_scale, float *col_scale, const float *q,
-                   const float *k, const float *v, const float *a, const float *b, float *o,
-                   long u0, long u1) {
+int oref_step_pool_rule(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
+                        uint8_t *packed, float *row_scale, float *col_scale, const float *q,
+                        const float *k, const float *v, const float *a, const float *b, float *o,
+                        long u0, long u1, int rule) {
     pool_geom g;
     if (geom_init(&g, n_head, dv, dk, bits)) { geom_free(&g); return -1; }
     int8_t *codes = (int8_t *)malloc((size_t)dv * dk);
@@ -419,8 +453,9 @@ int oref_step_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_
         const float *au = (gate == OREF_KDA) ? a + (size_t)u * dk : a + u;
         oref_unpack(dv, dk, bh, tile, codes);
         scales_to_logical(dk, perm, row_scale + (size_t)u * dk, R);
-        oref_step(dv, dk, gate, bh, codes, R, col_scale + (size_t)u * dv, q + (size_t)u * dk,
-                  k + (size_t)u * dk, v + (size_t)u * dv, au, b[u], o + (size_t)u * dv, NULL);
+        oref_step_rule(dv, dk, gate, bh, codes, R, col_scale + (size_t)u * dv, q + (size_t)u * dk,
+                       k + (size_t)u * dk, v + (size_t)u * dv, au, b[u], o + (size_t)u * dv, NULL,
+                       rule);
         scales_to_physical(dk, perm, R, row_scale + (size_t)u * dk);
         oref_pack(dv, dk, bh, codes, tile);
     }
@@ -428,6 +463,14 @@ int oref_step_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_
     free(R);
     geom_free(&g);
     return 0;
+}
+
+int oref_step_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
+                   uint8_t *packed, float *row_scale, float *col_scale, const float *q,
+                   const float *k, const float *v, const float *a, const float *b, float *o,
+                   long u0, long u1) {
+    return oref_step_pool_rule(n_req, n_head, dv, dk, gate, bits, packed, row_scale, col_scale,
+                               q, k, v, a, b, o, u0, u1, OREF_RULE_STEP);
 }
 
 int oref_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,

@@ -77,12 +77,30 @@ void oref_quantize(int dv, int dk, const uint8_t *bits, const float *S, int8_t *
 void oref_dequantize(int dv, int dk, const int8_t *codes, const float *R, const float *c,
                      float *S);
 
+/* Scale rules. STEP: the two-stage absmax of the STEPQuant reading (key rows, then value
+ * columns). The comparison baselines of the dev.to page's "four options" section, in the
+ * same (R_j, c_i) format with c = 1: KEYROW, per-row INT8 (one range per key row, the
+ * first stage alone); TENSOR, uniform per-tensor INT8 (one range for the whole state,
+ * symmetric: the zero point is the code 0). */
+#define OREF_RULE_STEP 0
+#define OREF_RULE_KEYROW 1
+#define OREF_RULE_TENSOR 2
+
+/* Quantize with a scale rule (oref_quantize is rule STEP). */
+void oref_quantize_rule(int dv, int dk, const uint8_t *bits, const float *S, int8_t *codes,
+                        float *R, float *c, int rule);
+
 /* One decode step on one unit, in place on (codes, R, c).
  * a: GDN -> a[0]; KDA -> a[dk]. o[dv] receives S_new q.
  * S_new (optional, may be NULL) receives the fp32 state before requantization. */
 void oref_step(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
                float *c, const float *q, const float *k, const float *v, const float *a,
                float b, float *o, float *S_new);
+
+/* oref_step with the requantization of a given scale rule (oref_step is rule STEP). */
+void oref_step_rule(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
+                    float *c, const float *q, const float *k, const float *v, const float *a,
+                    float b, float *o, float *S_new, int rule);
 
 /* One window of W tokens on one unit (LeapQuant reading): the state is the dequantized
  * low-bit state at the window start; the exact recurrence runs in fp64 over the W
@@ -114,6 +132,14 @@ int oref_step_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_
                    uint8_t *packed, float *row_scale, float *col_scale, const float *q,
                    const float *k, const float *v, const float *a, const float *b, float *o,
                    long u0, long u1);
+/* The pool drivers with a scale rule (the functions above use rule STEP). */
+int oref_quantize_pool_rule(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                            const float *S, uint8_t *packed, float *row_scale, float *col_scale,
+                            int rule);
+int oref_step_pool_rule(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
+                        uint8_t *packed, float *row_scale, float *col_scale, const float *q,
+                        const float *k, const float *v, const float *a, const float *b, float *o,
+                        long u0, long u1, int rule);
 /* Window over W tokens for every unit: token inputs are [W][n_req][n_head][...]. */
 int oref_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
                      uint8_t *packed, float *row_scale, float *col_scale, int W,
