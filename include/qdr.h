@@ -72,6 +72,15 @@ extern "C" {
 #define QDR_GATE_GDN 0 /* scalar gate per (request, head) */
 #define QDR_GATE_KDA 1 /* diagonal gate, one value per key channel */
 
+/* Scale rules. STEP (default): the STEPQuant reading, key-row ranges then value-column
+ * scales. The comparison baselines of the dev.to page's section on the quantization
+ * options, in the same (R_j, c_i) format with every c_i = 1: KEYROW, per-row INT8 (one
+ * range per key row); TENSOR, uniform per-tensor INT8 (one range per state; symmetric,
+ * the zero point is code 0). */
+#define QDR_RULE_STEP 0
+#define QDR_RULE_KEYROW 1
+#define QDR_RULE_TENSOR 2
+
 typedef struct qdr_desc {
     int32_t n_req;        /* requests (>= 0; 0 makes every call a no-op)            */
     int32_t n_head;       /* heads per request (1..1024)                            */
@@ -80,6 +89,8 @@ typedef struct qdr_desc {
     const uint8_t *bits;  /* HOST [n_head][dk], each in {4,6,8}; per head, the count */
                           /* of channels of each width is a multiple of 32           */
     int32_t window;       /* W >= 1 for qdr_decode_window, 0 otherwise               */
+    int32_t rule;         /* QDR_RULE_*: scale rule of qdr_quantize_state and          */
+                          /* qdr_decode_step; window and chunk mode take QDR_RULE_STEP */
 } qdr_desc;
 
 /* S0 -- lifetime-based bit map (STEPQuant abstract; STEPQuant page Fig. 1(b), Fig. 4 /
@@ -111,6 +122,8 @@ int qdr_init_state(const qdr_desc *desc, void *packed, float *row_scale, float *
  * read as a two-stage absmax, key axis first:
  *   A_j = max_i |S_ij| (1 if 0), R_j = A_j/Qmax_j, y_ij = S_ij*(1/A_j),
  *   c_i = max_j |y_ij| (1 if 0), code_ij = RNE(y_ij * (Qmax_j*(1/c_i))).
+ * desc->rule = QDR_RULE_KEYROW keeps c_i = 1; QDR_RULE_TENSOR also replaces every A_j by
+ * max_j A_j (1 if 0) before the rest.
  * meta must come from qdr_init_state with the same descriptor. Errors: all codes. */
 int qdr_quantize_state(const qdr_desc *desc, const void *meta, const float *S,
                        void *packed, float *row_scale, float *col_scale, void *stream);

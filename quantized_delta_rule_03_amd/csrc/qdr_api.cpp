@@ -86,6 +86,8 @@ int check_desc(const qdr_desc* d, Geometry* g) {
     return fail(QDR_EINVAL, "gate = %d is neither GDN (0) nor KDA (1)", d->gate);
   if (!d->bits) return fail(QDR_EINVAL, "desc->bits is NULL");
   if (d->window < 0) return fail(QDR_EINVAL, "window = %d < 0", d->window);
+  if (d->rule < QDR_RULE_STEP || d->rule > QDR_RULE_TENSOR)
+    return fail(QDR_EINVAL, "rule = %d is not a QDR_RULE_* value", d->rule);
   if ((long long)d->n_req * d->n_head > (1LL << 31) - 1)
     return fail(QDR_EINVAL, "n_req * n_head overflows");
   if (g) {
@@ -139,6 +141,7 @@ qdr::Pool pool_of(const qdr_desc* d, const void* meta, const Geometry& g) {
   p.req_bytes = g.req_bytes;
   p.uniform = g.uniform ? 1 : 0;
   for (int c = 0; c < 3; ++c) p.n_class[c] = g.n_class[c];
+  p.rule = d->rule;
   return p;
 }
 
@@ -301,6 +304,8 @@ int qdr_decode_window(const qdr_desc* d, const void* meta, void* packed, float* 
   Geometry g;
   CHECK(check_desc(d, &g));
   if (d->window < 1) return fail(QDR_EUNSUPPORTED, "desc->window = %d: no window mode", d->window);
+  if (d->rule != QDR_RULE_STEP)
+    return fail(QDR_EUNSUPPORTED, "window mode takes only QDR_RULE_STEP (rule = %d)", d->rule);
   if (d->window > qdr::kWindowMax)
     return fail(QDR_EUNSUPPORTED, "desc->window = %d exceeds %d", d->window, qdr::kWindowMax);
   if (t < 0 || t >= d->window)
@@ -330,6 +335,8 @@ int qdr_decode_chunk(const qdr_desc* d, const void* meta, void* packed, float* r
   Geometry g;
   CHECK(check_desc(d, &g));
   if (T < 0) return fail(QDR_EINVAL, "T = %d is negative", T);
+  if (d->rule != QDR_RULE_STEP)
+    return fail(QDR_EUNSUPPORTED, "chunk mode takes only QDR_RULE_STEP (rule = %d)", d->rule);
   const bool any = d->n_req > 0 && T > 0;
   CHECK(check_ptr(meta, "meta", true));
   CHECK(check_ptr(packed, "packed", any));

@@ -64,6 +64,7 @@ struct Pool {
   uint32_t req_bytes;
   int uniform;      // every head has a single code width
   int n_class[3];   // heads of width 8, 6, 4 (uniform case)
+  int rule;         // scale rule (QDR_RULE_*)
 };
 
 // Launchers (kernels.hip). All enqueue on `stream` and return hipGetLastError().

@@ -30,6 +30,13 @@ namespace {
 
 constexpr int GDN = 0;
 constexpr int KDA = 1;
+constexpr int RULE_STEP = 0;    // key-row ranges, then value-column scales
+constexpr int RULE_KEYROW = 1;  // per-key-row INT8 baseline: c = 1
+constexpr int RULE_TENSOR = 2;  // per-tensor INT8 baseline: one range per state, c = 1
+
+// max over the 64 lanes of a wave (non-negative floats compared as unsigned ints),
+// wave-uniform result
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x);
 
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -196,6 +203,15 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
   return x;
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = row16_max_u32(x);
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return max(max(a, b), max(c, d));
+}
+
 // Key-row absmax of the lane-held state s over all 128 rows of this wave's segment;
 // the lanes write R (physical order) to global and 1/A to LDS for position p0 + (rg & 7).
 __device__ __forceinline__ void key_row_refit(const float (&s)[8][8], int rg, int p0, int B,
@@ -275,11 +291,13 @@ struct QuantLds {
   float invA[kD];
   float invc[kD];
   float cpart[16 * kD];
+  uint32_t tmax[4];
 };
 
 __global__ void __launch_bounds__(kThreads) k_quantize(const void* meta, int n_head,
                                                        uint32_t req_bytes, const float* S,
-                                                       uint8_t* packed, float* Rs, float* Cs) {
+                                                       uint8_t* packed, float* Rs, float* Cs,
+                                                       int rule) {
   __shared__ QuantLds L;
   const int u = blockIdx.x, r = u / n_head, h = u % n_head;
   const int w = wave_id(), lane = threadIdx.x & 63, rg = lane & 15, jg = lane >> 4;
@@ -297,14 +315,34 @@ __global__ void __launch_bounds__(kThreads) k_quantize(const void* meta, int n_h
 #pragma unroll
     for (int m = 0; m < 8; ++m) s[rr][m] = Su[(size_t)(rg + 16 * rr) * kD + col[m]];
   const size_t uo = (size_t)u * kD;
-  key_row_refit(s, rg, p0, sg.bits, Rs + uo, L.invA);
+  if (rule == RULE_TENSOR) {
+    // one range for the whole state
+    float mx = 0.0f;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) mx = fmaxf(mx, fabsf(s[rr][m]));
+    const uint32_t wm = wave_max_u32(__float_as_uint(mx));
+    if (lane == 0) L.tmax[w] = wm;
+    __syncthreads();
+    const float Am = __uint_as_float(max(max(L.tmax[0], L.tmax[1]), max(L.tmax[2], L.tmax[3])));
+    const float Aa = (Am == 0.0f) ? 1.0f : Am;
+    if (threadIdx.x < kD) {
+      const int p = threadIdx.x;
+      Rs[uo + p] = Aa / (float)((1 << (mh->seg_bits[p >> 5] - 1)) - 1);
+      L.invA[p] = 1.0f / Aa;
+    }
+  } else {
+    key_row_refit(s, rg, p0, sg.bits, Rs + uo, L.invA);
+  }
   __syncthreads();
   normalise_rows(s, L.invA, rg, p0, w * 4 + jg, L.cpart);
   __syncthreads();
   if (threadIdx.x < kD) {
     const int i = threadIdx.x;
     float cm = 0.0f;
-    for (int g = 0; g < 16; ++g) cm = fmaxf(cm, L.cpart[g * kD + i]);
+    if (rule == RULE_STEP)
+      for (int g = 0; g < 16; ++g) cm = fmaxf(cm, L.cpart[g * kD + i]);
     if (cm == 0.0f) cm = 1.0f;
     Cs[uo + i] = cm;
     L.invc[i] = 1.0f / cm;
@@ -413,6 +451,7 @@ struct StepWork {
   double osum[kD];  // rf_i-free readout sums from phase 2
   int8_t dig[4][kPlanes][4][8];  // [segment][plane][jg][operand byte]
   double scale_u[4], scale_o[4], kq[4];
+  uint32_t tmax[4];  // per-wave state absmax (per-tensor rule)
   union {
     double upart[16 * kDS];  // per (wave, jg) combined digit-plane sums
     float cpart[16 * kFS];   // per (wave, jg) partial value-column absmax
@@ -828,8 +867,9 @@ __device__ __forceinline__ void block_sync() {
     }                                     \
   } while (0)
 
-// One unit. `odd` alternates the two waves that form the value-column scales.
-template <int GATE, int B>
+// One unit. `odd` alternates the two waves that form the value-column scales. RULE is the
+// scale rule of the requantization (the comparison baselines keep c = 1).
+template <int GATE, int B, int RULE>
 __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecIn& vin, StepWork& W,
                                           const UnitInfo& cur, const UnitInfo& nx, int odd) {
   const int tid = threadIdx.x;
@@ -882,20 +922,55 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   float s[8][8];
   QDR_WIDTH_DISPATCH(B, Bw, (update_phase<BB>(W, rg, p0, op, s)));
   int rpos;
-  const float Rkeep = key_row_refit_rs(s, rg, p0, Bw, W.invA, rpos);
-  wait_lgkm();
-  __builtin_amdgcn_wave_barrier();
-  normalise_rows<kFS>(s, W.invA, rg, p0, w * 4 + jg, W.part.cpart);
+  float Rkeep;
+  if constexpr (RULE == RULE_TENSOR) {
+    // one range for the whole state: wave absmax, then the four waves
+    float mx = 0.0f;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) mx = fmaxf(mx, fabsf(s[rr][m]));
+    const uint32_t wm = wave_max_u32(__float_as_uint(mx));
+    if (lane == 0) W.tmax[w] = wm;
+    block_sync();
+    const float Am = __uint_as_float(max(max(W.tmax[0], W.tmax[1]), max(W.tmax[2], W.tmax[3])));
+    const float Aa = (Am == 0.0f) ? 1.0f : Am;
+    const float ia = 1.0f / Aa;
+    Rkeep = Aa / (float)((1 << (Bw - 1)) - 1);
+    rpos = rg & 7;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) s[rr][m] *= ia;
+  } else {
+    Rkeep = key_row_refit_rs(s, rg, p0, Bw, W.invA, rpos);
+    wait_lgkm();
+    __builtin_amdgcn_wave_barrier();
+    if constexpr (RULE == RULE_STEP) {
+      normalise_rows<kFS>(s, W.invA, rg, p0, w * 4 + jg, W.part.cpart);
+    } else {
+      float ia[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ia[m] = W.invA[p0 + m];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) s[rr][m] *= ia[m];
+    }
+  }
   block_sync();  // B3
 
-  // 4. value-column scales
-  float cm = 0.0f;
-  if ((tid >> 7) == odd) {
-    const int i = tid & (kD - 1);
+  // 4. value-column scales (the baselines keep c = 1)
+  float cm = 1.0f;
+  if constexpr (RULE == RULE_STEP) {
+    cm = 0.0f;
+    if ((tid >> 7) == odd) {
+      const int i = tid & (kD - 1);
 #pragma unroll
-    for (int g = 0; g < 16; ++g) cm = fmaxf(cm, W.part.cpart[g * kFS + i]);
-    if (cm == 0.0f) cm = 1.0f;
-    W.invc[i] = 1.0f / cm;
+      for (int g = 0; g < 16; ++g) cm = fmaxf(cm, W.part.cpart[g * kFS + i]);
+      if (cm == 0.0f) cm = 1.0f;
+      W.invc[i] = 1.0f / cm;
+    }
   }
   block_sync();  // B4
 
@@ -903,14 +978,14 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   const float qmax = (float)((1 << (Bw - 1)) - 1);
   float M[8];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) M[rr] = qmax * W.invc[rg + 16 * rr];
+  for (int rr = 0; rr < 8; ++rr) M[rr] = (RULE == RULE_STEP) ? qmax * W.invc[rg + 16 * rr] : qmax;
   uint8_t* gseg = A.packed + cur.toff + sg.off;
   QDR_WIDTH_DISPATCH(B, Bw, (requant_store<BB>(gseg, rg, jg, s, M)));
   if (rg < 8) A.Rs[uo + p0 + rpos] = Rkeep;
   if ((tid >> 7) == odd) A.Cs[uo + (tid & (kD - 1))] = cm;
 }
 
-template <int GATE, int B>
+template <int GATE, int B, int RULE>
 __device__ __forceinline__ void step_run(const StepArgs& A, uint8_t* tile, VecIn& vin, StepWork& W,
                                          UnitIter it, int count) {
   UnitInfo cur = unit_info(A, it);
@@ -918,12 +993,12 @@ __device__ __forceinline__ void step_run(const StepArgs& A, uint8_t* tile, VecIn
     advance(it);
     const bool nx = n + 1 < count;
     const UnitInfo u1 = nx ? unit_info(A, it) : cur;
-    step_unit<GATE, B>(A, tile, vin, W, cur, u1, n & 1);
+    step_unit<GATE, B, RULE>(A, tile, vin, W, cur, u1, n & 1);
     cur = u1;
   }
 }
 
-template <int GATE, bool UNIFORM>
+template <int GATE, bool UNIFORM, int RULE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(UNIFORM ? 3 : 2)))
 k_step(StepArgs A) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileMax];
@@ -978,11 +1053,11 @@ k_step(StepArgs A) {
   }
   const int count = k_end - k_begin;
   if constexpr (UNIFORM) {
-    if (cls == 0) step_run<GATE, 8>(A, tile, vin, W, it, count);
-    else if (cls == 1) step_run<GATE, 6>(A, tile, vin, W, it, count);
-    else step_run<GATE, 4>(A, tile, vin, W, it, count);
+    if (cls == 0) step_run<GATE, 8, RULE>(A, tile, vin, W, it, count);
+    else if (cls == 1) step_run<GATE, 6, RULE>(A, tile, vin, W, it, count);
+    else step_run<GATE, 4, RULE>(A, tile, vin, W, it, count);
   } else {
-    step_run<GATE, 0>(A, tile, vin, W, it, count);
+    step_run<GATE, 0, RULE>(A, tile, vin, W, it, count);
   }
 }
 
@@ -1824,7 +1899,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
-int g_step_grid[2][2] = {{0, 0}, {0, 0}};
+int g_step_grid[2][2][3] = {};
 
 }  // namespace
 
@@ -1839,7 +1914,7 @@ hipError_t launch_quantize(const Pool& p, const float* S, uint8_t* packed, float
                            hipStream_t s) {
   if (p.n_unit == 0) return hipSuccess;
   hipLaunchKernelGGL(k_quantize, dim3(p.n_unit), dim3(kThreads), 0, s, p.meta, p.n_head,
-                     p.req_bytes, S, packed, rs, cs);
+                     p.req_bytes, S, packed, rs, cs, p.rule);
   return hipGetLastError();
 }
 
@@ -1855,24 +1930,31 @@ hipError_t launch_dequantize(const Pool& p, const uint8_t* packed, const float* 
 // number of units. Queried once per process and kernel variant (one device per
 // process assumed for the cache; the value only sizes the grid, correctness does not
 // depend on it).
-template <int GATE, bool UNIFORM>
+template <int GATE, bool UNIFORM, int RULE>
 static int step_grid(int n_unit) {
-  int& g = g_step_grid[GATE][UNIFORM ? 1 : 0];
+  int& g = g_step_grid[GATE][UNIFORM ? 1 : 0][RULE];
   if (g == 0) {
     int dev = 0, cus = 0, per_cu = 0;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<GATE, UNIFORM>,
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<GATE, UNIFORM, RULE>,
                                                        kThreads, 0);
     g = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
   }
   return n_unit < g ? n_unit : g;
 }
 
-template <int GATE, bool UNIFORM>
-static void launch_step_variant(const StepArgs& A, hipStream_t s) {
-  hipLaunchKernelGGL((k_step<GATE, UNIFORM>), dim3(step_grid<GATE, UNIFORM>(A.n_unit)),
+template <int GATE, bool UNIFORM, int RULE>
+static void launch_step_rule(const StepArgs& A, hipStream_t s) {
+  hipLaunchKernelGGL((k_step<GATE, UNIFORM, RULE>), dim3(step_grid<GATE, UNIFORM, RULE>(A.n_unit)),
                      dim3(kThreads), 0, s, A);
+}
+
+template <int GATE, bool UNIFORM>
+static void launch_step_variant(const StepArgs& A, int rule, hipStream_t s) {
+  if (rule == RULE_KEYROW) launch_step_rule<GATE, UNIFORM, RULE_KEYROW>(A, s);
+  else if (rule == RULE_TENSOR) launch_step_rule<GATE, UNIFORM, RULE_TENSOR>(A, s);
+  else launch_step_rule<GATE, UNIFORM, RULE_STEP>(A, s);
 }
 
 hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, float* cs,
@@ -1882,11 +1964,11 @@ hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, floa
   StepArgs A{p.meta, p.n_head, p.n_unit / p.n_head, p.n_unit, p.req_bytes, p.uniform,
              {p.n_class[0], p.n_class[1], p.n_class[2]}, packed, rs, cs, q, k, v, a, b, o};
   if (gate == GDN) {
-    if (p.uniform) launch_step_variant<GDN, true>(A, s);
-    else launch_step_variant<GDN, false>(A, s);
+    if (p.uniform) launch_step_variant<GDN, true>(A, p.rule, s);
+    else launch_step_variant<GDN, false>(A, p.rule, s);
   } else {
-    if (p.uniform) launch_step_variant<KDA, true>(A, s);
-    else launch_step_variant<KDA, false>(A, s);
+    if (p.uniform) launch_step_variant<KDA, true>(A, p.rule, s);
+    else launch_step_variant<KDA, false>(A, p.rule, s);
   }
   return hipGetLastError();
 }

@@ -24,6 +24,7 @@ QDR_EALIGN = -3
 QDR_EHIP = -4
 GDN = 0
 KDA = 1
+RULE_STEP, RULE_KEYROW, RULE_TENSOR = 0, 1, 2  # scale rules (QDR_RULE_*)
 
 SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize_state",
            "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk", "qdr_dequantize_state",
@@ -39,7 +40,7 @@ class QdrError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("n_req", ctypes.c_int32), ("n_head", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("gate", ctypes.c_int32),
-                ("bits", ctypes.c_void_p), ("window", ctypes.c_int32)]
+                ("bits", ctypes.c_void_p), ("window", ctypes.c_int32), ("rule", ctypes.c_int32)]
 
 
 _lib = None
@@ -117,6 +118,7 @@ class Layout:
     gate: int
     bits: np.ndarray
     window: int = 0
+    rule: int = RULE_STEP
     packed_bytes: int = 0
     scale_bytes: int = 0
     meta_bytes: int = 0
@@ -126,7 +128,7 @@ class Layout:
     def __post_init__(self):
         self.bits = np.ascontiguousarray(self.bits, np.uint8).reshape(self.n_head, 128)
         self._desc = Desc(self.n_req, self.n_head, 128, 128, self.gate,
-                          self.bits.ctypes.data, self.window)
+                          self.bits.ctypes.data, self.window, self.rule)
         s = [ctypes.c_size_t() for _ in range(4)]
         _check(lib().qdr_state_bytes(ctypes.byref(self._desc), *[ctypes.byref(x) for x in s]),
                "qdr_state_bytes")
@@ -182,10 +184,10 @@ class StatePool:
     """Caller-owned device buffers of one layer's quantized state (torch allocations)."""
 
     def __init__(self, n_req: int, n_head: int, gate: int, bits: np.ndarray, window: int = 0,
-                 device="cuda"):
+                 device="cuda", rule: int = RULE_STEP):
         import torch
 
-        self.layout = Layout(n_req, n_head, gate, bits, window)
+        self.layout = Layout(n_req, n_head, gate, bits, window, rule)
         L = self.layout
         self.device = torch.device(device)
         self.packed = torch.empty(max(L.packed_bytes, 16), dtype=torch.uint8, device=device)

@@ -63,8 +63,9 @@ def compare_codes(packed_a, packed_b, pool: oracle.Pool):
 
 
 def gpu_to_oracle(gpu, bits) -> oracle.Pool:
+    """The GPU pool's state as an oracle pool (same scale rule)."""
     packed, R, c = gpu.to_host()
-    p = oracle.Pool(gpu.layout.n_req, gpu.layout.n_head, bits)
+    p = oracle.Pool(gpu.layout.n_req, gpu.layout.n_head, bits, rule=gpu.layout.rule)
     p.packed[:] = packed
     p.row_scale[:] = R
     p.col_scale[:] = c

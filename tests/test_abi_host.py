@@ -51,11 +51,11 @@ def test_state_bytes_matches_oracle_layout(oref, gate):
     assert L.window_bytes == 7 * 32 * (64 * 2 * 128 * 4 + 128 * 4)
 
 
-def _desc(n_req=2, n_head=4, dk=128, dv=128, gate=0, bits=None, window=0):
+def _desc(n_req=2, n_head=4, dk=128, dv=128, gate=0, bits=None, window=0, rule=0):
     if bits is None:
         bits = np.full((n_head, 128), 8, np.uint8)
     d = qdr.Desc(n_req, n_head, dk, dv, gate, bits.ctypes.data if bits is not False else None,
-                 window)
+                 window, rule)
     return d, bits
 
 
@@ -136,6 +136,21 @@ def test_chunk_validation():
     assert rc == qdr.QDR_EINVAL and "o is NULL" in qdr.last_error()
     rc = L.qdr_decode_chunk(ctypes.byref(d), P, P, P, P, 16, P, P + 4, P, P, P, P, None)
     assert rc == qdr.QDR_EALIGN and "k" in qdr.last_error()
+
+
+def test_rule_validation():
+    L = qdr.lib()
+    P = 1 << 20
+    for bad in (-1, 3):
+        d, keep = _desc(rule=bad)
+        assert _state_bytes(d) == qdr.QDR_EINVAL and "rule" in qdr.last_error()
+    d, keep = _desc(rule=qdr.RULE_TENSOR)
+    assert _state_bytes(d) == qdr.QDR_OK
+    d, keep = _desc(window=8, rule=qdr.RULE_KEYROW)
+    rc = L.qdr_decode_window(ctypes.byref(d), P, P, P, P, P, 0, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED and "QDR_RULE_STEP" in qdr.last_error()
+    rc = L.qdr_decode_chunk(ctypes.byref(d), P, P, P, P, 4, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED and "QDR_RULE_STEP" in qdr.last_error()
 
 
 def test_errors_are_thread_local():
