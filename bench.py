@@ -218,6 +218,54 @@ def bench_chunk(args, torch, qdr, wl, dev):
     }
 
 
+def bench_compare(args, torch, qdr, wl, dev):
+    """The decode step under each scale rule on the serving shape (1024 requests x 32 GDN
+    heads): STEPQuant at the lifetime map (the default line) and at 8 bits, and the
+    per-key-row and per-tensor INT8 baselines (8 bits). Same kernel skeleton; the rules
+    differ only in the refit."""
+    w = wl.WORKLOADS[3]
+    mixed = qdr.assign_bits(w.gate, wl.halflives(w, args.seed))
+    b8 = wl.uniform_bits(w.n_head, 8)
+    settings = [("step_mixed", mixed, qdr.RULE_STEP), ("step_8bit", b8, qdr.RULE_STEP),
+                ("keyrow_int8", b8, qdr.RULE_KEYROW), ("tensor_int8", b8, qdr.RULE_TENSOR)]
+    a = torch.from_numpy(wl.static_gate(w, args.seed)).to(dev)
+    n_in = 8
+    inputs = [wl.device_step_inputs(w, t, dev, args.seed) for t in range(n_in)]
+    o = torch.empty((w.n_req, w.n_head, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    steps = max(16, args.steps)
+    rules = {}
+    for name, bits, rule in settings:
+        pool = qdr.StatePool(w.n_req, w.n_head, w.gate, bits, device=dev, rule=rule)
+        for t in range(max(3, args.warmup)):
+            x = inputs[t % n_in]
+            pool.step(x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            x = inputs[i % n_in]
+            ev[i][0].record(stream)
+            pool.step(x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev])) * 1e3
+        nbytes = algorithmic_bytes(pool.layout, w.n_unit, w.gate)
+        rules[name] = {"us_per_step": us, "state_updates_per_s": w.n_unit / (us / 1e6),
+                       "gbps": nbytes / (us / 1e6) / 1e9, "bytes_per_step": nbytes}
+        log(f"{name}: {us:.1f} us per step, {rules[name]['gbps']:.0f} GB/s algorithmic")
+        del pool
+    ref = rules["step_8bit"]
+    return {
+        "metric": "decode-step time per scale rule, 1024-req GDN (STEPQuant vs INT8 baselines)",
+        "value": ref["state_updates_per_s"], "unit": "state-updates/s (STEPQuant 8-bit)",
+        "n_gpus": 1, "steps": steps, "warmup": max(3, args.warmup), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name + " (rules)", "n_req": w.n_req, "n_head": w.n_head},
+        "rules": rules,
+    }
+
+
 def cpu_baseline(w, bits, threads: int, n_req: int, steps: int):
     import oracle
     from quantized_delta_rule_03_amd import workloads as wl
@@ -247,9 +295,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=1024)
     ap.add_argument("--cpu-steps", type=int, default=24)
-    ap.add_argument("--workload", choices=["serving", "window", "chunk"], default="serving",
+    ap.add_argument("--workload", choices=["serving", "window", "chunk", "compare"],
+                    default="serving",
                     help="serving: the decode-step metric (default); window: window mode "
-                         "(one call per token); chunk: chunk mode (one call per window)")
+                         "(one call per token); chunk: chunk mode (one call per window); "
+                         "compare: the decode step under each scale rule")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step has "
@@ -269,6 +319,9 @@ def main():
         return
     if args.workload == "chunk":
         print(json.dumps(bench_chunk(args, torch, qdr, wl, dev)), flush=True)
+        return
+    if args.workload == "compare":
+        print(json.dumps(bench_compare(args, torch, qdr, wl, dev)), flush=True)
         return
     w = wl.WORKLOADS[3]
     bits = qdr.assign_bits(w.gate, wl.halflives(w, args.seed))
