@@ -48,6 +48,7 @@ def lib():
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int, ctypes.c_long, ctypes.c_float
+        u64 = ctypes.c_uint64
         sig = {
             "oref_assign_bits": (i32, [i32, i32, i32, P, P]),
             "oref_layout": (i64, [i32, i32, P, P, P]),
@@ -70,6 +71,14 @@ def lib():
                                           P, i64, i64, i32]),
             "oref_window_pool": (i32, [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, P, P,
                                        P, P, i64, i64]),
+            "oref_philox4x32_10": (None, [P, P, P]),
+            "oref_f32_to_f16": (ctypes.c_uint16, [f32]),
+            "oref_f16_to_f32": (f32, [ctypes.c_uint16]),
+            "oref_damp_perm": (i32, [i32, P, P]),
+            "oref_damp_quantize_pool": (i32, [i32, i32, i32, P, P, P, P, P, u64, u64]),
+            "oref_damp_dequantize_pool": (i32, [i32, i32, i32, P, P, P, P, P]),
+            "oref_damp_step_pool": (i32, [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                          u64, u64, i64, i64]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -308,4 +317,80 @@ class Pool:
                                     _p(b), _p(o), u0, u1)
         if rc:
             raise RuntimeError("oref_window_pool failed")
+        return o
+
+
+# ---------------------------------------------------------------------------
+# DAMP-style storage variant (see qdr_oracle.h)
+# ---------------------------------------------------------------------------
+
+DAMP_HALF = 16
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 block: 4 counter words, 2 key words -> 4 output words."""
+    c = np.asarray(ctr, np.uint32).copy()
+    k = np.asarray(key, np.uint32).copy()
+    out = np.zeros(4, np.uint32)
+    lib().oref_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def f32_to_f16_bits(x: float) -> int:
+    return int(lib().oref_f32_to_f16(float(x)))
+
+
+def f16_bits_to_f32(h: int) -> float:
+    return float(lib().oref_f16_to_f32(int(h)))
+
+
+def damp_perm(sel: np.ndarray) -> np.ndarray:
+    """sel [n_head][128] flags (16 per head) -> perm [n_head][128] (physical -> logical)."""
+    sel = _c(sel, np.uint8).reshape(-1, 128)
+    perm = np.zeros_like(sel)
+    for h in range(sel.shape[0]):
+        if lib().oref_damp_perm(128, _p(sel[h]), _p(perm[h])) != 0:
+            raise ValueError("each head needs exactly 16 selected channels")
+    return perm
+
+
+class DampPool:
+    """Host DAMP-variant pool: half [n_unit][128][16] (binary16 bits), codes
+    [n_unit][128][112], R [n_unit][112]; units r * n_head + h."""
+
+    def __init__(self, n_req, n_head, sel, seed=0):
+        self.n_req, self.n_head = n_req, n_head
+        self.n_unit = n_req * n_head
+        self.perm = damp_perm(sel)
+        self.seed = int(seed)
+        self.half = np.zeros((self.n_unit, 128, DAMP_HALF), np.uint16)
+        self.codes = np.zeros((self.n_unit, 128, 128 - DAMP_HALF), np.int8)
+        self.R = np.full((self.n_unit, 128 - DAMP_HALF), np.float32(1.0 / 127.0), np.float32)
+
+    def copy(self):
+        p = DampPool.__new__(DampPool)
+        p.__dict__.update(self.__dict__)
+        p.half, p.codes, p.R = self.half.copy(), self.codes.copy(), self.R.copy()
+        return p
+
+    def quantize(self, S: np.ndarray, step: int = 0):
+        S = _c(S, np.float32).reshape(self.n_unit, 128, 128)
+        lib().oref_damp_quantize_pool(self.n_unit, self.n_head, 128, _p(self.perm), _p(S),
+                                      _p(self.half), _p(self.codes), _p(self.R), self.seed,
+                                      int(step))
+
+    def dequantize(self) -> np.ndarray:
+        S = np.zeros((self.n_unit, 128, 128), np.float32)
+        lib().oref_damp_dequantize_pool(self.n_unit, self.n_head, 128, _p(self.perm),
+                                        _p(self.half), _p(self.codes), _p(self.R), _p(S))
+        return S.reshape(self.n_req, self.n_head, 128, 128)
+
+    def step(self, gate, q, k, v, a, b, step: int):
+        q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        o = np.zeros((self.n_req, self.n_head, 128), np.float32)
+        lib().oref_damp_step_pool(self.n_unit, self.n_head, 128, gate, _p(self.perm),
+                                  _p(self.half), _p(self.codes), _p(self.R), _p(q), _p(k),
+                                  _p(v), _p(a), _p(b), _p(o), self.seed, int(step), 0,
+                                  self.n_unit)
         return o

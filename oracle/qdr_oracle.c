@@ -516,3 +516,244 @@ int oref_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint
     geom_free(&g);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------
+ * DAMP-style storage variant ([MEAS] section "DAMP: accuracy depends on the task":
+ * selected key channels kept in FP16, the rest in INT8 with stochastic rounding).
+ * Written from the storage description and the arithmetic contract in the header.
+ * ---------------------------------------------------------------------------- */
+
+/* Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+ * 1, 2, 3" (SC11). Ten rounds of two 32x32->64 multiplies on the counter, the key
+ * bumped by the Weyl constants between rounds. */
+void oref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        const uint32_t n0 = hi1 ^ c1 ^ k0;
+        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* IEEE 754 binary16 from binary32, round to nearest even (subnormals kept, overflow to
+ * infinity, NaN to the quiet NaN 0x7E00), and back (exact). */
+uint16_t oref_f32_to_f16(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const uint32_t ex = (u >> 23) & 0xFFu;
+    uint32_t man = u & 0x7FFFFFu;
+    if (ex == 0xFF) return (uint16_t)(sign | (man ? 0x7E00u : 0x7C00u));
+    /* value = 1.man * 2^(ex-127) (or 0.man * 2^-126 when ex == 0) */
+    int e = (int)ex - 127;
+    if (ex == 0) return (uint16_t)sign; /* fp32 subnormals are far below half's range */
+    uint32_t sig = man | 0x800000u;     /* 24-bit significand */
+    if (e > 15) return (uint16_t)(sign | 0x7C00u);
+    int shift; /* bits of the 24-bit significand dropped */
+    uint32_t hexp;
+    if (e >= -14) {
+        shift = 13;
+        hexp = (uint32_t)(e + 15);
+    } else {
+        shift = 13 + (-14 - e); /* subnormal: 2^-24 units */
+        hexp = 0;
+        if (shift > 24) return (uint16_t)sign;
+    }
+    uint32_t q = sig >> shift;
+    const uint32_t rem = sig & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1;
+    uint32_t h;
+    if (hexp == 0) {
+        h = q; /* may carry into the smallest normal, which is the right encoding */
+    } else {
+        /* q holds 11 bits (implicit one); a carry to 12 bits bumps the exponent */
+        if (q & 0x800u) {
+            q >>= 1;
+            hexp += 1;
+        }
+        if (hexp >= 31) return (uint16_t)(sign | 0x7C00u);
+        h = (hexp << 10) | (q & 0x3FFu);
+    }
+    return (uint16_t)(sign | h);
+}
+
+float oref_f16_to_f32(uint16_t h) {
+    const int sign = (h >> 15) & 1;
+    const int ex = (h >> 10) & 0x1F;
+    const int man = h & 0x3FF;
+    double v;
+    if (ex == 0) v = ldexp((double)man, -24);
+    else if (ex == 31) v = man ? NAN : INFINITY;
+    else v = ldexp((double)(man | 0x400), ex - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* uniform in [0, 1) for state entry (i, p) of a unit at a step: the top 24 bits of the
+ * first Philox word for the counter (i*128 + p, unit, step low, step high), key = seed */
+static double damp_uniform(uint64_t seed, uint32_t unit, uint64_t step, int i, int p) {
+    const uint32_t ctr[4] = {(uint32_t)(i * 128 + p), unit, (uint32_t)step, (uint32_t)(step >> 32)};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oref_philox4x32_10(ctr, key, out);
+    return ldexp((double)(out[0] >> 8), -24);
+}
+
+int oref_damp_perm(int dk, const uint8_t *sel, uint8_t *perm) {
+    int n = 0;
+    for (int j = 0; j < dk; ++j) n += sel[j] ? 1 : 0;
+    if (dk != 128 || n != OREF_DAMP_HALF) return -1;
+    int a = 0, b = OREF_DAMP_HALF;
+    for (int j = 0; j < dk; ++j) {
+        if (sel[j]) perm[a++] = (uint8_t)j;
+        else perm[b++] = (uint8_t)j;
+    }
+    return 0;
+}
+
+void oref_damp_dequantize(int dv, const uint8_t *perm, const uint16_t *half, const int8_t *codes,
+                          const float *R, float *S) {
+    const int NI = 128 - OREF_DAMP_HALF;
+    for (int i = 0; i < dv; ++i)
+        for (int p = 0; p < 128; ++p) {
+            const int j = perm[p];
+            S[(size_t)i * 128 + j] =
+                p < OREF_DAMP_HALF ? oref_f16_to_f32(half[(size_t)i * OREF_DAMP_HALF + p])
+                                   : (float)codes[(size_t)i * NI + (p - OREF_DAMP_HALF)] *
+                                         R[p - OREF_DAMP_HALF];
+        }
+}
+
+/* requantize a physical-order fp32 state Sp[dv][128] into (half, codes, R) */
+static void damp_requant(int dv, const float *Sp, uint16_t *half, int8_t *codes, float *R,
+                         uint64_t seed, uint32_t unit, uint64_t step) {
+    const int NI = 128 - OREF_DAMP_HALF;
+    for (int i = 0; i < dv; ++i)
+        for (int p = 0; p < OREF_DAMP_HALF; ++p)
+            half[(size_t)i * OREF_DAMP_HALF + p] = oref_f32_to_f16(Sp[(size_t)i * 128 + p]);
+    for (int c = 0; c < NI; ++c) {
+        const int p = OREF_DAMP_HALF + c;
+        float A = 0.0f;
+        for (int i = 0; i < dv; ++i) {
+            const float m = fabsf(Sp[(size_t)i * 128 + p]);
+            if (m > A) A = m;
+        }
+        if (A == 0.0f) A = 1.0f;
+        R[c] = A / 127.0f;
+        const float invA = 1.0f / A;
+        for (int i = 0; i < dv; ++i) {
+            const float y = Sp[(size_t)i * 128 + p] * invA;
+            /* stochastic rounding: floor(y*127 + u), u uniform in [0, 1); exact in fp64 */
+            double t = floor((double)y * 127.0 + damp_uniform(seed, unit, step, i, p));
+            if (t > 127.0) t = 127.0;
+            if (t < -127.0) t = -127.0;
+            codes[(size_t)i * NI + c] = (int8_t)t;
+        }
+    }
+}
+
+void oref_damp_quantize(int dv, const uint8_t *perm, const float *S, uint16_t *half,
+                        int8_t *codes, float *R, uint64_t seed, uint32_t unit, uint64_t step) {
+    float *Sp = (float *)malloc(sizeof(float) * (size_t)dv * 128);
+    for (int i = 0; i < dv; ++i)
+        for (int p = 0; p < 128; ++p) Sp[(size_t)i * 128 + p] = S[(size_t)i * 128 + perm[p]];
+    damp_requant(dv, Sp, half, codes, R, seed, unit, step);
+    free(Sp);
+}
+
+void oref_damp_step(int dv, int gate, const uint8_t *perm, uint16_t *half, int8_t *codes,
+                    float *R, const float *q, const float *k, const float *v, const float *a,
+                    float b, float *o, uint64_t seed, uint32_t unit, uint64_t step) {
+    const int NI = 128 - OREF_DAMP_HALF;
+    float *Sp = (float *)malloc(sizeof(float) * (size_t)dv * 128);
+    float kp[128], qp[128], gp[128];
+    for (int p = 0; p < 128; ++p) {
+        kp[p] = k[perm[p]];
+        qp[p] = q[perm[p]];
+        gp[p] = (gate == OREF_KDA) ? a[perm[p]] : a[0];
+    }
+    /* gated dequantization: fp16 channels fl(h * a_j); INT8 channels fl(code * fl(a_j R_j)) */
+    for (int i = 0; i < dv; ++i)
+        for (int p = 0; p < 128; ++p)
+            Sp[(size_t)i * 128 + p] =
+                p < OREF_DAMP_HALF
+                    ? oref_f16_to_f32(half[(size_t)i * OREF_DAMP_HALF + p]) * gp[p]
+                    : (float)codes[(size_t)i * NI + (p - OREF_DAMP_HALF)] *
+                          (gp[p] * R[p - OREF_DAMP_HALF]);
+    for (int i = 0; i < dv; ++i) {
+        /* u = S' k: two fp64 partial sums over the position halves, in position order */
+        double s0 = 0.0, s1 = 0.0;
+        for (int p = 0; p < 64; ++p) s0 += (double)Sp[(size_t)i * 128 + p] * (double)kp[p];
+        for (int p = 64; p < 128; ++p) s1 += (double)Sp[(size_t)i * 128 + p] * (double)kp[p];
+        const float u = (float)(s0 + s1);
+        const float w = b * (v[i] - u);
+        for (int p = 0; p < 128; ++p)
+            Sp[(size_t)i * 128 + p] = fmaf(w, kp[p], Sp[(size_t)i * 128 + p]);
+        double t0 = 0.0, t1 = 0.0;
+        for (int p = 0; p < 64; ++p) t0 += (double)Sp[(size_t)i * 128 + p] * (double)qp[p];
+        for (int p = 64; p < 128; ++p) t1 += (double)Sp[(size_t)i * 128 + p] * (double)qp[p];
+        o[i] = (float)(t0 + t1);
+    }
+    damp_requant(dv, Sp, half, codes, R, seed, unit, step);
+    free(Sp);
+}
+
+/* pools: half [n_unit][dv][16] (uint16), codes [n_unit][dv][112] (int8), R [n_unit][112];
+ * perm [n_head][128]; unit index u = r * n_head + h */
+int oref_damp_quantize_pool(int n_unit, int n_head, int dv, const uint8_t *perm, const float *S,
+                            uint16_t *half, int8_t *codes, float *R, uint64_t seed,
+                            uint64_t step) {
+    const int NI = 128 - OREF_DAMP_HALF;
+    for (long u = 0; u < n_unit; ++u) {
+        const int h = (int)(u % n_head);
+        oref_damp_quantize(dv, perm + (size_t)h * 128, S + (size_t)u * dv * 128,
+                           half + (size_t)u * dv * OREF_DAMP_HALF, codes + (size_t)u * dv * NI,
+                           R + (size_t)u * NI, seed, (uint32_t)u, step);
+    }
+    return 0;
+}
+
+int oref_damp_dequantize_pool(int n_unit, int n_head, int dv, const uint8_t *perm,
+                              const uint16_t *half, const int8_t *codes, const float *R,
+                              float *S) {
+    const int NI = 128 - OREF_DAMP_HALF;
+    for (long u = 0; u < n_unit; ++u) {
+        const int h = (int)(u % n_head);
+        oref_damp_dequantize(dv, perm + (size_t)h * 128, half + (size_t)u * dv * OREF_DAMP_HALF,
+                             codes + (size_t)u * dv * NI, R + (size_t)u * NI,
+                             S + (size_t)u * dv * 128);
+    }
+    return 0;
+}
+
+int oref_damp_step_pool(int n_unit, int n_head, int dv, int gate, const uint8_t *perm,
+                        uint16_t *half, int8_t *codes, float *R, const float *q, const float *k,
+                        const float *v, const float *a, const float *b, float *o, uint64_t seed,
+                        uint64_t step, long u0, long u1) {
+    const int NI = 128 - OREF_DAMP_HALF;
+    for (long u = u0; u < u1; ++u) {
+        const int h = (int)(u % n_head);
+        const float *au = (gate == OREF_KDA) ? a + (size_t)u * 128 : a + u;
+        oref_damp_step(dv, gate, perm + (size_t)h * 128, half + (size_t)u * dv * OREF_DAMP_HALF,
+                       codes + (size_t)u * dv * NI, R + (size_t)u * NI, q + (size_t)u * 128,
+                       k + (size_t)u * 128, v + (size_t)u * dv, au, b[u], o + (size_t)u * dv,
+                       seed, (uint32_t)u, step);
+    }
+    return 0;
+}

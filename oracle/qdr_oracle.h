@@ -146,6 +146,45 @@ int oref_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint
                      const float *q, const float *k, const float *v, const float *a,
                      const float *b, float *o, long u0, long u1);
 
+/* ---- DAMP-style storage variant ([MEAS] section "DAMP: accuracy depends on the task")
+ * Per unit, 16 selected key channels are kept in IEEE binary16 and the other 112 in
+ * INT8 with one range per key row and stochastic rounding. Physical positions 0..15 are
+ * the selected channels, 16..127 the others, each in increasing channel order
+ * (perm[p] = logical channel). Storage per unit: half[dv][16], codes[dv][112], R[112].
+ * Contract (shared with the GPU variant):
+ *   dequantize   S = f32(h) (selected) or fl(code * R_j)
+ *   gate         S' = fl(f32(h) * a_j) or fl(code * fl(a_j * R_j))   (GDN: a_j = a)
+ *   u_i          fl32(s0 + s1), s0 / s1 = fp64 sums of S'_ip k_p over positions 0..63 /
+ *                64..127 in position order; w_i = fl(b fl(v_i - u_i));
+ *                S_new = fma(w_i, k_p, S'_ip); o_i the same sums with S_new and q
+ *   requantize   selected: binary16 round-to-nearest-even; others: A_j = max_i |S_ij|
+ *                (1 if 0), R_j = fl(A_j/127), y = fl(S * fl(1/A_j)),
+ *                code = clamp(floor(y*127 + u), +-127) in fp64, u = uniform [0, 1) from
+ *                Philox4x32-10 with counter (i*128 + p, unit, step lo, step hi), key seed. */
+#define OREF_DAMP_HALF 16
+
+void oref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+uint16_t oref_f32_to_f16(float x);
+float oref_f16_to_f32(uint16_t h);
+int oref_damp_perm(int dk, const uint8_t *sel, uint8_t *perm);
+void oref_damp_dequantize(int dv, const uint8_t *perm, const uint16_t *half, const int8_t *codes,
+                          const float *R, float *S);
+void oref_damp_quantize(int dv, const uint8_t *perm, const float *S, uint16_t *half,
+                        int8_t *codes, float *R, uint64_t seed, uint32_t unit, uint64_t step);
+void oref_damp_step(int dv, int gate, const uint8_t *perm, uint16_t *half, int8_t *codes,
+                    float *R, const float *q, const float *k, const float *v, const float *a,
+                    float b, float *o, uint64_t seed, uint32_t unit, uint64_t step);
+int oref_damp_quantize_pool(int n_unit, int n_head, int dv, const uint8_t *perm, const float *S,
+                            uint16_t *half, int8_t *codes, float *R, uint64_t seed,
+                            uint64_t step);
+int oref_damp_dequantize_pool(int n_unit, int n_head, int dv, const uint8_t *perm,
+                              const uint16_t *half, const int8_t *codes, const float *R,
+                              float *S);
+int oref_damp_step_pool(int n_unit, int n_head, int dv, int gate, const uint8_t *perm,
+                        uint16_t *half, int8_t *codes, float *R, const float *q, const float *k,
+                        const float *v, const float *a, const float *b, float *o, uint64_t seed,
+                        uint64_t step, long u0, long u1);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,180 @@
+"""CPU pins of the oracle's DAMP-style storage variant (no GPU).
+
+The variant follows the freedom251 page's description of DAMP (section "DAMP: accuracy
+depends on the task"): a few selected key channels per head in FP16, the rest in INT8 with
+stochastic rounding; the page gives 16 channels per head and 9.9 effective bits per value.
+Pins: Philox4x32-10 against the known-answer vectors published with the generator
+(Salmon et al., SC11, Random123 distribution); binary16 conversion against numpy's
+independent implementation (exhaustively in one direction); stochastic rounding's support
+and unbiasedness; the write property through the variant's step; the identity step on
+FP16 channels; the zero state; bit accounting against the page's numbers.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_philox_known_answers():
+    kat = [
+        ([0, 0, 0, 0], [0, 0], [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]),
+        ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2, [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]),
+        ([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344], [0xA4093822, 0x299F31D0],
+         [0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1]),
+    ]
+    for ctr, key, want in kat:
+        assert [int(x) for x in oracle.philox4x32_10(ctr, key)] == want
+
+
+def test_f16_to_f32_exhaustive():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_bits_to_f32(int(h)) for h in bits], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f32_to_f16_round_to_nearest_even():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000) * np.exp2(rng.uniform(-30, 18, 20000)),
+        np.float32([0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e30, -1e30, np.inf, -np.inf,
+                    2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -26, 2.0 ** -14,
+                    (1 - 2 ** -11) * 2.0 ** -14, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11,
+                    2049.0, 2051.0, -2049.0]),
+    ]).astype(np.float32)
+    # every half-way point between adjacent binary16 values of one binade
+    h = np.arange(0x3C00, 0x4000, dtype=np.uint16).view(np.float16).astype(np.float32)
+    x = np.concatenate([x, (h[:-1] + h[1:]) / 2]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_f16_bits(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, ref)
+    assert oracle.f32_to_f16_bits(float("nan")) & 0x7C00 == 0x7C00
+
+
+def sel_flags(n_head, seed=0):
+    rng = np.random.default_rng(seed)
+    sel = np.zeros((n_head, 128), np.uint8)
+    for h in range(n_head):
+        sel[h, rng.choice(128, 16, replace=False)] = 1
+    return sel
+
+
+def test_perm_rejects_wrong_counts():
+    sel = sel_flags(2)
+    sel[1, np.flatnonzero(sel[1] == 0)[0]] = 1  # 17 channels
+    with pytest.raises(ValueError):
+        oracle.damp_perm(sel)
+
+
+def test_zero_state():
+    p = oracle.DampPool(1, 2, sel_flags(2))
+    p.quantize(np.zeros((1, 2, 128, 128), np.float32))
+    assert np.all(p.half == 0) and np.all(p.codes == 0)
+    assert np.all(p.R == np.float32(1.0 / 127.0))
+
+
+def test_fp16_channels_round_like_binary16_and_int8_support():
+    rng = np.random.default_rng(1)
+    sel = sel_flags(1, 2)
+    S = (rng.standard_normal((1, 1, 128, 128)) * 3).astype(np.float32)
+    p = oracle.DampPool(1, 1, sel, seed=7)
+    p.quantize(S, step=3)
+    Sd = p.dequantize()[0, 0]
+    chan = np.flatnonzero(sel[0])
+    assert np.array_equal(Sd[:, chan], S[0, 0][:, chan].astype(np.float16).astype(np.float32))
+    # INT8 channels: code in {floor(y*127), floor(y*127) + 1}; error below one step
+    other = np.flatnonzero(sel[0] == 0)
+    A = np.abs(S[0, 0][:, other]).max(axis=0)
+    R = (A / np.float32(127)).astype(np.float32)
+    assert np.array_equal(p.R[0], R)
+    err = np.abs(Sd[:, other].astype(np.float64) - S[0, 0][:, other])
+    assert np.all(err < R.astype(np.float64) * (1 + 1e-6))
+
+
+def test_stochastic_rounding_is_unbiased():
+    """Mean code over many seeds approaches y*127 (within 5 standard errors)."""
+    S = np.zeros((1, 1, 128, 128), np.float32)
+    sel = np.zeros((1, 128), np.uint8)
+    sel[0, :16] = 1
+    rng = np.random.default_rng(3)
+    col = rng.uniform(-1, 1, 128).astype(np.float32)
+    col[0] = 1.0  # the key-row range is exactly 1: y = S
+    S[0, 0, :, 16] = col
+    n = 2048
+    acc = np.zeros(128)
+    for s in range(n):
+        p = oracle.DampPool(1, 1, sel, seed=s)
+        p.quantize(S)
+        acc += p.codes[0, :, 0]
+    mean = acc / n
+    target = col.astype(np.float64) * 127.0
+    frac = target - np.floor(target)
+    se = np.sqrt(np.maximum(frac * (1 - frac), 1e-12) / n)
+    assert np.all(np.abs(mean - target) <= 5 * se + 1e-9)
+
+
+def test_rounding_depends_on_seed_unit_and_step_only():
+    rng = np.random.default_rng(4)
+    sel = sel_flags(2, 5)
+    S = rng.standard_normal((1, 2, 128, 128)).astype(np.float32)
+    a = oracle.DampPool(1, 2, sel, seed=11)
+    b = oracle.DampPool(1, 2, sel, seed=11)
+    a.quantize(S, step=5)
+    b.quantize(S, step=5)
+    assert np.array_equal(a.codes, b.codes)
+    b.quantize(S, step=6)
+    assert not np.array_equal(a.codes, b.codes)
+    c = oracle.DampPool(1, 2, sel, seed=12)
+    c.quantize(S, step=5)
+    assert not np.array_equal(a.codes, c.codes)
+
+
+def unit(rng, n=128):
+    x = rng.standard_normal(n)
+    return (x / np.linalg.norm(x)).astype(np.float32)
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_write_property_through_the_step(gate):
+    """Unit-norm k, b = 1, a = 1: the updated fp32 state maps k to v, so the readout with
+    q = k returns v (up to fp32 rounding of the state)."""
+    rng = np.random.default_rng(6 + gate)
+    sel = sel_flags(1, 7)
+    p = oracle.DampPool(1, 1, sel)
+    p.quantize((rng.standard_normal((1, 1, 128, 128)) * 0.3).astype(np.float32))
+    k = unit(rng)[None, None]
+    v = rng.standard_normal((1, 1, 128)).astype(np.float32)
+    a = np.ones((1, 1, 128) if gate else (1, 1), np.float32)
+    o = p.step(gate, k, k, v, a, np.ones((1, 1), np.float32), step=1)
+    assert np.allclose(o, v, atol=2e-5)
+
+
+def test_identity_step_keeps_fp16_channels_and_moves_int8_by_at_most_one():
+    rng = np.random.default_rng(8)
+    sel = sel_flags(1, 9)
+    p = oracle.DampPool(1, 1, sel, seed=3)
+    p.quantize((rng.standard_normal((1, 1, 128, 128))).astype(np.float32))
+    half0, codes0 = p.half.copy(), p.codes.astype(np.int32)
+    k = unit(rng)[None, None]
+    o = p.step(1, k, k, k, np.ones((1, 1, 128), np.float32), np.zeros((1, 1), np.float32), 9)
+    assert np.array_equal(p.half, half0)
+    assert np.abs(p.codes.astype(np.int32) - codes0).max() <= 1
+
+
+def test_bit_accounting_against_the_page():
+    g = json.load(open(os.path.join(GOLD, "pages_numbers.json")))
+    bits = g["damp_bits_per_value"]["value"]
+    pct = g["damp_storage_reduction_pct"]["value"]
+    assert abs(100 * (1 - bits / 32) - pct) < 0.05  # 9.9 bits vs fp32 <-> 69.1%
+    p = oracle.DampPool(1, 1, sel_flags(1))
+    ours = 8 * (p.half.nbytes + p.codes.nbytes + p.R.nbytes) / (128 * 128)
+    assert abs(ours - (16 * 16 + 112 * 8 + 112 * 32 / 128) / 128) < 1e-12
+    assert ours < bits  # 9.22 bits: fp32 key-row scales only, no other metadata
