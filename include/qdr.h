@@ -177,6 +177,52 @@ int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *pac
                          const float *row_scale, const float *col_scale, float *S_out,
                          void *stream);
 
+/* ---- DAMP-style storage variant (freedom251 page, section "DAMP: accuracy depends on
+ * the task": selected key channels kept in FP16, the others in INT8 with stochastic
+ * rounding; 16 channels per head). A second state format on the same decode step:
+ *   half  [n_req*n_head][128 rows][16]  binary16 values of the selected key channels
+ *   codes [n_req*n_head][128 rows][112] int8 codes of the other channels
+ *   R     [n_req*n_head][112]           fp32 range per INT8 key row (R_j = A_j/127)
+ *   meta  [n_head][128]                 physical position -> key channel (written by init)
+ * Physical positions 0..15 are the selected channels, 16..127 the others, each in
+ * increasing channel order. One decode step: S'_ij = fl(f32(h) a_j) or fl(code fl(a_j R_j));
+ * u_i = fl32(s0 + s1) with s0, s1 the fp64 sums of S'_ij k_j over positions 0..63 and
+ * 64..127 in position order; w_i = fl(b fl(v_i - u_i)); S_new = fma(w_i, k_j, S'_ij); o the
+ * same sums with S_new and q; then binary16 (round to nearest even) for the selected
+ * channels and, for the others, A_j = max_i |S_ij| (1 if 0), R_j = fl(A_j/127),
+ * y = fl(S fl(1/A_j)), code = clamp(floor(y*127 + u), +-127) evaluated in fp64 with u the
+ * top 24 bits (times 2^-24) of the first word of Philox4x32-10 (Salmon et al., SC11) for
+ * counter (row*128 + position, unit, step low, step high) and key (seed low, seed high);
+ * unit = request*n_head + head. The caller passes a fresh step per call. Errors: as for
+ * the main format; QDR_EUNSUPPORTED if a head does not select exactly 16 channels. */
+typedef struct qdr_damp_desc {
+    int32_t n_req, n_head;  /* as in qdr_desc                                          */
+    int32_t gate;           /* QDR_GATE_GDN or QDR_GATE_KDA                            */
+    const uint8_t *sel;     /* HOST [n_head][128]: nonzero marks a binary16 channel     */
+} qdr_damp_desc;
+
+/* HOST: the binary16 channels as a stand-in for DAMP's calibrated ranking (which needs
+ * model data): KDA, per head the 16 key channels of longest gate half-life (ties by
+ * index); GDN (one half-life per head), channels 0..15. halflife: GDN [n_head], KDA
+ * [n_head][128]; sel_out [n_head][128]. Errors: QDR_EINVAL. */
+int qdr_damp_select(int32_t gate, int32_t n_head, const double *halflife, uint8_t *sel_out);
+int qdr_damp_bytes(const qdr_damp_desc *desc, size_t *half, size_t *codes, size_t *scales,
+                   size_t *meta);
+/* write meta and the zero state (codes 0, binary16 zeros, R = 1/127); synchronizes once */
+int qdr_damp_init(const qdr_damp_desc *desc, void *meta, void *half, void *codes, float *R,
+                  void *stream);
+/* quantize a caller fp32 state S [n_req][n_head][128][128] (logical key order) */
+int qdr_damp_quantize(const qdr_damp_desc *desc, const void *meta, const float *S, void *half,
+                      void *codes, float *R, uint64_t seed, uint64_t step, void *stream);
+/* one decode step in place; q, k, a(KDA): [n_req][n_head][128]; v, o: [n_req][n_head][128];
+ * a(GDN), b: [n_req][n_head] */
+int qdr_damp_step(const qdr_damp_desc *desc, const void *meta, void *half, void *codes,
+                  float *R, const float *q, const float *k, const float *v, const float *a,
+                  const float *b, float *o, uint64_t seed, uint64_t step, void *stream);
+/* readback S [n_req][n_head][128][128] (logical key order): f32(h) or fl(code R_j) */
+int qdr_damp_dequantize(const qdr_damp_desc *desc, const void *meta, const void *half,
+                        const void *codes, const float *R, float *S, void *stream);
+
 /* Text of the last error on the calling thread ("" if none). Never NULL. */
 const char *qdr_last_error(void);
 

@@ -354,6 +354,148 @@ int qdr_decode_chunk(const qdr_desc* d, const void* meta, void* packed, float* r
                     "qdr_decode_chunk: launch");
 }
 
+// ---- DAMP-style storage variant ----------------------------------------------
+
+static int check_damp(const qdr_damp_desc* d, std::vector<uint8_t>* perm) {
+  if (!d) return fail(QDR_EINVAL, "desc is NULL");
+  if (d->n_req < 0) return fail(QDR_EINVAL, "n_req = %d < 0", d->n_req);
+  if (d->n_head < 1 || d->n_head > 1024)
+    return fail(QDR_EINVAL, "n_head = %d outside [1, 1024]", d->n_head);
+  if (d->gate != QDR_GATE_GDN && d->gate != QDR_GATE_KDA)
+    return fail(QDR_EINVAL, "gate = %d is neither GDN (0) nor KDA (1)", d->gate);
+  if ((long long)d->n_req * d->n_head > (1LL << 31) - 1)
+    return fail(QDR_EINVAL, "n_req * n_head overflows");
+  if (!d->sel) return fail(QDR_EINVAL, "desc->sel is NULL");
+  if (perm) perm->assign((size_t)d->n_head * qdr::kD, 0);
+  for (int h = 0; h < d->n_head; ++h) {
+    const uint8_t* sh = d->sel + (size_t)h * qdr::kD;
+    int n = 0;
+    for (int j = 0; j < qdr::kD; ++j) n += sh[j] ? 1 : 0;
+    if (n != qdr::kDampHalf)
+      return fail(QDR_EUNSUPPORTED, "head %d selects %d binary16 channels, not %d", h, n,
+                  qdr::kDampHalf);
+    if (perm) {
+      uint8_t* ph = perm->data() + (size_t)h * qdr::kD;
+      int a = 0, b = qdr::kDampHalf;
+      for (int j = 0; j < qdr::kD; ++j) ph[sh[j] ? a++ : b++] = (uint8_t)j;
+    }
+  }
+  return QDR_OK;
+}
+
+static qdr::DampPool damp_pool(const qdr_damp_desc* d, const void* meta) {
+  return {static_cast<const uint8_t*>(meta), d->n_head, d->n_req * d->n_head, d->gate};
+}
+
+int qdr_damp_select(int32_t gate, int32_t n_head, const double* halflife, uint8_t* sel_out) {
+  if (gate != QDR_GATE_GDN && gate != QDR_GATE_KDA)
+    return fail(QDR_EINVAL, "gate = %d is neither GDN (0) nor KDA (1)", gate);
+  if (n_head < 1 || n_head > 1024) return fail(QDR_EINVAL, "n_head = %d outside [1, 1024]", n_head);
+  if (!halflife || !sel_out) return fail(QDR_EINVAL, "halflife or sel_out is NULL");
+  for (int h = 0; h < n_head; ++h) {
+    uint8_t* sh = sel_out + (size_t)h * qdr::kD;
+    memset(sh, 0, qdr::kD);
+    if (gate == QDR_GATE_GDN) {
+      for (int j = 0; j < qdr::kDampHalf; ++j) sh[j] = 1;  // one lifetime per head
+      continue;
+    }
+    const double* th = halflife + (size_t)h * qdr::kD;
+    std::vector<int> idx(qdr::kD);
+    for (int j = 0; j < qdr::kD; ++j) idx[j] = j;
+    // longest-lived first, ties by channel index
+    std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return th[x] > th[y]; });
+    for (int j = 0; j < qdr::kDampHalf; ++j) sh[idx[j]] = 1;
+  }
+  return ok();
+}
+
+int qdr_damp_bytes(const qdr_damp_desc* d, size_t* half, size_t* codes, size_t* scales,
+                   size_t* meta) {
+  CHECK(check_damp(d, nullptr));
+  const size_t n_unit = (size_t)d->n_req * d->n_head;
+  if (half) *half = n_unit * qdr::kD * qdr::kDampHalf * 2;
+  if (codes) *codes = n_unit * qdr::kD * (qdr::kD - qdr::kDampHalf);
+  if (scales) *scales = n_unit * (qdr::kD - qdr::kDampHalf) * sizeof(float);
+  if (meta) *meta = (size_t)d->n_head * qdr::kD;
+  return ok();
+}
+
+int qdr_damp_init(const qdr_damp_desc* d, void* meta, void* half, void* codes, float* R,
+                  void* stream) {
+  std::vector<uint8_t> perm;
+  CHECK(check_damp(d, &perm));
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(half, "half", any));
+  CHECK(check_ptr(codes, "codes", any));
+  CHECK(check_ptr(R, "R", any));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(meta, perm.data(), perm.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "qdr_damp_init: metadata copy");
+  return hip_status(qdr::launch_damp(qdr::kDampInit, damp_pool(d, meta),
+                                     static_cast<uint16_t*>(half), static_cast<int8_t*>(codes),
+                                     R, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, 0, 0, s),
+                    "qdr_damp_init: launch");
+}
+
+int qdr_damp_quantize(const qdr_damp_desc* d, const void* meta, const float* S, void* half,
+                      void* codes, float* R, uint64_t seed, uint64_t step, void* stream) {
+  CHECK(check_damp(d, nullptr));
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(S, "S", any));
+  CHECK(check_ptr(half, "half", any));
+  CHECK(check_ptr(codes, "codes", any));
+  CHECK(check_ptr(R, "R", any));
+  return hip_status(qdr::launch_damp(qdr::kDampQuantize, damp_pool(d, meta),
+                                     static_cast<uint16_t*>(half), static_cast<int8_t*>(codes),
+                                     R, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, S,
+                                     nullptr, seed, step, static_cast<hipStream_t>(stream)),
+                    "qdr_damp_quantize: launch");
+}
+
+int qdr_damp_step(const qdr_damp_desc* d, const void* meta, void* half, void* codes, float* R,
+                  const float* q, const float* k, const float* v, const float* a,
+                  const float* b, float* o, uint64_t seed, uint64_t step, void* stream) {
+  CHECK(check_damp(d, nullptr));
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(half, "half", any));
+  CHECK(check_ptr(codes, "codes", any));
+  CHECK(check_ptr(R, "R", any));
+  CHECK(check_ptr(q, "q", any));
+  CHECK(check_ptr(k, "k", any));
+  CHECK(check_ptr(v, "v", any));
+  CHECK(check_ptr(a, "a", any));
+  CHECK(check_ptr(b, "b", any));
+  CHECK(check_ptr(o, "o", any));
+  return hip_status(qdr::launch_damp(qdr::kDampStep, damp_pool(d, meta),
+                                     static_cast<uint16_t*>(half), static_cast<int8_t*>(codes),
+                                     R, q, k, v, a, b, o, nullptr, nullptr, seed, step,
+                                     static_cast<hipStream_t>(stream)),
+                    "qdr_damp_step: launch");
+}
+
+int qdr_damp_dequantize(const qdr_damp_desc* d, const void* meta, const void* half,
+                        const void* codes, const float* R, float* S, void* stream) {
+  CHECK(check_damp(d, nullptr));
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(half, "half", any));
+  CHECK(check_ptr(codes, "codes", any));
+  CHECK(check_ptr(R, "R", any));
+  CHECK(check_ptr(S, "S", any));
+  return hip_status(qdr::launch_damp(qdr::kDampDequantize, damp_pool(d, meta),
+                                     const_cast<uint16_t*>(static_cast<const uint16_t*>(half)),
+                                     const_cast<int8_t*>(static_cast<const int8_t*>(codes)),
+                                     const_cast<float*>(R), nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, nullptr, S, 0, 0,
+                                     static_cast<hipStream_t>(stream)),
+                    "qdr_damp_dequantize: launch");
+}
+
 const char* qdr_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -86,4 +86,16 @@ hipError_t launch_chunk(const Pool& p, int gate, int T, uint8_t* packed, float* 
                         const float* q, const float* k, const float* v, const float* a,
                         const float* b, float* o, hipStream_t s);
 
+// DAMP-style storage variant (qdr_damp.hip)
+constexpr int kDampHalf = 16;  // key channels per head kept in binary16
+struct DampPool {
+  const uint8_t* perm;  // device [n_head][128]: physical position -> logical channel
+  int n_head, n_unit, gate;
+};
+enum { kDampInit = 0, kDampQuantize = 1, kDampStep = 2, kDampDequantize = 3 };
+hipError_t launch_damp(int op, const DampPool& p, uint16_t* half, int8_t* codes, float* R,
+                       const float* q, const float* k, const float* v, const float* a,
+                       const float* b, float* o, const float* S, float* Sout, uint64_t seed,
+                       uint64_t step, hipStream_t s);
+
 }  // namespace qdr

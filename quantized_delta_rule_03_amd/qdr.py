@@ -28,13 +28,19 @@ RULE_STEP, RULE_KEYROW, RULE_TENSOR = 0, 1, 2  # scale rules (QDR_RULE_*)
 
 SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize_state",
            "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk", "qdr_dequantize_state",
-           "qdr_last_error")
+           "qdr_damp_select", "qdr_damp_bytes", "qdr_damp_init", "qdr_damp_quantize", "qdr_damp_step",
+           "qdr_damp_dequantize", "qdr_last_error")
 
 
 class QdrError(RuntimeError):
     def __init__(self, code: int, where: str, text: str):
         super().__init__(f"{where} failed with {code}: {text}")
         self.code = code
+
+
+class DampDesc(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("n_head", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("sel", ctypes.c_void_p)]
 
 
 class Desc(ctypes.Structure):
@@ -56,6 +62,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, i32 = ctypes.c_void_p, ctypes.c_int32
         D = ctypes.POINTER(Desc)
+        DD = ctypes.POINTER(DampDesc)
+        u64 = ctypes.c_uint64
         sz = ctypes.POINTER(ctypes.c_size_t)
         sigs = {
             "qdr_assign_bits": [i32, i32, i32, P, P],
@@ -65,6 +73,12 @@ def lib():
             "qdr_decode_step": [D, P, P, P, P, P, P, P, P, P, P, P],
             "qdr_decode_window": [D, P, P, P, P, P, i32, P, P, P, P, P, P, P],
             "qdr_decode_chunk": [D, P, P, P, P, i32, P, P, P, P, P, P, P],
+            "qdr_damp_select": [i32, i32, P, P],
+            "qdr_damp_bytes": [DD, sz, sz, sz, sz],
+            "qdr_damp_init": [DD, P, P, P, P, P],
+            "qdr_damp_quantize": [DD, P, P, P, P, P, u64, u64, P],
+            "qdr_damp_step": [DD, P, P, P, P, P, P, P, P, P, P, u64, u64, P],
+            "qdr_damp_dequantize": [DD, P, P, P, P, P, P],
             "qdr_dequantize_state": [D, P, P, P, P, P, P],
         }
         for name, args in sigs.items():
@@ -239,3 +253,71 @@ class StatePool:
         n = self.layout.packed_bytes
         return (self.packed[:n].cpu().numpy().reshape(self.layout.n_req, -1),
                 self.row_scale.cpu().numpy(), self.col_scale.cpu().numpy())
+
+
+def damp_select(gate: int, halflife: np.ndarray, n_head: int) -> np.ndarray:
+    """Binary16 channels of the DAMP-style variant (qdr_damp_select)."""
+    hl = np.ascontiguousarray(halflife, np.float64)
+    out = np.zeros((n_head, 128), np.uint8)
+    _check(lib().qdr_damp_select(int(gate), int(n_head), hl.ctypes.data, out.ctypes.data),
+           "qdr_damp_select")
+    return out
+
+
+class DampState:
+    """Device buffers of the DAMP-style storage variant (torch allocations): half
+    [n_unit][128][16] (binary16 bits as int16), codes [n_unit][128][112] int8, R
+    [n_unit][112], meta [n_head][128]."""
+
+    def __init__(self, n_req: int, n_head: int, gate: int, sel: np.ndarray, seed: int = 0,
+                 device="cuda"):
+        import torch
+
+        self.n_req, self.n_head, self.gate, self.seed = n_req, n_head, gate, int(seed)
+        self.sel = np.ascontiguousarray(sel, np.uint8).reshape(n_head, 128)
+        self._desc = DampDesc(n_req, n_head, gate, self.sel.ctypes.data)
+        s = [ctypes.c_size_t() for _ in range(4)]
+        _check(lib().qdr_damp_bytes(ctypes.byref(self._desc), *[ctypes.byref(x) for x in s]),
+               "qdr_damp_bytes")
+        n_unit = n_req * n_head
+        self.device = torch.device(device)
+        self.half = torch.empty((n_unit, 128, 16), dtype=torch.int16, device=device)
+        self.codes = torch.empty((n_unit, 128, 112), dtype=torch.int8, device=device)
+        self.R = torch.empty((n_unit, 112), dtype=torch.float32, device=device)
+        self.meta = torch.empty(max(int(s[3].value), 16), dtype=torch.uint8, device=device)
+        _check(lib().qdr_damp_init(ctypes.byref(self._desc), _ptr(self.meta), _ptr(self.half),
+                                   _ptr(self.codes), _ptr(self.R), _stream(None)),
+               "qdr_damp_init")
+
+    def quantize(self, S, step: int = 0, stream=None):
+        _check(lib().qdr_damp_quantize(ctypes.byref(self._desc), _ptr(self.meta), _ptr(S),
+                                       _ptr(self.half), _ptr(self.codes), _ptr(self.R),
+                                       self.seed, int(step), _stream(stream)),
+               "qdr_damp_quantize")
+
+    def step(self, q, k, v, a, b, o, step: int, stream=None):
+        _check(lib().qdr_damp_step(ctypes.byref(self._desc), _ptr(self.meta), _ptr(self.half),
+                                   _ptr(self.codes), _ptr(self.R), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(a), _ptr(b), _ptr(o), self.seed, int(step),
+                                   _stream(stream)), "qdr_damp_step")
+
+    def dequantize(self, stream=None):
+        import torch
+
+        S = torch.empty((self.n_req, self.n_head, 128, 128), dtype=torch.float32,
+                        device=self.device)
+        _check(lib().qdr_damp_dequantize(ctypes.byref(self._desc), _ptr(self.meta),
+                                         _ptr(self.half), _ptr(self.codes), _ptr(self.R),
+                                         _ptr(S), _stream(stream)), "qdr_damp_dequantize")
+        return S
+
+    def load_host(self, half: np.ndarray, codes: np.ndarray, R: np.ndarray):
+        import torch
+
+        self.half.copy_(torch.from_numpy(np.ascontiguousarray(half).view(np.int16)))
+        self.codes.copy_(torch.from_numpy(np.ascontiguousarray(codes)))
+        self.R.copy_(torch.from_numpy(np.ascontiguousarray(R)))
+
+    def to_host(self):
+        return (self.half.cpu().numpy().view(np.uint16), self.codes.cpu().numpy(),
+                self.R.cpu().numpy())

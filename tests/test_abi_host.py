@@ -153,6 +153,41 @@ def test_rule_validation():
     assert rc == qdr.QDR_EUNSUPPORTED and "QDR_RULE_STEP" in qdr.last_error()
 
 
+def test_damp_validation_and_sizes():
+    L = qdr.lib()
+    P = 1 << 20
+    sel = np.zeros((4, 128), np.uint8)
+    sel[:, :16] = 1
+    d = qdr.DampDesc(2, 4, 1, sel.ctypes.data)
+    s = [ctypes.c_size_t() for _ in range(4)]
+    assert L.qdr_damp_bytes(ctypes.byref(d), *[ctypes.byref(x) for x in s]) == qdr.QDR_OK
+    assert [x.value for x in s] == [8 * 128 * 16 * 2, 8 * 128 * 112, 8 * 112 * 4, 4 * 128]
+    sel[2, 40] = 1
+    assert L.qdr_damp_bytes(ctypes.byref(d), None, None, None, None) == qdr.QDR_EUNSUPPORTED
+    assert "17" in qdr.last_error()
+    d = qdr.DampDesc(2, 4, 1, None)
+    assert L.qdr_damp_bytes(ctypes.byref(d), None, None, None, None) == qdr.QDR_EINVAL
+    sel[2, 40] = 0
+    d = qdr.DampDesc(2, 4, 1, sel.ctypes.data)
+    rc = L.qdr_damp_step(ctypes.byref(d), P, P, P, P, P, P, P, P, None, P, 0, 0, None)
+    assert rc == qdr.QDR_EINVAL and "b is NULL" in qdr.last_error()
+    rc = L.qdr_damp_quantize(ctypes.byref(d), P, P + 4, P, P, P, 0, 0, None)
+    assert rc == qdr.QDR_EALIGN
+
+
+def test_damp_select_takes_the_longest_lived_channels():
+    rng = np.random.default_rng(0)
+    tau = np.exp(rng.uniform(0, 9, (3, 128)))
+    tau[1, 5:40] = tau[1, 5]  # ties: lowest indices first
+    sel = qdr.damp_select(1, tau, 3)
+    for h in range(3):
+        want = np.zeros(128, np.uint8)
+        want[np.argsort(-tau[h], kind="stable")[:16]] = 1
+        assert np.array_equal(sel[h], want)
+    g = qdr.damp_select(0, np.ones(3), 3)
+    assert np.all(g[:, :16] == 1) and np.all(g[:, 16:] == 0)
+
+
 def test_errors_are_thread_local():
     import threading
 
