@@ -191,8 +191,8 @@ int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *pac
  * same sums with S_new and q; then binary16 (round to nearest even) for the selected
  * channels and, for the others, A_j = max_i |S_ij| (1 if 0), R_j = fl(A_j/127),
  * y = fl(S fl(1/A_j)), code = clamp(floor(y*127 + u), +-127) evaluated in fp64 with u the
- * top 24 bits (times 2^-24) of the first word of Philox4x32-10 (Salmon et al., SC11) for
- * counter (row*128 + position, unit, step low, step high) and key (seed low, seed high);
+ * top 24 bits (times 2^-24) of word position%4 of Philox4x32-10 (Salmon et al., SC11) for
+ * counter (row*32 + position/4, unit, step low, step high) and key (seed low, seed high);
  * unit = request*n_head + head. The caller passes a fresh step per call. Errors: as for
  * the main format; QDR_EUNSUPPORTED if a head does not select exactly 16 channels. */
 typedef struct qdr_damp_desc {

@@ -605,14 +605,16 @@ float oref_f16_to_f32(uint16_t h) {
     return (float)(sign ? -v : v);
 }
 
-/* uniform in [0, 1) for state entry (i, p) of a unit at a step: the top 24 bits of the
- * first Philox word for the counter (i*128 + p, unit, step low, step high), key = seed */
+/* uniform in [0, 1) for state entry (i, p) of a unit at a step: the top 24 bits of word
+ * p mod 4 of the Philox block for the counter (i*32 + p/4, unit, step low, step high),
+ * key = seed (one block serves four consecutive positions of a row) */
 static double damp_uniform(uint64_t seed, uint32_t unit, uint64_t step, int i, int p) {
-    const uint32_t ctr[4] = {(uint32_t)(i * 128 + p), unit, (uint32_t)step, (uint32_t)(step >> 32)};
+    const uint32_t ctr[4] = {(uint32_t)(i * 32 + p / 4), unit, (uint32_t)step,
+                             (uint32_t)(step >> 32)};
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     uint32_t out[4];
     oref_philox4x32_10(ctr, key, out);
-    return ldexp((double)(out[0] >> 8), -24);
+    return ldexp((double)(out[p % 4] >> 8), -24);
 }
 
 int oref_damp_perm(int dk, const uint8_t *sel, uint8_t *perm) {

@@ -15,8 +15,8 @@
 //   requantize         p < 16: binary16, round to nearest even; p >= 16: A_p = max_i
 //                      |S_ip| (1 if 0), R_p = fl(A_p/127), y = fl(S * fl(1/A_p)),
 //                      code = clamp(floor(y*127 + u), +-127) in fp64, u in [0, 1) = top 24
-//                      bits of the first Philox4x32-10 word for the counter
-//                      (i*128 + p, unit, step lo, step hi) and key (seed lo, seed hi).
+//                      bits of word p%4 of the Philox4x32-10 block for the counter
+//                      (i*32 + p/4, unit, step lo, step hi) and key (seed lo, seed hi).
 //
 // Work decomposition: one work-group of 256 threads per unit; the fp32 state tile sits in
 // LDS (rows padded against bank conflicts); thread t owns value row t >> 1 and the
@@ -41,8 +41,8 @@ struct DampLds {
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC11): ten rounds of two 32x32 -> 64-bit
 // products on the counter, the key advanced by the Weyl constants between rounds.
-__device__ __forceinline__ uint32_t philox_first(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                                 uint32_t k0, uint32_t k1) {
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r > 0) {
@@ -58,7 +58,7 @@ __device__ __forceinline__ uint32_t philox_first(uint32_t c0, uint32_t c1, uint3
     c2 = n2;
     c3 = lo0;
   }
-  return c0;
+  return make_uint4(c0, c1, c2, c3);
 }
 
 struct DampArgs {
@@ -89,13 +89,20 @@ __device__ __forceinline__ float f16_value(uint16_t h) {
 // key-row ranges over the tile and the requantized stores (the rows' owners)
 __device__ void damp_requant(DampLds& L, const DampArgs& A, int u) {
   const int tid = threadIdx.x;
-  if (tid < kI) {
-    const int p = kH + tid;
+  {
+    // column absmax: threads (position, row half), then the two halves
+    const int p = tid & (kD - 1), r0 = (tid >> 7) * 64;
     float m = 0.0f;
-    for (int i = 0; i < kD; ++i) m = fmaxf(m, fabsf(L.S[i][p]));
-    const float Aa = (m == 0.0f) ? 1.0f : m;
-    A.R[(size_t)u * kI + tid] = Aa / 127.0f;
-    L.invA[p] = 1.0f / Aa;
+    if (p >= kH)
+      for (int i = r0; i < r0 + 64; ++i) m = fmaxf(m, fabsf(L.S[i][p]));
+    if (tid >= kD) L.cf[p] = m;  // cf is dead by now: it holds the second halves
+    __syncthreads();
+    if (tid < kD && p >= kH) {
+      m = fmaxf(m, L.cf[p]);
+      const float Aa = (m == 0.0f) ? 1.0f : m;
+      A.R[(size_t)u * kI + (p - kH)] = Aa / 127.0f;
+      L.invA[p] = 1.0f / Aa;
+    }
   }
   __syncthreads();
   const int i = tid >> 1, seg = tid & 1;
@@ -117,13 +124,15 @@ __device__ void damp_requant(DampLds& L, const DampArgs& A, int u) {
     uint32_t pk[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
+      const int pq = pb + 4 * q4;
+      const uint4 r = philox4x32_10((uint32_t)(i * 32 + pq / 4), (uint32_t)u, s0, s1, k0, k1);
+      const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
       uint32_t word = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int p = pb + 4 * q4 + e;
+        const int p = pq + e;
         const float y = L.S[i][p] * L.invA[p];
-        const uint32_t r = philox_first((uint32_t)(i * kD + p), (uint32_t)u, s0, s1, k0, k1);
-        double t = floor((double)y * 127.0 + ldexp((double)(r >> 8), -24));
+        double t = floor((double)y * 127.0 + ldexp((double)(rw[e] >> 8), -24));
         t = fmin(fmax(t, -127.0), 127.0);
         word |= ((uint32_t)(uint8_t)(int8_t)(int)t) << (8 * e);
       }
@@ -156,9 +165,20 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
     for (int p = 0; p < kH; ++p) L.S[i][p] = f16_value(hr[p]) * L.cf[p];
   }
   {
-    const int8_t* cr = A.codes + (uo + i) * kI;
-    const int c0 = seg ? 64 - kH : 0, c1 = seg ? kI : 64 - kH;
-    for (int c = c0; c < c1; ++c) L.S[i][kH + c] = (float)cr[c] * L.cf[kH + c];
+    // this half's codes: 48 (seg 0) or 64 (seg 1) bytes, 16-byte aligned
+    const uint4* cr = reinterpret_cast<const uint4*>(A.codes + (uo + i) * kI + (seg ? 64 - kH : 0));
+    const int n16 = seg ? 4 : 3;
+    const int pb = seg ? 64 : kH;
+    for (int v16 = 0; v16 < n16; ++v16) {
+      const uint4 x = cr[v16];
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int p = pb + 16 * v16 + e;
+        const float c = (float)(int8_t)(xw[e >> 2] >> (8 * (e & 3)));
+        L.S[i][p] = c * L.cf[p];
+      }
+    }
   }
   // u_i: this thread's fp64 half sum in position order, the pair combined as s0 + s1
   double s = 0.0;
