@@ -266,6 +266,65 @@ def bench_compare(args, torch, qdr, wl, dev):
     }
 
 
+PROFILE_DAMP = os.path.join(ROOT, "profiles", "k_damp_step_gdn_serving_1024x32.md")
+
+
+def damp_algorithmic_bytes(n_unit: int, gate: int) -> int:
+    """Bytes one DAMP-variant step must move per launch: binary16 channels, codes and
+    key-row ranges read and written, q/k/v, a and b read, o written."""
+    state = 128 * 16 * 2 + 128 * 112 + 112 * 4
+    return n_unit * (2 * state + 3 * 512 + 4 * (128 if gate == 1 else 1) + 4 + 512)
+
+
+def bench_damp(args, torch, qdr, wl, dev):
+    """The DAMP-style storage variant (16 binary16 + 112 INT8 key channels per head,
+    stochastic rounding) on the serving shape, one step per launch."""
+    w = wl.WORKLOADS[3]
+    sel = qdr.damp_select(w.gate, wl.halflives(w, args.seed), w.n_head)
+    st = qdr.DampState(w.n_req, w.n_head, w.gate, sel, seed=args.seed, device=dev)
+    a = torch.from_numpy(wl.static_gate(w, args.seed)).to(dev)
+    n_in = 8
+    inputs = [wl.device_step_inputs(w, t, dev, args.seed) for t in range(n_in)]
+    o = torch.empty((w.n_req, w.n_head, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for t in range(args.warmup):
+        x = inputs[t % n_in]
+        st.step(x["q"], x["k"], x["v"], a, x["b"], o, step=t, stream=stream)
+    torch.cuda.synchronize()
+    steps = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        x = inputs[i % n_in]
+        ev[i][0].record(stream)
+        st.step(x["q"], x["k"], x["v"], a, x["b"], o, step=args.warmup + i, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_s = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev])) / 1e3
+    nbytes = damp_algorithmic_bytes(w.n_unit, w.gate)
+    achieved = nbytes / kern_s / 1e9
+    log(f"damp step: {kern_s * 1e6:.1f} us per launch; {achieved:.0f} GB/s algorithmic "
+        f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    prof = profile_record(PROFILE_DAMP)
+    traffic = float(prof["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in prof else None
+    return {
+        "metric": "state-updates/s (req x head), DAMP-style variant, 1024-req GDN",
+        "value": w.n_unit / (wall / steps), "unit": "state-updates/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name + " (damp)", "n_req": w.n_req, "n_head": w.n_head,
+                   "bits": "16 binary16 + 112 INT8 (stochastic rounding) key channels per head"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "k_damp_step<GDN>", "bytes_per_launch": nbytes,
+                     "avg_launch_us": kern_s * 1e6},
+        "cpu_baseline": None,
+    }
+
+
 def cpu_baseline(w, bits, threads: int, n_req: int, steps: int):
     import oracle
     from quantized_delta_rule_03_amd import workloads as wl
@@ -295,11 +354,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=1024)
     ap.add_argument("--cpu-steps", type=int, default=24)
-    ap.add_argument("--workload", choices=["serving", "window", "chunk", "compare"],
+    ap.add_argument("--workload", choices=["serving", "window", "chunk", "compare", "damp"],
                     default="serving",
                     help="serving: the decode-step metric (default); window: window mode "
                          "(one call per token); chunk: chunk mode (one call per window); "
-                         "compare: the decode step under each scale rule")
+                         "compare: the decode step under each scale rule; damp: the "
+                         "DAMP-style storage variant")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step has "
@@ -322,6 +382,9 @@ def main():
         return
     if args.workload == "compare":
         print(json.dumps(bench_compare(args, torch, qdr, wl, dev)), flush=True)
+        return
+    if args.workload == "damp":
+        print(json.dumps(bench_damp(args, torch, qdr, wl, dev)), flush=True)
         return
     w = wl.WORKLOADS[3]
     bits = qdr.assign_bits(w.gate, wl.halflives(w, args.seed))

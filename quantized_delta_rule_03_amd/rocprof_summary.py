@@ -51,6 +51,7 @@ def is_copy(name):
 def kernel_source_sha256(root):
     h = hashlib.sha256()
     for rel in ("quantized_delta_rule_03_amd/csrc/qdr_kernels.hip",
+                "quantized_delta_rule_03_amd/csrc/qdr_damp.hip",
                 "quantized_delta_rule_03_amd/csrc/qdr_internal.h"):
         with open(os.path.join(root, rel), "rb") as f:
             h.update(f.read())
