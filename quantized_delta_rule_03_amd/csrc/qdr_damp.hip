@@ -18,10 +18,11 @@
 //                      bits of word p%4 of the Philox4x32-10 block for the counter
 //                      (i*32 + p/4, unit, step lo, step hi) and key (seed lo, seed hi).
 //
-// Work decomposition: one work-group of 256 threads per unit; the fp32 state tile sits in
-// LDS (rows padded against bank conflicts); thread t owns value row t >> 1 and the
-// position half t & 1 for the dot products, the update and the requantization, and key
-// row 16 + t (t < 112) for the range.
+// Work decomposition: one work-group of 256 threads per unit. Thread t holds value row
+// t >> 1 at the 64 positions of half t & 1 in registers (the fp64 half sums of the
+// prediction and the readout are then in-thread and in position order); the key-row
+// absmax is a shuffle reduce-scatter over the wave's 32 rows, then a max over the four
+// waves through LDS. LDS holds only the input vectors and the ranges (3.5 KB).
 #include "qdr_internal.h"
 
 namespace qdr {
@@ -34,9 +35,9 @@ constexpr int kI = kD - kDampHalf;  // INT8 channels
 constexpr int kP = kD + 4;        // LDS row pitch (floats)
 
 struct DampLds {
-  float S[kD][kP];
-  float kp[kD], qp[kD], gp[kD], cf[kD];
+  float kp[kD], qp[kD], cf[kD];
   float invA[kD];
+  float part[4][kD];  // per-wave key-row absmax
 };
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC11): ten rounds of two 32x32 -> 64-bit
@@ -86,59 +87,93 @@ __device__ __forceinline__ float f16_value(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// key-row ranges over the tile and the requantized stores (the rows' owners)
-__device__ void damp_requant(DampLds& L, const DampArgs& A, int u) {
-  const int tid = threadIdx.x;
+// Max over the 32 rows of the wave that share this lane's half, for each of the lane's 64
+// positions, as a reduce-scatter over lane bits 5..1: lane l ends with the positions
+// off + 0 and off + 1 of its half, off = 32 b5 + 16 b4 + 8 b3 + 4 b2 + 2 b1.
+__device__ __forceinline__ void half_colmax(const float (&a)[64], int lane, float& m0, float& m1,
+                                            int& off) {
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  float x[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    x[j] = fmaxf(b5 ? a[j + 32] : a[j], __shfl_xor(b5 ? a[j] : a[j + 32], 32));
+  float y[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    y[j] = fmaxf(b4 ? x[j + 16] : x[j], __shfl_xor(b4 ? x[j] : x[j + 16], 16));
+  float z[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = fmaxf(b3 ? y[j + 8] : y[j], __shfl_xor(b3 ? y[j] : y[j + 8], 8));
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = fmaxf(b2 ? z[j + 4] : z[j], __shfl_xor(b2 ? z[j] : z[j + 4], 4));
+  m0 = fmaxf(b1 ? v[2] : v[0], __shfl_xor(b1 ? v[0] : v[2], 2));
+  m1 = fmaxf(b1 ? v[3] : v[1], __shfl_xor(b1 ? v[1] : v[3], 2));
+  off = 32 * (int)b5 + 16 * (int)b4 + 8 * (int)b3 + 4 * (int)b2 + 2 * (int)b1;
+}
+
+// Row i's half-row pointers: raw code words q = 0..3 hold the codes of positions
+// p0 + 16q .. p0 + 16q + 15 (for half 0, word 0 would be the binary16 positions: unused).
+__device__ __forceinline__ int8_t* code_word(int8_t* crow, int seg, int q) {
+  return crow + (seg ? 48 + 16 * q : 16 * (q - 1));
+}
+
+// ranges and requantization of the register-held half rows, stored in place
+__device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int u,
+                                             float (&Sr)[64]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
   {
-    // column absmax: threads (position, row half), then the two halves
-    const int p = tid & (kD - 1), r0 = (tid >> 7) * 64;
-    float m = 0.0f;
-    if (p >= kH)
-      for (int i = r0; i < r0 + 64; ++i) m = fmaxf(m, fabsf(L.S[i][p]));
-    if (tid >= kD) L.cf[p] = m;  // cf is dead by now: it holds the second halves
-    __syncthreads();
-    if (tid < kD && p >= kH) {
-      m = fmaxf(m, L.cf[p]);
-      const float Aa = (m == 0.0f) ? 1.0f : m;
-      A.R[(size_t)u * kI + (p - kH)] = Aa / 127.0f;
-      L.invA[p] = 1.0f / Aa;
-    }
+    float ab[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) ab[e] = fabsf(Sr[e]);
+    float m0, m1;
+    int off;
+    half_colmax(ab, lane, m0, m1, off);
+    L.part[w][p0 + off] = m0;
+    L.part[w][p0 + off + 1] = m1;
   }
   __syncthreads();
-  const int i = tid >> 1, seg = tid & 1;
+  if (tid < kD && tid >= kH) {
+    const int p = tid;
+    const float m = fmaxf(fmaxf(L.part[0][p], L.part[1][p]), fmaxf(L.part[2][p], L.part[3][p]));
+    const float Aa = (m == 0.0f) ? 1.0f : m;
+    A.R[(size_t)u * kI + (p - kH)] = Aa / 127.0f;
+    L.invA[p] = 1.0f / Aa;
+  }
+  __syncthreads();
   const uint32_t k0 = (uint32_t)A.seed, k1 = (uint32_t)(A.seed >> 32);
   const uint32_t s0 = (uint32_t)A.step, s1 = (uint32_t)(A.step >> 32);
   if (seg == 0) {
-    uint16_t hb[kH];
+    uint32_t hw[8];
 #pragma unroll
-    for (int p = 0; p < kH; ++p) hb[p] = f16_bits(L.S[i][p]);
+    for (int e = 0; e < 8; ++e)
+      hw[e] = (uint32_t)f16_bits(Sr[2 * e]) | ((uint32_t)f16_bits(Sr[2 * e + 1]) << 16);
     uint4* dst = reinterpret_cast<uint4*>(A.half + ((size_t)u * kD + i) * kH);
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(hb);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
   }
-  // INT8 positions of this half: 16..63 (seg 0) or 64..127 (seg 1)
-  const int p0 = seg ? 64 : kH, p1 = seg ? kD : 64;
   int8_t* crow = A.codes + ((size_t)u * kD + i) * kI;
-  for (int pb = p0; pb < p1; pb += 16) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q == 0 && seg == 0) continue;
     uint32_t pk[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int pq = pb + 4 * q4;
+      const int e0 = 16 * q + 4 * q4, pq = p0 + e0;
       const uint4 r = philox4x32_10((uint32_t)(i * 32 + pq / 4), (uint32_t)u, s0, s1, k0, k1);
       const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
       uint32_t word = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int p = pq + e;
-        const float y = L.S[i][p] * L.invA[p];
+        const float y = Sr[e0 + e] * L.invA[pq + e];
         double t = floor((double)y * 127.0 + ldexp((double)(rw[e] >> 8), -24));
         t = fmin(fmax(t, -127.0), 127.0);
         word |= ((uint32_t)(uint8_t)(int8_t)(int)t) << (8 * e);
       }
       pk[q4] = word;
     }
-    *reinterpret_cast<uint4*>(crow + (pb - kH)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(code_word(crow, seg, q)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   }
 }
 
@@ -152,63 +187,69 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
     L.kp[p] = A.k[uo + j];
     L.qp[p] = A.q[uo + j];
     const float g = (GATE == KDA) ? A.a[uo + j] : A.a[u];
-    L.gp[p] = g;
     L.cf[p] = p < kH ? g : g * A.R[(size_t)u * kI + (p - kH)];
   }
-  __syncthreads();
-  const int i = tid >> 1, seg = tid & 1;
-  const int p0 = seg * 64;
-  // gated dequantization of this thread's 64 positions
+  const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
+  // this thread's half row: binary16 words (half 0) and code words
+  uint4 raw[4], hraw[2];
+  const int8_t* crow = A.codes + (uo + i) * kI;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    raw[q] = (q == 0 && seg == 0) ? make_uint4(0, 0, 0, 0)
+                                  : *reinterpret_cast<const uint4*>(code_word(const_cast<int8_t*>(crow), seg, q));
   if (seg == 0) {
-    const uint16_t* hr = A.half + (uo + i) * kH;
-#pragma unroll
-    for (int p = 0; p < kH; ++p) L.S[i][p] = f16_value(hr[p]) * L.cf[p];
+    const uint4* hr = reinterpret_cast<const uint4*>(A.half + (uo + i) * kH);
+    hraw[0] = hr[0];
+    hraw[1] = hr[1];
+  } else {
+    hraw[0] = hraw[1] = make_uint4(0, 0, 0, 0);
   }
-  {
-    // this half's codes: 48 (seg 0) or 64 (seg 1) bytes, 16-byte aligned
-    const uint4* cr = reinterpret_cast<const uint4*>(A.codes + (uo + i) * kI + (seg ? 64 - kH : 0));
-    const int n16 = seg ? 4 : 3;
-    const int pb = seg ? 64 : kH;
-    for (int v16 = 0; v16 < n16; ++v16) {
-      const uint4 x = cr[v16];
-      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+  __syncthreads();
+  // gated dequantization into registers
+  float Sr[64];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int p = pb + 16 * v16 + e;
-        const float c = (float)(int8_t)(xw[e >> 2] >> (8 * (e & 3)));
-        L.S[i][p] = c * L.cf[p];
-      }
+  for (int e = 0; e < 64; ++e) {
+    const uint4 x = raw[e >> 4];
+    const uint32_t word = ((e >> 2) & 3) == 0 ? x.x : (((e >> 2) & 3) == 1 ? x.y : (((e >> 2) & 3) == 2 ? x.z : x.w));
+    const float c = (float)(int8_t)(word >> (8 * (e & 3)));
+    if (e < kH) {
+      const uint4 hx = hraw[e >> 3];
+      const int hq = (e >> 1) & 3;
+      const uint32_t hw = hq == 0 ? hx.x : (hq == 1 ? hx.y : (hq == 2 ? hx.z : hx.w));
+      const float hv = f16_value((uint16_t)(hw >> (16 * (e & 1))));
+      Sr[e] = (seg == 0 ? hv : c) * L.cf[p0 + e];
+    } else {
+      Sr[e] = c * L.cf[p0 + e];
     }
   }
   // u_i: this thread's fp64 half sum in position order, the pair combined as s0 + s1
   double s = 0.0;
-  for (int p = p0; p < p0 + 64; ++p) s += (double)L.S[i][p] * (double)L.kp[p];
+#pragma unroll
+  for (int e = 0; e < 64; ++e) s += (double)Sr[e] * (double)L.kp[p0 + e];
   const double so = __shfl_xor(s, 1);
   const float uu = (float)(seg ? so + s : s + so);
   const float w = A.b[u] * (A.v[uo + i] - uu);
   double t = 0.0;
-  for (int p = p0; p < p0 + 64; ++p) {
-    const float sn = fmaf(w, L.kp[p], L.S[i][p]);
-    L.S[i][p] = sn;
-    t += (double)sn * (double)L.qp[p];
+#pragma unroll
+  for (int e = 0; e < 64; ++e) {
+    Sr[e] = fmaf(w, L.kp[p0 + e], Sr[e]);
+    t += (double)Sr[e] * (double)L.qp[p0 + e];
   }
   const double to = __shfl_xor(t, 1);
   if (seg == 0) A.o[uo + i] = (float)(t + to);
-  __syncthreads();
-  damp_requant(L, A, u);
+  damp_requant(L, A, u, Sr);
 }
 
 __global__ void __launch_bounds__(kThreads) k_damp_quantize(DampArgs A) {
   __shared__ __attribute__((aligned(16))) DampLds L;
   const int tid = threadIdx.x, u = blockIdx.x, h = u % A.n_head;
-  const float* Su = A.S + (size_t)u * kD * kD;
+  const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
+  const float* Si = A.S + ((size_t)u * kD + i) * kD;
   const uint8_t* perm = A.perm + (size_t)h * kD;
-  for (int e = tid; e < kD * kD; e += kThreads) {
-    const int i = e >> 7, p = e & (kD - 1);
-    L.S[i][p] = Su[(size_t)i * kD + perm[p]];
-  }
-  __syncthreads();
-  damp_requant(L, A, u);
+  float Sr[64];
+#pragma unroll
+  for (int e = 0; e < 64; ++e) Sr[e] = Si[perm[p0 + e]];
+  damp_requant(L, A, u, Sr);
 }
 
 // readback S [unit][128][128] (logical order): f32(h) or fl(code * R)
