@@ -32,10 +32,10 @@ constexpr int GDN = 0;
 constexpr int KDA = 1;
 constexpr int kH = kDampHalf;     // binary16 channels
 constexpr int kI = kD - kDampHalf;  // INT8 channels
-constexpr int kP = kD + 4;        // LDS row pitch (floats)
 
 struct DampLds {
-  float kp[kD], qp[kD], cf[kD];
+  double kd[kD], qd[kD];  // k, q in fp64 for the dot products
+  float kp[kD], cf[kD];
   float invA[kD];
   float part[4][kD];  // per-wave key-row absmax
 };
@@ -50,8 +50,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     const uint32_t n0 = hi1 ^ c1 ^ k0;
     const uint32_t n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
@@ -118,6 +119,17 @@ __device__ __forceinline__ int8_t* code_word(int8_t* crow, int seg, int q) {
   return crow + (seg ? 48 + 16 * q : 16 * (q - 1));
 }
 
+// floor(127 y + r 2^-24) clamped to [-127, 127]. Scaled by 2^24 it is
+// floor(127 2^24 y + r) >> 24 (floor of a floor quotient), and 127 2^24 y + r is one fp64
+// fma with the same single rounding as the unscaled fp64 sum (exact for |y| >= 2^-23; no
+// integer is crossed below that); y is clamped to [-1, 1] first, which leaves the clamped
+// result unchanged and keeps the floor inside int32.
+__device__ __forceinline__ int sr_code(float y, uint32_t r24) {
+  const float yc = fminf(fmaxf(y, -1.0f), 1.0f);
+  const double t = floor(fma((double)yc, 2130706432.0, (double)r24));  // 127 * 2^24
+  return (int)t >> 24;
+}
+
 // ranges and requantization of the register-held half rows, stored in place
 __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int u,
                                              float (&Sr)[64]) {
@@ -153,27 +165,40 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
     dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
   }
-  int8_t* crow = A.codes + ((size_t)u * kD + i) * kI;
+  // the row's 112 INT8 positions split 56/56 over the pair: half 0 takes 16..71 (64..71
+  // from its partner's registers), half 1 takes 72..127; 14 Philox blocks each
+  float x[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (q == 0 && seg == 0) continue;
-    uint32_t pk[4];
+  for (int e = 0; e < 8; ++e) x[e] = __shfl_xor(Sr[e], 1);
+  const int base = seg ? 72 : kH;
+  uint32_t wd[14];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int e0 = 16 * q + 4 * q4, pq = p0 + e0;
-      const uint4 r = philox4x32_10((uint32_t)(i * 32 + pq / 4), (uint32_t)u, s0, s1, k0, k1);
-      const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-      uint32_t word = 0;
+  for (int b = 0; b < 14; ++b) {
+    const uint4 r = philox4x32_10((uint32_t)(i * 32 + base / 4 + b), (uint32_t)u, s0, s1, k0, k1);
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+    uint32_t word = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float y = Sr[e0 + e] * L.invA[pq + e];
-        double t = floor((double)y * 127.0 + ldexp((double)(rw[e] >> 8), -24));
-        t = fmin(fmax(t, -127.0), 127.0);
-        word |= ((uint32_t)(uint8_t)(int8_t)(int)t) << (8 * e);
-      }
-      pk[q4] = word;
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * b + e;  // position base + j
+      const float sv = seg ? Sr[8 + j] : (j < 48 ? Sr[16 + j] : x[j - 48]);
+      const float y = sv * L.invA[base + j];
+      word |= ((uint32_t)(uint8_t)(int8_t)sr_code(y, rw[e] >> 8)) << (8 * e);
     }
-    *reinterpret_cast<uint4*>(code_word(crow, seg, q)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    wd[b] = word;
+  }
+  int8_t* crow = A.codes + ((size_t)u * kD + i) * kI;
+  if (seg == 0) {
+    uint4* d = reinterpret_cast<uint4*>(crow);
+    d[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    d[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+    d[2] = make_uint4(wd[8], wd[9], wd[10], wd[11]);
+    *reinterpret_cast<uint2*>(crow + 48) = make_uint2(wd[12], wd[13]);
+  } else {
+    *reinterpret_cast<uint2*>(crow + 56) = make_uint2(wd[0], wd[1]);
+    uint4* d = reinterpret_cast<uint4*>(crow + 64);
+    d[0] = make_uint4(wd[2], wd[3], wd[4], wd[5]);
+    d[1] = make_uint4(wd[6], wd[7], wd[8], wd[9]);
+    d[2] = make_uint4(wd[10], wd[11], wd[12], wd[13]);
   }
 }
 
@@ -184,8 +209,10 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
   const size_t uo = (size_t)u * kD;
   if (tid < kD) {
     const int p = tid, j = A.perm[(size_t)h * kD + p];
-    L.kp[p] = A.k[uo + j];
-    L.qp[p] = A.q[uo + j];
+    const float kv = A.k[uo + j];
+    L.kp[p] = kv;
+    L.kd[p] = kv;
+    L.qd[p] = A.q[uo + j];
     const float g = (GATE == KDA) ? A.a[uo + j] : A.a[u];
     L.cf[p] = p < kH ? g : g * A.R[(size_t)u * kI + (p - kH)];
   }
@@ -222,10 +249,11 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
       Sr[e] = c * L.cf[p0 + e];
     }
   }
-  // u_i: this thread's fp64 half sum in position order, the pair combined as s0 + s1
+  // u_i: this thread's fp64 half sum in position order (a product of two fp32 values is exact
+  // in fp64, so each fma adds exactly the product), the pair combined as s0 + s1
   double s = 0.0;
 #pragma unroll
-  for (int e = 0; e < 64; ++e) s += (double)Sr[e] * (double)L.kp[p0 + e];
+  for (int e = 0; e < 64; ++e) s = fma((double)Sr[e], L.kd[p0 + e], s);
   const double so = __shfl_xor(s, 1);
   const float uu = (float)(seg ? so + s : s + so);
   const float w = A.b[u] * (A.v[uo + i] - uu);
@@ -233,7 +261,7 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
 #pragma unroll
   for (int e = 0; e < 64; ++e) {
     Sr[e] = fmaf(w, L.kp[p0 + e], Sr[e]);
-    t += (double)Sr[e] * (double)L.qp[p0 + e];
+    t = fma((double)Sr[e], L.qd[p0 + e], t);
   }
   const double to = __shfl_xor(t, 1);
   if (seg == 0) A.o[uo + i] = (float)(t + to);
