@@ -71,6 +71,15 @@ def lib():
                                           P, i64, i64, i32]),
             "oref_window_pool": (i32, [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, P, P,
                                        P, P, i64, i64]),
+            "oref_comp_select": (None, [i32, i32, i32, P, P, P]),
+            "oref_comp_quantize": (None, [i32, i32, P, P, i32, P, P, P, P, P]),
+            "oref_comp_dequantize": (None, [i32, i32, P, P, P, i32, P, P, P]),
+            "oref_comp_window": (None, [i32, i32, i32, P, P, P, P, i32, P, P, i32, P, P, P, P,
+                                        P, P, P]),
+            "oref_comp_quantize_pool": (i32, [i32, i32, i32, i32, P, P, i32, P, P, P, P, P]),
+            "oref_comp_dequantize_pool": (i32, [i32, i32, i32, i32, P, P, P, P, i32, P, P, P]),
+            "oref_comp_window_pool": (i32, [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, i32,
+                                            P, P, P, P, P, P, i64, i64]),
             "oref_philox4x32_10": (None, [P, P, P]),
             "oref_f32_to_f16": (ctypes.c_uint16, [f32]),
             "oref_f16_to_f32": (f32, [ctypes.c_uint16]),
@@ -220,6 +229,71 @@ def recur_fp64(S: np.ndarray, gate, q, k, v, a, b):
 
 
 # ---------------------------------------------------------------------------
+# compensator tokens (see qdr_oracle.h): m fp32 entries per unit, largest |S| first
+# ---------------------------------------------------------------------------
+
+TOK_EMPTY = 0xFFFF
+
+
+def comp_select(S: np.ndarray, m: int):
+    """Tokens of one unit's fp32 state: (tok_idx uint16 [m], tok_val [m], residual)."""
+    R = _c(S, np.float32).copy()
+    dv, dk = R.shape
+    idx = np.zeros(m, np.uint16)
+    val = np.zeros(m, np.float32)
+    lib().oref_comp_select(dv, dk, int(m), _p(R), _p(idx), _p(val))
+    return idx, val, R
+
+
+def comp_quantize(S: np.ndarray, bits: np.ndarray, m: int):
+    """(codes, R, c, tok_idx, tok_val) of one unit: tokens, then the residual quantized."""
+    S = _c(S, np.float32)
+    b = _c(bits, np.uint8)
+    dv, dk = S.shape
+    codes = np.zeros((dv, dk), np.int8)
+    R = np.zeros(dk, np.float32)
+    c = np.zeros(dv, np.float32)
+    idx = np.zeros(m, np.uint16)
+    val = np.zeros(m, np.float32)
+    lib().oref_comp_quantize(dv, dk, _p(b), _p(S), int(m), _p(codes), _p(R), _p(c), _p(idx),
+                             _p(val))
+    return codes, R, c, idx, val
+
+
+def comp_dequantize(codes, R, c, tok_idx, tok_val) -> np.ndarray:
+    codes = _c(codes, np.int8)
+    R, c = _c(R, np.float32), _c(c, np.float32)
+    idx, val = _c(tok_idx, np.uint16), _c(tok_val, np.float32)
+    dv, dk = codes.shape
+    S = np.zeros((dv, dk), np.float32)
+    lib().oref_comp_dequantize(dv, dk, _p(codes), _p(R), _p(c), idx.shape[0], _p(idx), _p(val),
+                               _p(S))
+    return S
+
+
+def comp_window(codes, R, c, tok_idx, tok_val, bits, gate, q, k, v, a, b, return_state=False):
+    """One window with compensator tokens on one unit.
+    Returns (codes, R, c, tok_idx, tok_val, o[W, dv][, S_end])."""
+    codes = _c(codes, np.int8).copy()
+    R = _c(R, np.float32).copy()
+    c = _c(c, np.float32).copy()
+    idx = _c(tok_idx, np.uint16).copy()
+    val = _c(tok_val, np.float32).copy()
+    bb = _c(bits, np.uint8)
+    dv, dk = codes.shape
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    a, b = _c(a, np.float32), _c(b, np.float32)
+    W = b.shape[0]
+    o = np.zeros((W, dv), np.float32)
+    S_end = np.zeros((dv, dk), np.float32) if return_state else None
+    lib().oref_comp_window(dv, dk, gate, _p(bb), _p(codes), _p(R), _p(c), idx.shape[0],
+                           _p(idx), _p(val), W, _p(q), _p(k), _p(v), _p(a), _p(b), _p(o),
+                           _p(S_end))
+    out = (codes, R, c, idx, val, o)
+    return out + (S_end,) if return_state else out
+
+
+# ---------------------------------------------------------------------------
 # pool interface (the packed layout the product library uses)
 # ---------------------------------------------------------------------------
 
@@ -244,7 +318,53 @@ class Pool:
         p.packed = self.packed.copy()
         p.row_scale = self.row_scale.copy()
         p.col_scale = self.col_scale.copy()
+        if hasattr(self, "tok_idx"):
+            p.tok_idx = self.tok_idx.copy()
+            p.tok_val = self.tok_val.copy()
         return p
+
+    # compensator tokens: tok_idx / tok_val [n_req, n_head, m]
+    def comp_init(self, m: int):
+        self.tok_idx = np.full((self.n_req, self.n_head, m), TOK_EMPTY, np.uint16)
+        self.tok_val = np.zeros((self.n_req, self.n_head, m), np.float32)
+
+    def comp_quantize(self, S: np.ndarray, m: int):
+        S = _c(S, np.float32)
+        assert S.shape == (self.n_req, self.n_head, self.dv, self.dk)
+        self.comp_init(m)
+        rc = lib().oref_comp_quantize_pool(self.n_req, self.n_head, self.dv, self.dk,
+                                           _p(self.bits), _p(S), int(m), _p(self.packed),
+                                           _p(self.row_scale), _p(self.col_scale),
+                                           _p(self.tok_idx), _p(self.tok_val))
+        if rc:
+            raise RuntimeError("oref_comp_quantize_pool failed")
+
+    def comp_dequantize(self) -> np.ndarray:
+        S = np.zeros((self.n_req, self.n_head, self.dv, self.dk), np.float32)
+        rc = lib().oref_comp_dequantize_pool(self.n_req, self.n_head, self.dv, self.dk,
+                                             _p(self.bits), _p(self.packed), _p(self.row_scale),
+                                             _p(self.col_scale), self.tok_idx.shape[-1],
+                                             _p(self.tok_idx), _p(self.tok_val), _p(S))
+        if rc:
+            raise RuntimeError("oref_comp_dequantize_pool failed")
+        return S
+
+    def comp_window(self, gate, q, k, v, a, b, u0=0, u1=None):
+        """window() with the pool's compensator tokens; returns o [W, n_req, n_head, dv]."""
+        n_unit = self.n_req * self.n_head
+        u1 = n_unit if u1 is None else u1
+        q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        W = b.shape[0]
+        o = np.zeros((W, self.n_req, self.n_head, self.dv), np.float32)
+        rc = lib().oref_comp_window_pool(self.n_req, self.n_head, self.dv, self.dk, gate,
+                                         _p(self.bits), _p(self.packed), _p(self.row_scale),
+                                         _p(self.col_scale), self.tok_idx.shape[-1],
+                                         _p(self.tok_idx), _p(self.tok_val), W, _p(q), _p(k),
+                                         _p(v), _p(a), _p(b), _p(o), u0, u1)
+        if rc:
+            raise RuntimeError("oref_comp_window_pool failed")
+        return o
 
     def quantize(self, S: np.ndarray):
         S = _c(S, np.float32)

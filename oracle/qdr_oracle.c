@@ -518,6 +518,173 @@ int oref_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint
 }
 
 /* ------------------------------------------------------------------------------
+ * Compensator tokens. [ABS] LeapQuant abstract: the state's largest outliers are kept
+ * as a few high-precision tokens that share the update path of the real tokens, and
+ * the remaining residual is quantized. Reading (the abstract gives no selection rule):
+ * a token is one state entry x at (i, j) kept in fp32, i.e. the rank-one term
+ * x e_i e_j^T. At a quantization the m nonzero entries of largest magnitude become the
+ * tokens, listed in that order (equal magnitudes: smaller flat index i*dk + j first);
+ * slots beyond the number of nonzero entries are empty. The residual, S with those
+ * entries set to 0, is quantized. The next window starts from the dequantized residual
+ * plus the tokens, so the tokens go through the same gated delta updates as the rest
+ * of the state (the recurrence is linear in the state).
+ * ---------------------------------------------------------------------------- */
+typedef struct {
+    float mag;
+    uint32_t idx;
+} tok_cand;
+
+static int tok_order(const void *pa, const void *pb) {
+    const tok_cand *a = (const tok_cand *)pa, *b = (const tok_cand *)pb;
+    if (a->mag != b->mag) return a->mag > b->mag ? -1 : 1;
+    return (a->idx > b->idx) - (a->idx < b->idx);
+}
+
+void oref_comp_select(int dv, int dk, int m, float *S, uint16_t *tok_idx, float *tok_val) {
+    const size_t n = (size_t)dv * dk;
+    size_t nz = 0;
+    tok_cand *c = (tok_cand *)malloc(sizeof(tok_cand) * (n ? n : 1));
+    for (size_t e = 0; e < n; ++e)
+        if (S[e] != 0.0f) {
+            c[nz].mag = fabsf(S[e]);
+            c[nz].idx = (uint32_t)e;
+            ++nz;
+        }
+    qsort(c, nz, sizeof(tok_cand), tok_order);
+    for (int t = 0; t < m; ++t) {
+        if ((size_t)t < nz) {
+            tok_idx[t] = (uint16_t)c[t].idx;
+            tok_val[t] = S[c[t].idx];
+        } else {
+            tok_idx[t] = OREF_TOK_EMPTY;
+            tok_val[t] = 0.0f;
+        }
+    }
+    for (int t = 0; t < m && (size_t)t < nz; ++t) S[c[t].idx] = 0.0f;
+    free(c);
+}
+
+void oref_comp_add(int m, const uint16_t *tok_idx, const float *tok_val, float *S) {
+    for (int t = 0; t < m; ++t)
+        if (tok_idx[t] != OREF_TOK_EMPTY) S[tok_idx[t]] += tok_val[t];
+}
+
+void oref_comp_quantize(int dv, int dk, const uint8_t *bits, const float *S, int m,
+                        int8_t *codes, float *R, float *c, uint16_t *tok_idx, float *tok_val) {
+    float *Sr = (float *)malloc(sizeof(float) * (size_t)dv * dk);
+    memcpy(Sr, S, sizeof(float) * (size_t)dv * dk);
+    oref_comp_select(dv, dk, m, Sr, tok_idx, tok_val);
+    oref_quantize(dv, dk, bits, Sr, codes, R, c);
+    free(Sr);
+}
+
+void oref_comp_dequantize(int dv, int dk, const int8_t *codes, const float *R, const float *c,
+                          int m, const uint16_t *tok_idx, const float *tok_val, float *S) {
+    oref_dequantize(dv, dk, codes, R, c, S);
+    oref_comp_add(m, tok_idx, tok_val, S);
+}
+
+void oref_comp_window(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
+                      float *c, int m, uint16_t *tok_idx, float *tok_val, int W, const float *q,
+                      const float *k, const float *v, const float *a, const float *b, float *o,
+                      float *S_end) {
+    float *Sh = (float *)malloc(sizeof(float) * (size_t)dv * dk);
+    double *S = (double *)malloc(sizeof(double) * (size_t)dv * dk);
+    oref_comp_dequantize(dv, dk, codes, R, c, m, tok_idx, tok_val, Sh);
+    for (size_t e = 0; e < (size_t)dv * dk; ++e) S[e] = (double)Sh[e];
+    for (int t = 0; t < W; ++t) {
+        const float *at = (gate == OREF_KDA) ? a + (size_t)t * dk : a + t;
+        oref_recur_fp64(dv, dk, gate, S, q + (size_t)t * dk, k + (size_t)t * dk,
+                        v + (size_t)t * dv, at, b[t], o + (size_t)t * dv);
+    }
+    for (size_t e = 0; e < (size_t)dv * dk; ++e) Sh[e] = (float)S[e];
+    if (S_end) memcpy(S_end, Sh, sizeof(float) * (size_t)dv * dk);
+    oref_comp_select(dv, dk, m, Sh, tok_idx, tok_val);
+    oref_quantize(dv, dk, bits, Sh, codes, R, c);
+    free(Sh);
+    free(S);
+}
+
+int oref_comp_quantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                            const float *S, int m, uint8_t *packed, float *row_scale,
+                            float *col_scale, uint16_t *tok_idx, float *tok_val) {
+    pool_geom g;
+    if (geom_init(&g, n_head, dv, dk, bits)) { geom_free(&g); return -1; }
+    int8_t *codes = (int8_t *)malloc((size_t)dv * dk);
+    float *R = (float *)malloc(sizeof(float) * (size_t)dk);
+    for (int r = 0; r < n_req; ++r)
+        for (int h = 0; h < n_head; ++h) {
+            size_t u = (size_t)r * n_head + h;
+            const uint8_t *bh = bits + (size_t)h * dk;
+            oref_comp_quantize(dv, dk, bh, S + u * dv * dk, m, codes, R, col_scale + u * dv,
+                               tok_idx + u * m, tok_val + u * m);
+            scales_to_physical(dk, g.perm + (size_t)h * dk, R, row_scale + u * dk);
+            oref_pack(dv, dk, bh, codes, packed + (size_t)r * g.req_bytes + g.head_off[h]);
+        }
+    free(codes);
+    free(R);
+    geom_free(&g);
+    return 0;
+}
+
+int oref_comp_dequantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                              const uint8_t *packed, const float *row_scale,
+                              const float *col_scale, int m, const uint16_t *tok_idx,
+                              const float *tok_val, float *S) {
+    if (oref_dequantize_pool(n_req, n_head, dv, dk, bits, packed, row_scale, col_scale, S))
+        return -1;
+    for (size_t u = 0; u < (size_t)n_req * n_head; ++u)
+        oref_comp_add(m, tok_idx + u * m, tok_val + u * m, S + u * dv * dk);
+    return 0;
+}
+
+int oref_comp_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
+                          uint8_t *packed, float *row_scale, float *col_scale, int m,
+                          uint16_t *tok_idx, float *tok_val, int W, const float *q,
+                          const float *k, const float *v, const float *a, const float *b,
+                          float *o, long u0, long u1) {
+    pool_geom g;
+    if (geom_init(&g, n_head, dv, dk, bits)) { geom_free(&g); return -1; }
+    size_t n_unit = (size_t)n_req * n_head;
+    size_t a_len = (gate == OREF_KDA) ? (size_t)dk : 1;
+    int8_t *codes = (int8_t *)malloc((size_t)dv * dk);
+    float *R = (float *)malloc(sizeof(float) * (size_t)dk);
+    float *tq = (float *)malloc(sizeof(float) * (size_t)W * dk);
+    float *tk = (float *)malloc(sizeof(float) * (size_t)W * dk);
+    float *tv = (float *)malloc(sizeof(float) * (size_t)W * dv);
+    float *ta = (float *)malloc(sizeof(float) * (size_t)W * a_len);
+    float *tb = (float *)malloc(sizeof(float) * (size_t)(W ? W : 1));
+    float *to = (float *)malloc(sizeof(float) * (size_t)W * dv);
+    for (long u = u0; u < u1; ++u) {
+        int r = (int)(u / n_head), h = (int)(u % n_head);
+        const uint8_t *bh = bits + (size_t)h * dk;
+        const uint8_t *perm = g.perm + (size_t)h * dk;
+        uint8_t *tile = packed + (size_t)r * g.req_bytes + g.head_off[h];
+        for (int t = 0; t < W; ++t) {
+            size_t base = (size_t)t * n_unit + (size_t)u;
+            memcpy(tq + (size_t)t * dk, q + base * dk, sizeof(float) * (size_t)dk);
+            memcpy(tk + (size_t)t * dk, k + base * dk, sizeof(float) * (size_t)dk);
+            memcpy(tv + (size_t)t * dv, v + base * dv, sizeof(float) * (size_t)dv);
+            memcpy(ta + (size_t)t * a_len, a + base * a_len, sizeof(float) * a_len);
+            tb[t] = b[base];
+        }
+        oref_unpack(dv, dk, bh, tile, codes);
+        scales_to_logical(dk, perm, row_scale + (size_t)u * dk, R);
+        oref_comp_window(dv, dk, gate, bh, codes, R, col_scale + (size_t)u * dv, m,
+                         tok_idx + (size_t)u * m, tok_val + (size_t)u * m, W, tq, tk, tv, ta,
+                         tb, to, NULL);
+        scales_to_physical(dk, perm, R, row_scale + (size_t)u * dk);
+        oref_pack(dv, dk, bh, codes, tile);
+        for (int t = 0; t < W; ++t)
+            memcpy(o + ((size_t)t * n_unit + (size_t)u) * dv, to + (size_t)t * dv,
+                   sizeof(float) * (size_t)dv);
+    }
+    free(codes); free(R); free(tq); free(tk); free(tv); free(ta); free(tb); free(to);
+    geom_free(&g);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------
  * DAMP-style storage variant ([MEAS] section "DAMP: accuracy depends on the task":
  * selected key channels kept in FP16, the rest in INT8 with stochastic rounding).
  * Written from the storage description and the arithmetic contract in the header.

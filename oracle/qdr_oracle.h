@@ -146,6 +146,44 @@ int oref_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint
                      const float *q, const float *k, const float *v, const float *a,
                      const float *b, float *o, long u0, long u1);
 
+/* ---- compensator tokens ([ABS] LeapQuant abstract: the largest outliers kept as a few
+ * high-precision tokens sharing the real tokens' update path; the residual quantized).
+ * Reading: a token is one entry x at (i, j) in fp32 (the rank-one term x e_i e_j^T);
+ * the m tokens are the m nonzero entries of largest |S| (equal magnitudes: smaller
+ * flat index i*dk + j first), in that order; unused slots hold OREF_TOK_EMPTY and 0.
+ * tok_idx / tok_val: [m] per unit (pools: [n_req][n_head][m]); flat index in logical
+ * key order. dv*dk must be below 65535. */
+#define OREF_TOK_EMPTY 0xFFFFu
+/* selects the tokens of S and sets their entries to 0 in place (S becomes the residual) */
+void oref_comp_select(int dv, int dk, int m, float *S, uint16_t *tok_idx, float *tok_val);
+/* S += tokens */
+void oref_comp_add(int m, const uint16_t *tok_idx, const float *tok_val, float *S);
+/* tokens of S, then the residual quantized by rule STEP */
+void oref_comp_quantize(int dv, int dk, const uint8_t *bits, const float *S, int m,
+                        int8_t *codes, float *R, float *c, uint16_t *tok_idx, float *tok_val);
+/* dequantized residual plus the tokens */
+void oref_comp_dequantize(int dv, int dk, const int8_t *codes, const float *R, const float *c,
+                          int m, const uint16_t *tok_idx, const float *tok_val, float *S);
+/* oref_window started from the dequantized residual plus the tokens; at the end the new
+ * tokens are selected from the fp32 state and the residual is quantized (in place on
+ * codes, R, c, tok_idx, tok_val). S_end (optional): the state before the selection. */
+void oref_comp_window(int dv, int dk, int gate, const uint8_t *bits, int8_t *codes, float *R,
+                      float *c, int m, uint16_t *tok_idx, float *tok_val, int W, const float *q,
+                      const float *k, const float *v, const float *a, const float *b, float *o,
+                      float *S_end);
+int oref_comp_quantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                            const float *S, int m, uint8_t *packed, float *row_scale,
+                            float *col_scale, uint16_t *tok_idx, float *tok_val);
+int oref_comp_dequantize_pool(int n_req, int n_head, int dv, int dk, const uint8_t *bits,
+                              const uint8_t *packed, const float *row_scale,
+                              const float *col_scale, int m, const uint16_t *tok_idx,
+                              const float *tok_val, float *S);
+int oref_comp_window_pool(int n_req, int n_head, int dv, int dk, int gate, const uint8_t *bits,
+                          uint8_t *packed, float *row_scale, float *col_scale, int m,
+                          uint16_t *tok_idx, float *tok_val, int W, const float *q,
+                          const float *k, const float *v, const float *a, const float *b,
+                          float *o, long u0, long u1);
+
 /* ---- DAMP-style storage variant ([MEAS] section "DAMP: accuracy depends on the task")
  * Per unit, 16 selected key channels are kept in IEEE binary16 and the other 112 in
  * INT8 with one range per key row and stochastic rounding. Physical positions 0..15 are
