@@ -171,6 +171,44 @@ int qdr_decode_chunk(const qdr_desc *desc, const void *meta, void *packed, float
                      float *col_scale, int32_t T, const float *q, const float *k,
                      const float *v, const float *a, const float *b, float *o, void *stream);
 
+/* ---- compensator tokens (LeapQuant abstract: the state's largest outliers are kept as
+ * a few high-precision tokens that share the update path of the real tokens; the
+ * remaining residual is quantized) ----------------------------------------------------
+ * A token is one state entry kept in fp32, the rank-one term x e_i e_j^T. At each
+ * quantization the m nonzero entries of largest |S_ij| become the unit's tokens, listed
+ * largest first (equal magnitudes: smaller flat index i*dk + j first; j is the logical key
+ * channel), and are set to 0 in the residual, which the STEPQuant rule quantizes.
+ * Unused slots hold index QDR_TOK_EMPTY and value 0. The stored state is the dequantized
+ * residual plus the tokens; a chunk starts from it, so the tokens go through the same
+ * gated delta updates as the rest of the state, and the tokens are selected afresh from
+ * the fp32 state at the chunk's end.
+ * tok_idx: uint16 [n_req][n_head][m] (flat index i*128 + j); tok_val: fp32, same shape;
+ * both caller-owned device buffers, 16-byte aligned. 0 <= m <= QDR_COMP_MAX; m = 0 is the
+ * plain mode. Only QDR_RULE_STEP. Errors: all codes; QDR_EINVAL for m out of range;
+ * QDR_EUNSUPPORTED for another rule. */
+#define QDR_TOK_EMPTY 0xFFFFu
+#define QDR_COMP_MAX 64
+
+/* Tokens of the fp32 state S_in [n_req][n_head][dv][dk] (logical order), then the residual
+ * quantized into (packed, row_scale, col_scale) as qdr_quantize_state does. */
+int qdr_comp_quantize(const qdr_desc *desc, const void *meta, void *packed, float *row_scale,
+                      float *col_scale, int32_t m, uint16_t *tok_idx, float *tok_val,
+                      const float *S_in, void *stream);
+
+/* qdr_decode_chunk on the state with tokens: the chunk starts from the dequantized residual
+ * plus the tokens and ends with new tokens and the requantized residual (all in place).
+ * T = 0 is a no-op. */
+int qdr_comp_chunk(const qdr_desc *desc, const void *meta, void *packed, float *row_scale,
+                   float *col_scale, int32_t m, uint16_t *tok_idx, float *tok_val, int32_t T,
+                   const float *q, const float *k, const float *v, const float *a,
+                   const float *b, float *o, void *stream);
+
+/* The dequantized residual plus the tokens, S_out [n_req][n_head][dv][dk] (logical). */
+int qdr_comp_dequantize(const qdr_desc *desc, const void *meta, const void *packed,
+                        const float *row_scale, const float *col_scale, int32_t m,
+                        const uint16_t *tok_idx, const float *tok_val, float *S_out,
+                        void *stream);
+
 /* Read back the dequantized state S_hat_ij = fl(code_ij * fl(R_j*c_i)) as
  * S_out [n_req][n_head][dv][dk] (logical key order). Errors: all codes. */
 int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *packed,

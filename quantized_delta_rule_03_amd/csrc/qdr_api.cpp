@@ -350,8 +350,91 @@ int qdr_decode_chunk(const qdr_desc* d, const void* meta, void* packed, float* r
   CHECK(check_ptr(o, "o", any));
   return hip_status(qdr::launch_chunk(pool_of(d, meta, g), d->gate, T,
                                       static_cast<uint8_t*>(packed), row_scale, col_scale, q, k,
-                                      v, a, b, o, static_cast<hipStream_t>(stream)),
+                                      v, a, b, o, 0, nullptr, nullptr, nullptr,
+                                      static_cast<hipStream_t>(stream)),
                     "qdr_decode_chunk: launch");
+}
+
+// ---- compensator tokens ---------------------------------------------------------
+
+static int check_comp(const qdr_desc* d, int32_t m, bool any, const void* tok_idx,
+                      const void* tok_val) {
+  if (m < 0 || m > qdr::kCompMax)
+    return fail(QDR_EINVAL, "m = %d outside [0, %d]", m, qdr::kCompMax);
+  if (d->rule != QDR_RULE_STEP)
+    return fail(QDR_EUNSUPPORTED, "compensator tokens take only QDR_RULE_STEP (rule = %d)",
+                d->rule);
+  CHECK(check_ptr(tok_idx, "tok_idx", any && m > 0));
+  CHECK(check_ptr(tok_val, "tok_val", any && m > 0));
+  return QDR_OK;
+}
+
+int qdr_comp_quantize(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
+                      float* col_scale, int32_t m, uint16_t* tok_idx, float* tok_val,
+                      const float* S_in, void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  const bool any = d->n_req > 0;
+  CHECK(check_comp(d, m, any, tok_idx, tok_val));
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(S_in, "S_in", any));
+  if (!any) return ok();
+  return hip_status(qdr::launch_chunk(pool_of(d, meta, g), d->gate, 0,
+                                      static_cast<uint8_t*>(packed), row_scale, col_scale,
+                                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, m,
+                                      tok_idx, tok_val, S_in, static_cast<hipStream_t>(stream)),
+                    "qdr_comp_quantize: launch");
+}
+
+int qdr_comp_chunk(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
+                   float* col_scale, int32_t m, uint16_t* tok_idx, float* tok_val, int32_t T,
+                   const float* q, const float* k, const float* v, const float* a,
+                   const float* b, float* o, void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  if (T < 0) return fail(QDR_EINVAL, "T = %d is negative", T);
+  const bool any = d->n_req > 0 && T > 0;
+  CHECK(check_comp(d, m, any, tok_idx, tok_val));
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(q, "q", any));
+  CHECK(check_ptr(k, "k", any));
+  CHECK(check_ptr(v, "v", any));
+  CHECK(check_ptr(a, "a", any));
+  CHECK(check_ptr(b, "b", any));
+  CHECK(check_ptr(o, "o", any));
+  return hip_status(qdr::launch_chunk(pool_of(d, meta, g), d->gate, T,
+                                      static_cast<uint8_t*>(packed), row_scale, col_scale, q, k,
+                                      v, a, b, o, m, tok_idx, tok_val, nullptr,
+                                      static_cast<hipStream_t>(stream)),
+                    "qdr_comp_chunk: launch");
+}
+
+int qdr_comp_dequantize(const qdr_desc* d, const void* meta, const void* packed,
+                        const float* row_scale, const float* col_scale, int32_t m,
+                        const uint16_t* tok_idx, const float* tok_val, float* S_out,
+                        void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  const bool any = d->n_req > 0;
+  CHECK(check_comp(d, m, any, tok_idx, tok_val));
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(S_out, "S_out", any));
+  const qdr::Pool p = pool_of(d, meta, g);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  CHECK(hip_status(qdr::launch_dequantize(p, static_cast<const uint8_t*>(packed), row_scale,
+                                          col_scale, S_out, s),
+                   "qdr_comp_dequantize: launch"));
+  return hip_status(qdr::launch_comp_add(p.n_unit, m, tok_idx, tok_val, S_out, s),
+                    "qdr_comp_dequantize: launch");
 }
 
 // ---- DAMP-style storage variant ----------------------------------------------

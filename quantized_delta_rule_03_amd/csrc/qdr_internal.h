@@ -82,9 +82,16 @@ hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed,
                          const float* a, const float* b, float* o, hipStream_t s);
 
 // T tokens of every unit in one call; token-major inputs [T][unit][...].
+// m > 0: compensator tokens tok_idx / tok_val [n_unit][m] (read at the start, rewritten
+// at the end); S_in (with T = 0): quantize the given fp32 state instead of a chunk.
 hipError_t launch_chunk(const Pool& p, int gate, int T, uint8_t* packed, float* rs, float* cs,
                         const float* q, const float* k, const float* v, const float* a,
-                        const float* b, float* o, hipStream_t s);
+                        const float* b, float* o, int m, uint16_t* tok_idx, float* tok_val,
+                        const float* S_in, hipStream_t s);
+// S [n_unit][128][128] += the compensator tokens
+hipError_t launch_comp_add(int n_unit, int m, const uint16_t* tok_idx, const float* tok_val,
+                           float* S, hipStream_t s);
+constexpr int kCompMax = 64;
 
 // DAMP-style storage variant (qdr_damp.hip)
 constexpr int kDampHalf = 16;  // key channels per head kept in binary16

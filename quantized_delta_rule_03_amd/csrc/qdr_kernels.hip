@@ -1448,6 +1448,11 @@ struct ChunkArgs {
   const float* a;  // GDN [T][n_unit]; KDA [T][n_unit][128]
   const float* b;  // [T][n_unit]
   float* o;        // [T][n_unit][128]
+  // compensator tokens (m = 0: none): [n_unit][m], flat index i * 128 + j (logical j)
+  int m;
+  uint16_t* tok_idx;
+  float* tok_val;
+  const float* S_in;  // when set: the fp32 state [n_unit][128][128] (logical), T = 0
 };
 
 struct ChunkLds {
@@ -1459,6 +1464,10 @@ struct ChunkLds {
   float ex[2][kD];          // gate products over the two token halves
   float gend[kD];
   float bb[kCB];
+  alignas(16) uint8_t jperm[kD];  // physical position -> logical key channel
+  uint8_t jinv[kD];   // logical key channel -> physical position
+  uint32_t tok_at[64];  // compensator token t: owning thread << 8 | register slot
+  float tok_v[64];
 };
 // After the third barrier of a sub-block the operand arrays are dead; each wave then
 // keeps its private arrays there.
@@ -1507,6 +1516,249 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Compensator tokens (LeapQuant abstract: the largest outliers kept as a few
+// high-precision tokens that share the real tokens' update path): the m nonzero entries
+// of largest |S| (equal magnitudes: smaller flat index i * 128 + j, j logical) are
+// written out largest first and set to 0 before the refit. Candidates are the entries at
+// or above T0, the m-th largest of the 64 lane-quad maxima (m <= 16) or of the 256
+// per-thread maxima (so at least m entries reach it); up to kCandCap of them are ranked
+// in LDS. More candidates (many equal magnitudes) take an exact bisection over the
+// magnitude bits and then over the flat index.
+constexpr int kCandCap = 1024;
+constexpr int kTokMax = 64;
+constexpr uint32_t kTokEmpty = 0xFFFFu;
+struct CompLds {
+  uint2 cand[kCandCap];  // (value bits, flat index)
+  uint32_t qm[kThreads];  // lane-quad (or per-thread) maxima of the magnitude bits
+  uint2 tok[kTokMax];
+  uint32_t n, T0;
+  uint32_t part[2][4];
+};
+static_assert(sizeof(CompLds) <= sizeof(ChunkLds::qpl), "selection scratch fits");
+
+// sum over the work-group (one barrier; `r` alternates the partial slots)
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t x, uint32_t (*part)[4], int r) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  if ((threadIdx.x & 63) == 0) part[r & 1][threadIdx.x >> 6] = x;
+  block_sync();
+  return part[r & 1][0] + part[r & 1][1] + part[r & 1][2] + part[r & 1][3];
+}
+
+__device__ __forceinline__ void comp_select_chunk(float (&S)[2][4][8], const ChunkArgs& A,
+                                                  ChunkLds& L, int u) {
+  CompLds& C = *reinterpret_cast<CompLds*>(&L.qpl[0][0][0]);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rg = lane & 15, jg = lane >> 4;
+  const uint32_t m = (uint32_t)A.m;
+  // logical key channels of this thread's 32 positions, four per word
+  uint32_t jp[8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint2 x = *reinterpret_cast<const uint2*>(&L.jperm[32 * s + 8 * jg]);
+    jp[2 * s] = x.x;
+    jp[2 * s + 1] = x.y;
+  }
+  auto key = [&](int h, int s, int e) { return __float_as_uint(S[h][s][e]) & 0x7FFFFFFFu; };
+  auto flat = [&](int h, int s, int e) {
+    return (uint32_t)((32 * w + 16 * h + rg) * kD) + ((jp[2 * s + (e >> 2)] >> (8 * (e & 3))) & 0xFFu);
+  };
+  uint32_t tmax = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tmax = max(tmax, key(h, s, e));
+  const bool quads = m <= 16;
+  if (quads) {
+    tmax = max(tmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tmax, 0xB1, 0xF, 0xF, false));
+    tmax = max(tmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tmax, 0x4E, 0xF, 0xF, false));
+    if ((lane & 3) == 0) C.qm[tid >> 2] = tmax;
+  } else {
+    C.qm[tid] = tmax;
+  }
+  if (tid == 0) {
+    C.n = 0;
+    C.T0 = 0;
+  }
+  block_sync();
+  // T0: the largest maximum that at least m of the maxima reach
+  if (quads) {
+    if (w == 0) {
+      const uint32_t x = C.qm[lane];
+      uint32_t ge = 0;
+#pragma unroll 16
+      for (int j = 0; j < 64; ++j)
+        ge += (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)x, j) >= x);
+      const uint32_t t0 = wave_max_u32(ge >= m ? x : 0u);
+      if (lane == 0) C.T0 = t0;
+    }
+  } else {
+    // wave w counts for the maxima 64 w + lane against all 256
+    const uint32_t x = C.qm[tid];
+    const uint32_t y0 = C.qm[lane], y1 = C.qm[64 + lane], y2 = C.qm[128 + lane],
+                   y3 = C.qm[192 + lane];
+    uint32_t ge = 0;
+#pragma unroll 16
+    for (int j = 0; j < 64; ++j)
+      ge += (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y0, j) >= x) +
+            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y1, j) >= x) +
+            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y2, j) >= x) +
+            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y3, j) >= x);
+    const uint32_t t0 = wave_max_u32(ge >= m ? x : 0u);
+    if (lane == 0) atomicMax(&C.T0, t0);
+  }
+  block_sync();
+  // candidates: |S| >= T0 and nonzero (T0 raised to the smallest positive magnitude).
+  // The wave counts its candidates, takes one range of slots, then writes them in order.
+  const float T0f = __uint_as_float(max(C.T0, 1u));
+  {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          cnt += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(fabsf(S[h][s][e]) >= T0f));
+    uint32_t base = 0;
+    if (lane == 0 && cnt) base = atomicAdd(&C.n, cnt);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool c = fabsf(S[h][s][e]) >= T0f;
+          const uint64_t mk = __builtin_amdgcn_ballot_w64(c);
+          if (mk) {
+            const uint32_t slot =
+                base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+            if (c && slot < (uint32_t)kCandCap)
+              C.cand[slot] = make_uint2(__float_as_uint(S[h][s][e]), flat(h, s, e));
+            base += (uint32_t)__builtin_popcountll(mk);
+          }
+        }
+  }
+  block_sync();
+  uint32_t n = C.n;
+  if (n > (uint32_t)kCandCap) {
+    // the m-th largest magnitude T (n > kCandCap >= m nonzero entries exist), then the
+    // flat-index cut among the entries of magnitude T
+    int r = 0;
+    uint32_t T = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cnt += (uint32_t)(key(h, s, e) >= c);
+      if (block_sum_u32(cnt, C.part, r++) >= m) T = c;
+    }
+    uint32_t gt = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gt += (uint32_t)(key(h, s, e) > T);
+    const uint32_t need = m - block_sum_u32(gt, C.part, r++);
+    uint32_t lo = 0, hi = kD * kD - 1;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            cnt += (uint32_t)(key(h, s, e) == T && flat(h, s, e) <= mid);
+      if (block_sum_u32(cnt, C.part, r++) >= need) hi = mid;
+      else lo = mid + 1;
+    }
+    if (tid == 0) C.n = 0;
+    block_sync();
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t kk = key(h, s, e);
+          if (kk >= T && (kk > T || flat(h, s, e) <= lo)) {
+            const uint32_t slot = atomicAdd(&C.n, 1u);
+            C.cand[slot] = make_uint2(__float_as_uint(S[h][s][e]), flat(h, s, e));
+          }
+        }
+    block_sync();
+    n = C.n;  // == m
+  }
+  // rank the candidates; the first m are the tokens, in order. G threads (adjacent lanes)
+  // share a candidate, each scanning every G-th entry of the list; the list is padded to a
+  // multiple of 8 G with zero keys, which rank below every candidate.
+  uint32_t G = 1;
+  while (G < 64 && 2 * G * n <= (uint32_t)kThreads) G *= 2;
+  const uint32_t nP = (n + 8 * G - 1) / (8 * G) * (8 * G);
+  for (uint32_t x = n + tid; x < nP; x += kThreads) C.cand[x] = make_uint2(0u, 0xFFFFFFFFu);
+  block_sync();
+  const uint32_t part = (uint32_t)tid & (G - 1);
+  for (uint32_t c0 = 0; c0 < n; c0 += kThreads / G) {
+    const uint32_t c = c0 + (uint32_t)tid / G;
+    uint2 me = make_uint2(0u, 0u);
+    uint32_t rk = 0;
+    if (c < n) {
+      me = C.cand[c];
+      const uint32_t km = me.x & 0x7FFFFFFFu;
+      for (uint32_t d = part; d < nP; d += 8 * G) {
+        uint2 ot[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) ot[x] = C.cand[d + x * G];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const uint32_t ko = ot[x].x & 0x7FFFFFFFu;
+          rk += (uint32_t)(ko > km || (ko == km && ot[x].y < me.y));
+        }
+      }
+    }
+    for (uint32_t o = 1; o < G; o <<= 1) rk += __shfl_xor(rk, (int)o);
+    if (c < n && part == 0 && rk < m) C.tok[rk] = me;
+  }
+  block_sync();
+  const uint32_t nv = min(n, m);
+  if ((uint32_t)tid < m) {
+    const size_t o = (size_t)u * m + tid;
+    const bool valid = (uint32_t)tid < nv;
+    A.tok_idx[o] = valid ? (uint16_t)C.tok[tid].y : (uint16_t)kTokEmpty;
+    A.tok_val[o] = valid ? __uint_as_float(C.tok[tid].x) : 0.0f;
+  }
+  if (nv > 0) {
+    // the selected entries: above the last token's magnitude, or equal to it at a flat
+    // index up to the last token's
+    const uint2 last = C.tok[nv - 1];
+    const uint32_t kl = last.x & 0x7FFFFFFFu;
+    const float klf = __uint_as_float(kl);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool c = fabsf(S[h][s][e]) >= klf;
+          if (__builtin_amdgcn_ballot_w64(c)) {
+            const uint32_t kk = key(h, s, e);
+            if (c && (kk > kl || flat(h, s, e) <= last.y)) S[h][s][e] = 0.0f;
+          }
+        }
+  }
+  block_sync();  // the scratch is reused by the refit
+}
+
 template <int GATE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) k_chunk(ChunkArgs A) {
   __shared__ __attribute__((aligned(16))) ChunkLds L;
@@ -1519,8 +1771,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const size_t ts = (size_t)A.n_unit * kD;  // token stride of q, k, v, o (and KDA a)
   const int T = A.T;
 
-  // dequantize: S_ij = fl(code fl(R_j c_i)) (the decode step's readback)
+  if (tid < kD) {
+    const int j = mh->identity ? tid : (int)mh->perm[tid];
+    L.jperm[tid] = (uint8_t)j;
+    L.jinv[j] = (uint8_t)tid;
+  }
   float S[2][4][8];
+  if (A.S_in) {
+    // a given fp32 state (logical key order), gathered into the register layout
+    const float* Su = A.S_in + (size_t)u * kD * kD;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int p = 32 * s + 8 * jg + e;
+        const int j = mh->identity ? p : (int)mh->perm[p];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) S[h][s][e] = Su[(32 * w + 16 * h + rg) * kD + j];
+      }
+  } else {
+  // dequantize: S_ij = fl(code fl(R_j c_i)) (the decode step's readback)
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const Seg sg = seg_from(cur.sb, s);
@@ -1538,6 +1808,48 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
       for (int e = 0; e < 8; ++e) S[h][s][e] = (f[e] - bias) * (R[e] * c);
     }
+  }
+  // the compensator tokens rejoin the state (their residual entries dequantize to 0):
+  // each token is placed by one thread, then every thread adds those it owns
+  if (A.m > 0) {
+    block_sync();  // jinv
+    const int m4 = (A.m + 3) & ~3;
+    if (tid < m4) {
+      uint32_t at = 0xFFFFFFFFu;
+      float val = 0.0f;
+      if (tid < A.m) {
+        const uint32_t ix = A.tok_idx[(size_t)u * A.m + tid];
+        if (ix < (uint32_t)(kD * kD)) {
+          const int i = (int)(ix >> 7), p = L.jinv[ix & (kD - 1)];
+          const uint32_t owner = (uint32_t)((i >> 5) * 64 + (i & 15) + 16 * ((p >> 3) & 3));
+          const uint32_t slot = (uint32_t)(((i >> 4) & 1) * 32 + (p >> 5) * 8 + (p & 7));
+          at = owner << 8 | slot;
+          val = A.tok_val[(size_t)u * A.m + tid];
+        }
+      }
+      L.tok_at[tid] = at;
+      L.tok_v[tid] = val;
+    }
+    block_sync();
+    for (int t = 0; t < m4; t += 4) {
+      const uint4 at4 = *reinterpret_cast<const uint4*>(&L.tok_at[t]);
+      const uint32_t ats[4] = {at4.x, at4.y, at4.z, at4.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((ats[c] >> 8) == (uint32_t)tid) {
+          const float val = L.tok_v[t + c];
+          const int slot = (int)(ats[c] & 63u);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (32 * h + 8 * s + e == slot) S[h][s][e] += val;
+        }
+      }
+    }
+  }
   }
   const int pl = tid & (kD - 1), half = tid >> 7;
   const int jl = mh->identity ? pl : (int)mh->perm[pl];
@@ -1569,7 +1881,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     f.b = tb < T ? bv : 0.0f;
   };
   ChunkPf pf;
-  issue(0, pf);
+  if (T > 0) issue(0, pf);
 
   for (int t0 = 0; t0 < T; t0 += kCB) {
     // A1. gate products over this thread's 8 tokens; the two halves exchange totals
@@ -1839,6 +2151,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   }
   block_sync();
 
+  if (A.m > 0) comp_select_chunk(S, A, L, u);
+
   // refit + requantize (the decode step's rule). Key-row absmax: the lane's two rows, the
   // 16 lanes of its DPP row (same positions), then the four waves.
   float* scr = reinterpret_cast<float*>(&L.kpl[0][0][0]);
@@ -1897,6 +2211,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       QDR_WIDTH_DISPATCH(0, sg.bits, (requant_row<BB>(seg, row, jg, S[h][s], M)));
     }
   }
+}
+
+// S += tokens (one thread per token slot)
+__global__ void __launch_bounds__(64) k_comp_add(int m, const uint16_t* tok_idx,
+                                                 const float* tok_val, float* S) {
+  const int t = threadIdx.x;
+  const size_t u = blockIdx.x;
+  if (t >= m) return;
+  const uint32_t ix = tok_idx[u * m + t];
+  if (ix >= (uint32_t)(kD * kD)) return;  // empty slot
+  S[u * kD * kD + ix] += tok_val[u * m + t];
 }
 
 int g_step_grid[2][2][3] = {};
@@ -1990,11 +2315,20 @@ hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed,
 
 hipError_t launch_chunk(const Pool& p, int gate, int T, uint8_t* packed, float* rs, float* cs,
                         const float* q, const float* k, const float* v, const float* a,
-                        const float* b, float* o, hipStream_t s) {
-  if (p.n_unit == 0 || T == 0) return hipSuccess;
-  ChunkArgs A{p.meta, p.n_head, p.n_unit, T, p.req_bytes, packed, rs, cs, q, k, v, a, b, o};
+                        const float* b, float* o, int m, uint16_t* tok_idx, float* tok_val,
+                        const float* S_in, hipStream_t s) {
+  if (p.n_unit == 0 || (T == 0 && !S_in)) return hipSuccess;
+  ChunkArgs A{p.meta, p.n_head, p.n_unit, T, p.req_bytes, packed, rs, cs, q, k, v, a, b, o,
+              m, tok_idx, tok_val, S_in};
   if (gate == GDN) hipLaunchKernelGGL(k_chunk<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
   else hipLaunchKernelGGL(k_chunk<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_comp_add(int n_unit, int m, const uint16_t* tok_idx, const float* tok_val,
+                           float* S, hipStream_t s) {
+  if (n_unit == 0 || m == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_comp_add, dim3(n_unit), dim3(64), 0, s, m, tok_idx, tok_val, S);
   return hipGetLastError();
 }
 

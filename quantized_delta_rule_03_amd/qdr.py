@@ -29,7 +29,8 @@ RULE_STEP, RULE_KEYROW, RULE_TENSOR = 0, 1, 2  # scale rules (QDR_RULE_*)
 SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize_state",
            "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk", "qdr_dequantize_state",
            "qdr_damp_select", "qdr_damp_bytes", "qdr_damp_init", "qdr_damp_quantize", "qdr_damp_step",
-           "qdr_damp_dequantize", "qdr_last_error")
+           "qdr_damp_dequantize", "qdr_comp_quantize", "qdr_comp_chunk", "qdr_comp_dequantize",
+           "qdr_last_error")
 
 
 class QdrError(RuntimeError):
@@ -80,6 +81,9 @@ def lib():
             "qdr_damp_step": [DD, P, P, P, P, P, P, P, P, P, P, u64, u64, P],
             "qdr_damp_dequantize": [DD, P, P, P, P, P, P],
             "qdr_dequantize_state": [D, P, P, P, P, P, P],
+            "qdr_comp_quantize": [D, P, P, P, P, i32, P, P, P, P],
+            "qdr_comp_chunk": [D, P, P, P, P, i32, P, P, i32, P, P, P, P, P, P, P],
+            "qdr_comp_dequantize": [D, P, P, P, P, i32, P, P, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -194,6 +198,32 @@ def dequantize_state(L: Layout, meta, packed, row_scale, col_scale, S_out, strea
            "qdr_dequantize_state")
 
 
+TOK_EMPTY = 0xFFFF  # empty compensator-token slot
+COMP_MAX = 64
+
+
+def comp_quantize(L: Layout, meta, packed, row_scale, col_scale, m, tok_idx, tok_val, S,
+                  stream=None):
+    _check(lib().qdr_comp_quantize(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                   _ptr(col_scale), int(m), _ptr(tok_idx), _ptr(tok_val), _ptr(S),
+                                   _stream(stream)), "qdr_comp_quantize")
+
+
+def comp_chunk(L: Layout, meta, packed, row_scale, col_scale, m, tok_idx, tok_val, T, q, k, v,
+               a, b, o, stream=None):
+    _check(lib().qdr_comp_chunk(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                _ptr(col_scale), int(m), _ptr(tok_idx), _ptr(tok_val), int(T),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(o),
+                                _stream(stream)), "qdr_comp_chunk")
+
+
+def comp_dequantize(L: Layout, meta, packed, row_scale, col_scale, m, tok_idx, tok_val, S_out,
+                    stream=None):
+    _check(lib().qdr_comp_dequantize(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                     _ptr(col_scale), int(m), _ptr(tok_idx), _ptr(tok_val),
+                                     _ptr(S_out), _stream(stream)), "qdr_comp_dequantize")
+
+
 class StatePool:
     """Caller-owned device buffers of one layer's quantized state (torch allocations)."""
 
@@ -253,6 +283,50 @@ class StatePool:
         n = self.layout.packed_bytes
         return (self.packed[:n].cpu().numpy().reshape(self.layout.n_req, -1),
                 self.row_scale.cpu().numpy(), self.col_scale.cpu().numpy())
+
+    # compensator tokens: tok_idx (uint16 bits in an int16 tensor) and tok_val,
+    # [n_req, n_head, m]; empty slots until the first comp_quantize / comp_chunk
+    def comp_enable(self, m: int):
+        import torch
+
+        L = self.layout
+        self.m = int(m)
+        shape = (L.n_req, L.n_head, max(self.m, 1))
+        self.tok_idx = torch.full(shape, -1, dtype=torch.int16, device=self.device)
+        self.tok_val = torch.zeros(shape, dtype=torch.float32, device=self.device)
+
+    def comp_quantize(self, S, m: int, stream=None):
+        self.comp_enable(m)
+        comp_quantize(self.layout, self.meta, self.packed, self.row_scale, self.col_scale,
+                      self.m, self.tok_idx, self.tok_val, S, stream)
+
+    def comp_chunk(self, q, k, v, a, b, o, stream=None):
+        comp_chunk(self.layout, self.meta, self.packed, self.row_scale, self.col_scale, self.m,
+                   self.tok_idx, self.tok_val, int(b.shape[0]), q, k, v, a, b, o, stream)
+
+    def comp_dequantize(self, S_out=None, stream=None):
+        import torch
+
+        if S_out is None:
+            S_out = torch.empty((self.layout.n_req, self.layout.n_head, 128, 128),
+                                dtype=torch.float32, device=self.device)
+        comp_dequantize(self.layout, self.meta, self.packed, self.row_scale, self.col_scale,
+                        self.m, self.tok_idx, self.tok_val, S_out, stream)
+        return S_out
+
+    def comp_load_host(self, tok_idx: np.ndarray, tok_val: np.ndarray):
+        import torch
+
+        self.comp_enable(tok_idx.shape[-1])
+        if self.m:
+            idx = np.ascontiguousarray(tok_idx, np.uint16).view(np.int16)
+            self.tok_idx.copy_(torch.from_numpy(idx))
+            self.tok_val.copy_(torch.from_numpy(np.ascontiguousarray(tok_val, np.float32)))
+
+    def comp_to_host(self):
+        m = self.m
+        return (self.tok_idx.cpu().numpy().view(np.uint16)[..., :m],
+                self.tok_val.cpu().numpy()[..., :m])
 
 
 def damp_select(gate: int, halflife: np.ndarray, n_head: int) -> np.ndarray:

@@ -138,6 +138,34 @@ def test_chunk_validation():
     assert rc == qdr.QDR_EALIGN and "k" in qdr.last_error()
 
 
+def test_comp_validation():
+    """Compensator-token entry points: m range, rule, token buffers (no GPU work)."""
+    d, keep = _desc()
+    L = qdr.lib()
+    P = 1 << 20
+    for bad in (-1, qdr.COMP_MAX + 1):
+        rc = L.qdr_comp_chunk(ctypes.byref(d), P, P, P, P, bad, P, P, 8, P, P, P, P, P, P, None)
+        assert rc == qdr.QDR_EINVAL and f"m = {bad}" in qdr.last_error()
+    rc = L.qdr_comp_quantize(ctypes.byref(d), P, P, P, P, 4, None, P, P, None)
+    assert rc == qdr.QDR_EINVAL and "tok_idx is NULL" in qdr.last_error()
+    rc = L.qdr_comp_dequantize(ctypes.byref(d), P, P, P, P, 4, P, P + 8, P, None)
+    assert rc == qdr.QDR_EALIGN and "tok_val" in qdr.last_error()
+    rc = L.qdr_comp_chunk(ctypes.byref(d), P, P, P, P, 4, P, P, -2, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EINVAL and "T = -2" in qdr.last_error()
+    rc = L.qdr_comp_quantize(ctypes.byref(d), P, P, P, P, 4, P, P, None, None)
+    assert rc == qdr.QDR_EINVAL and "S_in is NULL" in qdr.last_error()
+    d, keep = _desc(rule=qdr.RULE_KEYROW)
+    rc = L.qdr_comp_quantize(ctypes.byref(d), P, P, P, P, 4, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED and "QDR_RULE_STEP" in qdr.last_error()
+    # nothing to do: zero requests or T = 0 with no buffers at all
+    d, keep = _desc(n_req=0)
+    assert L.qdr_comp_quantize(ctypes.byref(d), P, None, None, None, 4, None, None, None,
+                               None) == qdr.QDR_OK
+    d, keep = _desc()
+    assert L.qdr_comp_chunk(ctypes.byref(d), P, None, None, None, 4, None, None, 0, None, None,
+                            None, None, None, None, None) == qdr.QDR_OK
+
+
 def test_rule_validation():
     L = qdr.lib()
     P = 1 << 20
