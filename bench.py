@@ -13,7 +13,8 @@ on host threads over a bounded sample of the same workload.
 
 ``--workload window`` and ``--workload chunk`` time the windowed serving shape (256
 requests x 32 KDA heads, 8-bit, windows of 64 tokens) in window mode (one call per
-token) and in chunk mode (one call per window) instead.
+token) and in chunk mode (one call per window) instead; ``--workload comp`` times chunk
+mode with 16 compensator tokens per state.
 """
 from __future__ import annotations
 
@@ -34,6 +35,8 @@ HBM_PEAK_GBPS = 8000.0
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 PROFILE = os.path.join(ROOT, "profiles", "k_step_gdn_serving_1024x32.md")
 PROFILE_CHUNK = os.path.join(ROOT, "profiles", "k_chunk_kda_256x32_t64.md")
+PROFILE_COMP = os.path.join(ROOT, "profiles", "k_chunk_comp16_kda_256x32_t64.md")
+COMP_TOKENS = 16  # compensator tokens per unit in the --workload comp line
 
 
 def log(msg):
@@ -146,24 +149,31 @@ def bench_window(args, torch, qdr, wl, dev):
     }
 
 
-def chunk_algorithmic_bytes(tile_bytes: int, n_unit: int, T: int) -> int:
+def chunk_algorithmic_bytes(tile_bytes: int, n_unit: int, T: int, m: int = 0) -> int:
     """Bytes one chunk call (T tokens) must move: the packed state and its scales read
     once and written once; per token q, k, v, the per-channel gate and b read and o
+    written; with m compensator tokens, their index (2 B) and value (4 B) read and
     written."""
-    per_unit = 2 * (tile_bytes + 2 * 512) + T * (3 * 512 + 512 + 4 + 512)
+    per_unit = 2 * (tile_bytes + 2 * 512) + T * (3 * 512 + 512 + 4 + 512) + 2 * 6 * m
     return per_unit * n_unit
 
 
-def bench_chunk(args, torch, qdr, wl, dev):
+def bench_chunk(args, torch, qdr, wl, dev, m=0):
     """Chunk mode on the windowed serving shape (256 requests x 32 KDA heads, 8-bit): one
-    qdr_decode_chunk call takes the window's T = 64 tokens at once."""
+    qdr_decode_chunk call takes the window's T = 64 tokens at once. m > 0: the same with
+    m compensator tokens per state (qdr_comp_chunk)."""
     w = wl.WORKLOADS[4]
     bits = wl.uniform_bits(w.n_head, 8)
     T = w.window
     pool = qdr.StatePool(w.n_req, w.n_head, w.gate, bits, device=dev)
     g = torch.Generator(device=dev)
     g.manual_seed(args.seed)
-    pool.quantize(0.1 * torch.randn((w.n_req, w.n_head, 128, 128), generator=g, device=dev))
+    S0 = 0.1 * torch.randn((w.n_req, w.n_head, 128, 128), generator=g, device=dev)
+    if m:
+        pool.comp_quantize(S0, m)
+    else:
+        pool.quantize(S0)
+    del S0
     a1 = torch.from_numpy(wl.static_gate(w, args.seed)).to(dev)
     n_chunk = max(16, args.steps // T)  # at least 16 calls (about 13 ms) in the timed region
     log(f"generating {T} tokens of inputs on the device")
@@ -175,7 +185,10 @@ def bench_chunk(args, torch, qdr, wl, dev):
     stream = torch.cuda.current_stream()
 
     def chunk():
-        pool.chunk(x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
+        if m:
+            pool.comp_chunk(x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
+        else:
+            pool.chunk(x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
 
     for _ in range(max(1, args.warmup)):
         chunk()
@@ -192,24 +205,29 @@ def bench_chunk(args, torch, qdr, wl, dev):
     wall = time.perf_counter() - t0
     chunk_s = float(np.mean([s.elapsed_time(e) for s, e in ev])) / 1e3
     n_unit = w.n_unit
-    nbytes = chunk_algorithmic_bytes(pool.layout.packed_bytes // w.n_req // w.n_head, n_unit, T)
+    nbytes = chunk_algorithmic_bytes(pool.layout.packed_bytes // w.n_req // w.n_head, n_unit, T,
+                                     m)
     achieved = nbytes / chunk_s / 1e9
     tokens = n_chunk * T
-    log(f"chunk: {chunk_s * 1e6:.1f} us per {T}-token call, {chunk_s * 1e6 / T:.2f} us per token; "
-        f"{achieved:.0f} GB/s algorithmic ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
-    prof = profile_record(PROFILE_CHUNK)
+    log(f"chunk (m={m}): {chunk_s * 1e6:.1f} us per {T}-token call, {chunk_s * 1e6 / T:.2f} us "
+        f"per token; {achieved:.0f} GB/s algorithmic "
+        f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    prof = profile_record(PROFILE_COMP if m else PROFILE_CHUNK)
     traffic = float(prof["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in prof else None
+    comp = f", {m} compensator tokens" if m else ""
     return {
-        "metric": "token-updates/s (req x head), chunk mode T=64, 256-req KDA 8-bit",
+        "metric": f"token-updates/s (req x head), chunk mode T=64{comp}, 256-req KDA 8-bit",
         "value": n_unit * tokens / wall,
         "unit": "token-updates/s",
         "n_gpus": 1, "steps": tokens, "warmup": max(1, args.warmup) * T,
         "ms_per_step": wall * 1e3 / tokens,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name + " (chunk)", "n_req": w.n_req, "n_head": w.n_head,
+        "config": {"workload": w.name + (" (chunk, compensator tokens)" if m else " (chunk)"),
+                   "n_req": w.n_req, "n_head": w.n_head,
                    "dk": 128, "dv": 128, "gate": "KDA per-channel, half-life log-uniform [1, 8192]",
-                   "bits": "8 (uniform)", "tokens_per_call": T, "parallelism": "single GPU"},
+                   "bits": "8 (uniform)", "tokens_per_call": T, "compensator_tokens": m,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_chunk<KDA>", "bytes_per_call": nbytes,
@@ -354,10 +372,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=1024)
     ap.add_argument("--cpu-steps", type=int, default=24)
-    ap.add_argument("--workload", choices=["serving", "window", "chunk", "compare", "damp"],
+    ap.add_argument("--workload",
+                    choices=["serving", "window", "chunk", "comp", "compare", "damp"],
                     default="serving",
                     help="serving: the decode-step metric (default); window: window mode "
                          "(one call per token); chunk: chunk mode (one call per window); "
+                         "comp: chunk mode with compensator tokens; "
                          "compare: the decode step under each scale rule; damp: the "
                          "DAMP-style storage variant")
     args = ap.parse_args()
@@ -379,6 +399,9 @@ def main():
         return
     if args.workload == "chunk":
         print(json.dumps(bench_chunk(args, torch, qdr, wl, dev)), flush=True)
+        return
+    if args.workload == "comp":
+        print(json.dumps(bench_chunk(args, torch, qdr, wl, dev, m=COMP_TOKENS)), flush=True)
         return
     if args.workload == "compare":
         print(json.dumps(bench_compare(args, torch, qdr, wl, dev)), flush=True)
