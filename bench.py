@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-updates/s (req x head) and % of HBM roofline, 1024-req mixed 6-bit"
 HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK = 2.5e15  # dense bf16 matrix FLOP/s of MI355X
 # non-packed fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 PROFILE = os.path.join(ROOT, "profiles", "k_step_gdn_serving_1024x32.md")
@@ -158,6 +159,16 @@ def chunk_algorithmic_bytes(tile_bytes: int, n_unit: int, T: int, m: int = 0) ->
     return per_unit * n_unit
 
 
+def chunk_mfma_flops(n_unit: int, T: int) -> float:
+    """Matrix-core FLOPs of one chunk call as the kernel schedules them: per unit and
+    16-token sub-block, 624 v_mfma_f32_16x16x32_bf16 (S_r(gam k) and S_r(gam q): 96 per wave,
+    the wave's Gram partials: 12, the state update: 48; each 16x16x32x2 FLOPs, the six bf16
+    part products of the three-way operand split counted as issued) and 32
+    v_mfma_f32_16x16x4_f32 (readouts, 16x16x4x2 FLOPs each)."""
+    n_sub = -(-T // 16)
+    return float(n_unit) * n_sub * (624 * 16 * 16 * 32 * 2 + 32 * 16 * 16 * 4 * 2)
+
+
 def bench_chunk(args, torch, qdr, wl, dev, m=0):
     """Chunk mode on the windowed serving shape (256 requests x 32 KDA heads, 8-bit): one
     qdr_decode_chunk call takes the window's T = 64 tokens at once. m > 0: the same with
@@ -214,6 +225,15 @@ def bench_chunk(args, torch, qdr, wl, dev, m=0):
         f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
     prof = profile_record(PROFILE_COMP if m else PROFILE_CHUNK)
     traffic = float(prof["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in prof else None
+    flops = chunk_mfma_flops(n_unit, T)
+    mfma = {"flops_per_call": flops, "achieved": flops / chunk_s, "peak": BF16_MFMA_PEAK,
+            "unit": "FLOP/s", "frac": flops / chunk_s / BF16_MFMA_PEAK}
+    valu = None
+    if "SQ_INSTS_VALU" in prof:
+        lane_ops = float(prof["SQ_INSTS_VALU"]) * 64
+        valu = {"lane_ops_per_launch": lane_ops, "achieved": lane_ops / chunk_s,
+                "peak": VALU_PEAK_LANE_OPS, "unit": "lane-ops/s",
+                "frac": lane_ops / chunk_s / VALU_PEAK_LANE_OPS}
     comp = f", {m} compensator tokens" if m else ""
     return {
         "metric": f"token-updates/s (req x head), chunk mode T=64{comp}, 256-req KDA 8-bit",
@@ -232,6 +252,8 @@ def bench_chunk(args, torch, qdr, wl, dev, m=0):
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_chunk<KDA>", "bytes_per_call": nbytes,
                      "avg_call_us": chunk_s * 1e6},
+        "mfma": mfma,
+        "valu": valu,
         "cpu_baseline": None,
     }
 
