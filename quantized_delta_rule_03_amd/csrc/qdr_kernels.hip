@@ -744,13 +744,13 @@ __device__ __forceinline__ Raw lds_row(const uint8_t* seg, int B, int i, int jg)
 // lane (4 planes of one row per 16-row block) into upart. The operands carry the
 // factor code_scale<B>(), which the segment's sum scales remove.
 template <int B>
-__device__ __forceinline__ void plane_sums(const StepWork& W, double* upart, const uint8_t* seg,
-                                           int w, int rg, int jg, long (&op)[8]) {
+__device__ __forceinline__ void plane_sums_raw(const StepWork& W, double* upart, const Raw (&raw)[8],
+                                               int w, int rg, int jg, long (&op)[8]) {
   const long a_op = *reinterpret_cast<const long*>(&W.dig[w][rg][jg][0]);
   const v4i zero = {0, 0, 0, 0};
   const Sel6 sl = sel6_for(jg);
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) op[rr] = code_operand<B>(lds_row(seg, B, rg + 16 * rr, jg), jg, sl);
+  for (int rr = 0; rr < 8; ++rr) op[rr] = code_operand<B>(raw[rr], jg, sl);
   // Keep the operands as built (they are reused for the update): without this the
   // compiler re-derives each field from the packed word instead of reading its byte.
 #pragma unroll
@@ -765,6 +765,15 @@ __device__ __forceinline__ void plane_sums(const StepWork& W, double* upart, con
     const v4i d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a_op, op[rr], zero, 0, 0, 0);
     upart[(4 * w + jg) * kDS + rg + 16 * rr] = combine4(d);
   }
+}
+
+template <int B>
+__device__ __forceinline__ void plane_sums(const StepWork& W, double* upart, const uint8_t* seg,
+                                           int w, int rg, int jg, long (&op)[8]) {
+  Raw raw[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) raw[rr] = lds_row(seg, B, rg + 16 * rr, jg);
+  plane_sums_raw<B>(W, upart, raw, w, rg, jg, op);
 }
 
 // Phase 3 for one code width: dequantize + gate and apply the rank-one update,
@@ -1148,6 +1157,14 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   float* Kt = win_kt(A, u);
   float* Wv = Kt + (size_t)W * kD;
   float* gbuf = Wv + (size_t)W * kD;
+  // the fixed state's rows, straight from HBM (each is used once per token), in flight
+  // while the token's vectors are staged and the digit planes formed
+  Raw raw[8];
+  {
+    const uint8_t* seg = A.packed + cur.toff + sg.off;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) raw[rr] = load_row_any(seg, Bw, rg + 16 * rr, jg);
+  }
 
   // 1. this token's vectors to LDS
   if (tid < kD) {
@@ -1174,9 +1191,7 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   wait_lgkm();
   __builtin_amdgcn_wave_barrier();
   long op[8];
-  // (the fixed state's rows are read straight from HBM: each is used once per token)
-  QDR_WIDTH_DISPATCH(0, Bw, (plane_sums<BB>(L.W, L.W.part.upart, A.packed + cur.toff + sg.off, w, rg,
-                                            jg, op)));
+  QDR_WIDTH_DISPATCH(0, Bw, (plane_sums_raw<BB>(L.W, L.W.part.upart, raw, w, rg, jg, op)));
   __syncthreads();
   {
     const int i = tid & (kD - 1);
@@ -1197,26 +1212,44 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   }
 
   // 3. buffered keys: decay by a_t in place; dot with k_t and q_t over this wave's 32
-  //    positions (one lane per buffered token)
-  for (int i = lane; i < t; i += 64) {
-    u32x4* kt = reinterpret_cast<u32x4*>(Kt + (size_t)i * kD + 32 * w);
-    float sa = 0.0f, sb = 0.0f;
+  //    positions. Eight lanes share a buffered token (16 bytes each: one contiguous
+  //    128-byte segment per token and load), eight tokens per pass; the eight partial
+  //    sums combine in a fixed butterfly order.
+  {
+    const int sub = lane & 7, tk = lane >> 3;
+    const int pb = 32 * w + 4 * sub;
+    float apl[4], kpl[4], qpl[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      u32x4 x = kt[c];
-      float e[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int p = 32 * w + 4 * c + m;
-        e[m] = __uint_as_float(x[m]) * L.ap[p];
-        sa = fmaf(e[m], L.W.kp[p], sa);
-        sb = fmaf(e[m], L.qp[p], sb);
-        x[m] = __float_as_uint(e[m]);
-      }
-      kt[c] = x;
+    for (int m = 0; m < 4; ++m) {
+      apl[m] = L.ap[pb + m];
+      kpl[m] = L.W.kp[pb + m];
+      qpl[m] = L.qp[pb + m];
     }
-    L.ab[0][w][i] = sa;
-    L.ab[1][w][i] = sb;
+    for (int i0 = 0; i0 < t; i0 += 8) {
+      const int i = i0 + tk;
+      float sa = 0.0f, sb = 0.0f;
+      if (i < t) {
+        u32x4* kt = reinterpret_cast<u32x4*>(Kt + (size_t)i * kD + pb);
+        u32x4 x = *kt;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float e = __uint_as_float(x[m]) * apl[m];
+          sa = fmaf(e, kpl[m], sa);
+          sb = fmaf(e, qpl[m], sb);
+          x[m] = __float_as_uint(e);
+        }
+        *kt = x;
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        sa += __shfl_xor(sa, o);
+        sb += __shfl_xor(sb, o);
+      }
+      if (sub == 0 && i < t) {
+        L.ab[0][w][i] = sa;
+        L.ab[1][w][i] = sb;
+      }
+    }
   }
   __syncthreads();
   if (tid < t) {
@@ -1525,7 +1558,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 // in LDS. More candidates (many equal magnitudes) take an exact bisection over the
 // magnitude bits and then over the flat index.
 constexpr int kCandCap = 1024;
-constexpr int kTokMax = 64;
+constexpr int kTokMax = kCompMax;
 constexpr uint32_t kTokEmpty = 0xFFFFu;
 struct CompLds {
   uint2 cand[kCandCap];  // (value bits, flat index)
@@ -2224,7 +2257,9 @@ __global__ void __launch_bounds__(64) k_comp_add(int m, const uint16_t* tok_idx,
   S[u * kD * kD + ix] += tok_val[u * m + t];
 }
 
-int g_step_grid[2][2][3] = {};
+// persistent grid of each decode-step variant, per device (occupancy x CU count)
+constexpr int kMaxDevices = 64;
+int g_step_grid[kMaxDevices][2][2][3] = {};
 
 }  // namespace
 
@@ -2257,10 +2292,11 @@ hipError_t launch_dequantize(const Pool& p, const uint8_t* packed, const float* 
 // depend on it).
 template <int GATE, bool UNIFORM, int RULE>
 static int step_grid(int n_unit) {
-  int& g = g_step_grid[GATE][UNIFORM ? 1 : 0][RULE];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int& g = g_step_grid[dev >= 0 && dev < kMaxDevices ? dev : 0][GATE][UNIFORM ? 1 : 0][RULE];
   if (g == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    (void)hipGetDevice(&dev);
+    int cus = 0, per_cu = 0;
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<GATE, UNIFORM, RULE>,
                                                        kThreads, 0);
