@@ -505,12 +505,13 @@ class DampPool:
                                         _p(self.half), _p(self.codes), _p(self.R), _p(S))
         return S.reshape(self.n_req, self.n_head, 128, 128)
 
-    def step(self, gate, q, k, v, a, b, step: int):
+    def step(self, gate, q, k, v, a, b, step: int, u0: int = 0, u1=None):
+        """One step on units [u0, u1) (default all); returns o for the whole pool."""
         q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
         a, b = _c(a, np.float32), _c(b, np.float32)
         o = np.zeros((self.n_req, self.n_head, 128), np.float32)
         lib().oref_damp_step_pool(self.n_unit, self.n_head, 128, gate, _p(self.perm),
                                   _p(self.half), _p(self.codes), _p(self.R), _p(q), _p(k),
-                                  _p(v), _p(a), _p(b), _p(o), self.seed, int(step), 0,
-                                  self.n_unit)
+                                  _p(v), _p(a), _p(b), _p(o), self.seed, int(step), int(u0),
+                                  self.n_unit if u1 is None else int(u1))
         return o
