@@ -324,8 +324,8 @@ int qdr_decode_window(const qdr_desc* d, const void* meta, void* packed, float* 
   CHECK(check_ptr(o, "o", any));
   return hip_status(qdr::launch_window(pool_of(d, meta, g), d->gate, d->window, t,
                                        static_cast<uint8_t*>(packed), row_scale, col_scale,
-                                       static_cast<uint8_t*>(window_buf), q, k, v, a, b, o,
-                                       static_cast<hipStream_t>(stream)),
+                                       static_cast<uint8_t*>(window_buf), q, k, v, a, b, o, 0,
+                                       nullptr, nullptr, static_cast<hipStream_t>(stream)),
                     "qdr_decode_window: launch");
 }
 
@@ -413,6 +413,37 @@ int qdr_comp_chunk(const qdr_desc* d, const void* meta, void* packed, float* row
                                       v, a, b, o, m, tok_idx, tok_val, nullptr,
                                       static_cast<hipStream_t>(stream)),
                     "qdr_comp_chunk: launch");
+}
+
+int qdr_comp_window(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
+                    float* col_scale, int32_t m, uint16_t* tok_idx, float* tok_val,
+                    void* window_buf, int32_t t, const float* q, const float* k, const float* v,
+                    const float* a, const float* b, float* o, void* stream) {
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  if (d->window < 1) return fail(QDR_EUNSUPPORTED, "desc->window = %d: no window mode", d->window);
+  if (d->window > qdr::kWindowMax)
+    return fail(QDR_EUNSUPPORTED, "desc->window = %d exceeds %d", d->window, qdr::kWindowMax);
+  if (t < 0 || t >= d->window)
+    return fail(QDR_EUNSUPPORTED, "window position t = %d outside [0, %d)", t, d->window);
+  const bool any = d->n_req > 0;
+  CHECK(check_comp(d, m, any, tok_idx, tok_val));
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(window_buf, "window_buf", any));
+  CHECK(check_ptr(q, "q", any));
+  CHECK(check_ptr(k, "k", any));
+  CHECK(check_ptr(v, "v", any));
+  CHECK(check_ptr(a, "a", any));
+  CHECK(check_ptr(b, "b", any));
+  CHECK(check_ptr(o, "o", any));
+  return hip_status(qdr::launch_window(pool_of(d, meta, g), d->gate, d->window, t,
+                                       static_cast<uint8_t*>(packed), row_scale, col_scale,
+                                       static_cast<uint8_t*>(window_buf), q, k, v, a, b, o, m,
+                                       tok_idx, tok_val, static_cast<hipStream_t>(stream)),
+                    "qdr_comp_window: launch");
 }
 
 int qdr_comp_dequantize(const qdr_desc* d, const void* meta, const void* packed,

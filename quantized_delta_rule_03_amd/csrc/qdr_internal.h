@@ -79,7 +79,8 @@ hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, floa
 // One window token (and, at t = W-1, the fold and requantization).
 hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed, float* rs,
                          float* cs, uint8_t* buf, const float* q, const float* k, const float* v,
-                         const float* a, const float* b, float* o, hipStream_t s);
+                         const float* a, const float* b, float* o, int m, uint16_t* tok_idx,
+                         float* tok_val, hipStream_t s);
 
 // T tokens of every unit in one call; token-major inputs [T][unit][...].
 // m > 0: compensator tokens tok_idx / tok_val [n_unit][m] (read at the start, rewritten

@@ -1108,6 +1108,10 @@ struct WinArgs {
   const float* a;
   const float* b;
   float* o;
+  // compensator tokens (m = 0: none): [n_unit][m], flat index i * 128 + j (logical j)
+  int m;
+  uint16_t* tok_idx;
+  float* tok_val;
 };
 
 __device__ __forceinline__ float* win_kt(const WinArgs& A, int u) {
@@ -1124,6 +1128,8 @@ struct WinLds {
   float al[kWinMax], be[kWinMax];
   float sp[2][2][kD];  // row sums over buffered tokens: [alpha|beta][token parity][row]
   float xs[kD];        // S0 (g_t k_t) per row
+  uint32_t tk_idx[64];  // the unit's compensator tokens
+  float tk_val[64];
 };
 
 // Unit u's addressing from the metadata (scalar reads).
@@ -1182,6 +1188,10 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
     L.vin.R[p] = A.Rs[uo + p];
     L.vin.C[tid] = A.Cs[uo + tid];
     if (tid == 0) L.vin.b = A.b[u];
+  }
+  if (tid < A.m) {
+    L.tk_idx[tid] = A.tok_idx[(size_t)u * A.m + tid];
+    L.tk_val[tid] = A.tok_val[(size_t)u * A.m + tid];
   }
   __syncthreads();
   if (tid < kD) L.qp[tid] = L.vin.q[L.vin.perm[tid]];
@@ -1285,14 +1295,26 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   }
   __syncthreads();
 
-  // 5. delta, readout, append
+  // 5. delta, readout, append. The compensator tokens are entries of S0: token x at
+  //    (i, j) adds x g_t,j k_t,j to the prediction and x g_t,j q_t,j to the readout of row i.
   if (tid < kD) {
     const int i = tid;
-    const float pred = L.xs[i] + (L.sp[0][0][i] + L.sp[0][1][i]);
+    float tu = 0.0f;
+    double to = 0.0;
+    for (int c = 0; c < A.m; ++c) {
+      const uint32_t ix = L.tk_idx[c];
+      if ((int)(ix >> 7) == i) {
+        const int j = (int)(ix & (kD - 1));
+        const float gx = L.tk_val[c] * L.vin.a[j];
+        tu = fmaf(gx, L.vin.k[j], tu);
+        to = fma((double)gx, (double)L.vin.q[j], to);
+      }
+    }
+    const float pred = (L.xs[i] + tu) + (L.sp[0][0][i] + L.sp[0][1][i]);
     const float wt = L.vin.b * (L.vin.v[i] - pred);
     const double kq = ((L.W.kq[0] + L.W.kq[1]) + L.W.kq[2]) + L.W.kq[3];
     A.o[uo + i] = (float)(fma((double)L.W.rf[i], L.W.osum[i],
-                              (double)(L.sp[1][0][i] + L.sp[1][1][i])) + (double)wt * kq);
+                              (double)(L.sp[1][0][i] + L.sp[1][1][i]) + to) + (double)wt * kq);
     Wv[(size_t)t * kD + i] = wt;
     Kt[(size_t)t * kD + i] = L.W.kp[i];
     gbuf[i] = L.gt[i];
@@ -1309,6 +1331,278 @@ __device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// Compensator tokens (LeapQuant abstract: the largest outliers kept as a few
+// high-precision tokens that share the real tokens' update path): the m nonzero entries
+// of largest |S| (equal magnitudes: smaller flat index i * 128 + j, j logical) are
+// written out largest first and set to 0 before the refit. Candidates are the entries at
+// or above T0, the m-th largest of the 64 lane-quad maxima (m <= 16) or of the 256
+// per-thread maxima (so at least m entries reach it); up to kCandCap of them are ranked
+// in LDS. More candidates (many equal magnitudes) take an exact bisection over the
+// magnitude bits and then over the flat index.
+constexpr int kCandCap = 1024;
+constexpr int kTokMax = kCompMax;
+constexpr uint32_t kTokEmpty = 0xFFFFu;
+struct CompLds {
+  uint2 cand[kCandCap];  // (value bits, flat index)
+  uint32_t qm[kThreads];  // lane-quad (or per-thread) maxima of the magnitude bits
+  uint2 tok[kTokMax];
+  uint32_t n, T0;
+  uint32_t part[2][4];
+};
+
+// sum over the work-group (one barrier; `r` alternates the partial slots)
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t x, uint32_t (*part)[4], int r) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  if ((threadIdx.x & 63) == 0) part[r & 1][threadIdx.x >> 6] = x;
+  block_sync();
+  return part[r & 1][0] + part[r & 1][1] + part[r & 1][2] + part[r & 1][3];
+}
+
+// Register layouts of a unit's state over the 256 threads (64 entries each): the value row
+// and key position of entry x of thread (wave w, lane rg + 16 jg), and the thread and
+// entry that hold (row i, position p).
+// The thread's distinct positions come in NW runs of four (jbase: the first of run k,
+// jword: the run of entry x).
+struct ChunkLayout {  // rows 32w + 16h + rg, positions 32s + 8jg + e; x = 32h + 8s + e
+  static constexpr int NW = 8;
+  __device__ static int row(int x, int w, int rg) { return 32 * w + 16 * (x >> 5) + rg; }
+  __device__ static int jbase(int k, int w, int jg) { return 32 * (k >> 1) + 8 * jg + 4 * (k & 1); }
+  __device__ static int jword(int x) { return 2 * ((x >> 3) & 3) + ((x >> 2) & 1); }
+  __device__ static int owner(int i, int p) { return (i >> 5) * 64 + (i & 15) + 16 * ((p >> 3) & 3); }
+  __device__ static int slot(int i, int p) { return ((i >> 4) & 1) * 32 + (p >> 5) * 8 + (p & 7); }
+};
+struct FoldLayout {  // rows rg + 16rr, positions 32w + 8jg + e; x = 8rr + e
+  static constexpr int NW = 2;
+  __device__ static int row(int x, int w, int rg) { return rg + 16 * (x >> 3); }
+  __device__ static int jbase(int k, int w, int jg) { return 32 * w + 8 * jg + 4 * k; }
+  __device__ static int jword(int x) { return (x >> 2) & 1; }
+  __device__ static int owner(int i, int p) { return (p >> 5) * 64 + 16 * ((p >> 3) & 3) + (i & 15); }
+  __device__ static int slot(int i, int p) { return (i >> 4) * 8 + (p & 7); }
+};
+
+// The compensator tokens rejoin the register state: each token is placed by one thread
+// (its owner and entry through the inverse key permutation; times gfac[p] when given,
+// the gate product that the token's entry has taken since it was stored), then every
+// thread adds those it owns. Their residual entries dequantize to 0. jinv must be
+// visible to all threads on entry.
+template <class LAYOUT>
+__device__ __forceinline__ void comp_scatter(float (&S)[64], int m, const uint16_t* tok_idx,
+                                             const float* tok_val, const float* gfac,
+                                             uint32_t* tok_at, float* tok_v, const uint8_t* jinv) {
+  const int tid = threadIdx.x;
+  const int m4 = (m + 3) & ~3;
+  if (tid < m4) {
+    uint32_t at = 0xFFFFFFFFu;
+    float val = 0.0f;
+    if (tid < m) {
+      const uint32_t ix = tok_idx[tid];
+      if (ix < (uint32_t)(kD * kD)) {
+        const int i = (int)(ix >> 7), p = jinv[ix & (kD - 1)];
+        at = (uint32_t)LAYOUT::owner(i, p) << 8 | (uint32_t)LAYOUT::slot(i, p);
+        val = gfac ? tok_val[tid] * gfac[p] : tok_val[tid];
+      }
+    }
+    tok_at[tid] = at;
+    tok_v[tid] = val;
+  }
+  block_sync();
+  for (int t = 0; t < m4; t += 4) {
+    const uint4 at4 = *reinterpret_cast<const uint4*>(&tok_at[t]);
+    const uint32_t ats[4] = {at4.x, at4.y, at4.z, at4.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if ((ats[c] >> 8) == (uint32_t)tid) {
+        const float val = tok_v[t + c];
+        const int sl = (int)(ats[c] & 63u);
+#pragma unroll
+        for (int x = 0; x < 64; ++x)
+          if (x == sl) S[x] += val;
+      }
+    }
+  }
+}
+
+// Selection of the new tokens from the register state (see above); writes tok_idx /
+// tok_val [m] of the unit and zeroes the selected entries. jperm must be visible to all
+// threads on entry; C is scratch that no thread uses until this returns.
+template <class LAYOUT>
+__device__ __forceinline__ void comp_select(float (&S)[64], int m_, uint16_t* tok_idx,
+                                            float* tok_val, CompLds& C, const uint8_t* jperm) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rg = lane & 15, jg = lane >> 4;
+  const uint32_t m = (uint32_t)m_;
+  // logical key channels of the thread's positions, four per word
+  uint32_t jp[LAYOUT::NW];
+#pragma unroll
+  for (int k = 0; k < LAYOUT::NW; ++k)
+    jp[k] = *reinterpret_cast<const uint32_t*>(&jperm[LAYOUT::jbase(k, w, jg)]);
+  auto key = [&](int x) { return __float_as_uint(S[x]) & 0x7FFFFFFFu; };
+  auto flat = [&](int x) {
+    return (uint32_t)(LAYOUT::row(x, w, rg) * kD) + ((jp[LAYOUT::jword(x)] >> (8 * (x & 3))) & 0xFFu);
+  };
+  uint32_t tmax = 0;
+#pragma unroll
+  for (int x = 0; x < 64; ++x) tmax = max(tmax, key(x));
+  const bool quads = m <= 16;
+  if (quads) {
+    tmax = max(tmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tmax, 0xB1, 0xF, 0xF, false));
+    tmax = max(tmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tmax, 0x4E, 0xF, 0xF, false));
+    if ((lane & 3) == 0) C.qm[tid >> 2] = tmax;
+  } else {
+    C.qm[tid] = tmax;
+  }
+  if (tid == 0) {
+    C.n = 0;
+    C.T0 = 0;
+  }
+  block_sync();
+  // T0: the largest maximum that at least m of the maxima reach
+  if (quads) {
+    if (w == 0) {
+      const uint32_t x = C.qm[lane];
+      uint32_t ge = 0;
+#pragma unroll 16
+      for (int j = 0; j < 64; ++j)
+        ge += (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)x, j) >= x);
+      const uint32_t t0 = wave_max_u32(ge >= m ? x : 0u);
+      if (lane == 0) C.T0 = t0;
+    }
+  } else {
+    // wave w counts for the maxima 64 w + lane against all 256
+    const uint32_t x = C.qm[tid];
+    const uint32_t y0 = C.qm[lane], y1 = C.qm[64 + lane], y2 = C.qm[128 + lane],
+                   y3 = C.qm[192 + lane];
+    uint32_t ge = 0;
+#pragma unroll 16
+    for (int j = 0; j < 64; ++j)
+      ge += (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y0, j) >= x) +
+            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y1, j) >= x) +
+            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y2, j) >= x) +
+            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y3, j) >= x);
+    const uint32_t t0 = wave_max_u32(ge >= m ? x : 0u);
+    if (lane == 0) atomicMax(&C.T0, t0);
+  }
+  block_sync();
+  // candidates: |S| >= T0 and nonzero (T0 raised to the smallest positive magnitude).
+  // The wave counts its candidates, takes one range of slots, then writes them in order.
+  const float T0f = __uint_as_float(max(C.T0, 1u));
+  {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int x = 0; x < 64; ++x)
+      cnt += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(fabsf(S[x]) >= T0f));
+    uint32_t base = 0;
+    if (lane == 0 && cnt) base = atomicAdd(&C.n, cnt);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+    for (int x = 0; x < 64; ++x) {
+      const bool c = fabsf(S[x]) >= T0f;
+      const uint64_t mk = __builtin_amdgcn_ballot_w64(c);
+      if (mk) {
+        const uint32_t slot =
+            base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+        if (c && slot < (uint32_t)kCandCap)
+          C.cand[slot] = make_uint2(__float_as_uint(S[x]), flat(x));
+        base += (uint32_t)__builtin_popcountll(mk);
+      }
+    }
+  }
+  block_sync();
+  uint32_t n = C.n;
+  if (n > (uint32_t)kCandCap) {
+    // the m-th largest magnitude T (n > kCandCap >= m nonzero entries exist), then the
+    // flat-index cut among the entries of magnitude T
+    int r = 0;
+    uint32_t T = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int x = 0; x < 64; ++x) cnt += (uint32_t)(key(x) >= c);
+      if (block_sum_u32(cnt, C.part, r++) >= m) T = c;
+    }
+    uint32_t gt = 0;
+#pragma unroll
+    for (int x = 0; x < 64; ++x) gt += (uint32_t)(key(x) > T);
+    const uint32_t need = m - block_sum_u32(gt, C.part, r++);
+    uint32_t lo = 0, hi = kD * kD - 1;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int x = 0; x < 64; ++x) cnt += (uint32_t)(key(x) == T && flat(x) <= mid);
+      if (block_sum_u32(cnt, C.part, r++) >= need) hi = mid;
+      else lo = mid + 1;
+    }
+    if (tid == 0) C.n = 0;
+    block_sync();
+#pragma unroll
+    for (int x = 0; x < 64; ++x) {
+      const uint32_t kk = key(x);
+      if (kk >= T && (kk > T || flat(x) <= lo)) {
+        const uint32_t slot = atomicAdd(&C.n, 1u);
+        C.cand[slot] = make_uint2(__float_as_uint(S[x]), flat(x));
+      }
+    }
+    block_sync();
+    n = C.n;  // == m
+  }
+  // rank the candidates; the first m are the tokens, in order. G threads (adjacent lanes)
+  // share a candidate, each scanning every G-th entry of the list; the list is padded to a
+  // multiple of 8 G with zero keys, which rank below every candidate.
+  uint32_t G = 1;
+  while (G < 64 && 2 * G * n <= (uint32_t)kThreads) G *= 2;
+  const uint32_t nP = (n + 8 * G - 1) / (8 * G) * (8 * G);
+  for (uint32_t x = n + tid; x < nP; x += kThreads) C.cand[x] = make_uint2(0u, 0xFFFFFFFFu);
+  block_sync();
+  const uint32_t part = (uint32_t)tid & (G - 1);
+  for (uint32_t c0 = 0; c0 < n; c0 += kThreads / G) {
+    const uint32_t c = c0 + (uint32_t)tid / G;
+    uint2 me = make_uint2(0u, 0u);
+    uint32_t rk = 0;
+    if (c < n) {
+      me = C.cand[c];
+      const uint32_t km = me.x & 0x7FFFFFFFu;
+      for (uint32_t d = part; d < nP; d += 8 * G) {
+        uint2 ot[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) ot[x] = C.cand[d + x * G];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const uint32_t ko = ot[x].x & 0x7FFFFFFFu;
+          rk += (uint32_t)(ko > km || (ko == km && ot[x].y < me.y));
+        }
+      }
+    }
+    for (uint32_t o = 1; o < G; o <<= 1) rk += __shfl_xor(rk, (int)o);
+    if (c < n && part == 0 && rk < m) C.tok[rk] = me;
+  }
+  block_sync();
+  const uint32_t nv = min(n, m);
+  if ((uint32_t)tid < m) {
+    const bool valid = (uint32_t)tid < nv;
+    tok_idx[tid] = valid ? (uint16_t)C.tok[tid].y : (uint16_t)kTokEmpty;
+    tok_val[tid] = valid ? __uint_as_float(C.tok[tid].x) : 0.0f;
+  }
+  if (nv > 0) {
+    // the selected entries: above the last token's magnitude, or equal to it at a flat
+    // index up to the last token's
+    const uint2 last = C.tok[nv - 1];
+    const uint32_t kl = last.x & 0x7FFFFFFFu;
+    const float klf = __uint_as_float(kl);
+#pragma unroll
+    for (int x = 0; x < 64; ++x) {
+      const bool c = fabsf(S[x]) >= klf;
+      if (__builtin_amdgcn_ballot_w64(c)) {
+        const uint32_t kk = key(x);
+        if (c && (kk > kl || flat(x) <= last.y)) S[x] = 0.0f;
+      }
+    }
+  }
+  block_sync();  // the scratch is reused by the refit
+}
+
 constexpr int kFoldChunk = 32;  // buffered tokens per staged chunk (one MFMA k-step)
 
 struct FoldLds {
@@ -1317,10 +1611,16 @@ struct FoldLds {
   float invA[kD];
   float invc[kD];
   float cpart[16 * kFS];
+  alignas(16) uint8_t jperm[kD];  // physical position -> logical key channel
+  uint8_t jinv[kD];               // logical key channel -> physical position
+  uint32_t tok_at[64];            // compensator token t: owning thread << 8 | register slot
+  float tok_v[64];
 };
+static_assert(sizeof(CompLds) <= sizeof(FoldLds::kt), "selection scratch fits");
 
 // Fold the window into the state and requantize: S = S0 diag(g) + sum_i w_i Kt_i^T.
-template <int GATE>
+// COMP: with compensator tokens (A.m > 0).
+template <int GATE, bool COMP>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 k_window_fold(WinArgs A) {
   __shared__ __attribute__((aligned(16))) FoldLds L;
@@ -1336,6 +1636,11 @@ k_window_fold(WinArgs A) {
   const float* Wv = Kt + (size_t)W * kD;
   const float* gbuf = Wv + (size_t)W * kD;
   const int p0 = 32 * w + 8 * jg;
+  if (COMP && tid < kD) {
+    const int j = meta_heads(A.meta)[cur.h].perm[tid];
+    L.jperm[tid] = (uint8_t)j;
+    L.jinv[j] = (uint8_t)tid;
+  }
 
   // sum_i w_i Kt_i^T on the matrix cores. Output tile (b, rr): rows rg + 16 rr, positions
   // p0 + 4b + (0..3) of this lane; A = Kt^T (16 positions x 32 tokens), B = Wv (32 tokens
@@ -1411,6 +1716,15 @@ k_window_fold(WinArgs A) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) s[rr][m] = (f[m] - bias) * (cf[m] * c) + d[m >> 2][rr][m & 3];
     }
+  }
+  // compensator tokens: the stored ones rejoin S0 (decayed by the window's gate product),
+  // then the new ones are selected from S and leave it before the refit
+  if (COMP) {
+    float(&sf)[64] = *reinterpret_cast<float(*)[64]>(&s[0][0]);
+    uint16_t* ti = A.tok_idx + (size_t)u * A.m;
+    float* tv = A.tok_val + (size_t)u * A.m;
+    comp_scatter<FoldLayout>(sf, A.m, ti, tv, gbuf, L.tok_at, L.tok_v, L.jinv);
+    comp_select<FoldLayout>(sf, A.m, ti, tv, *reinterpret_cast<CompLds*>(&L.kt[0][0]), L.jperm);
   }
 
   // refit + requantize (the decode step's rule)
@@ -1512,6 +1826,7 @@ struct ChunkX {
 };
 static_assert(4 * sizeof(ChunkPriv) <= sizeof(ChunkLds::kpl), "private Grams fit");
 static_assert(4 * sizeof(ChunkX) <= sizeof(ChunkLds::kmi), "private deltas fit");
+static_assert(sizeof(CompLds) <= sizeof(ChunkLds::qpl), "selection scratch fits");
 
 // One thread's share of a sub-block's inputs, loaded one sub-block ahead: tokens
 // 8 (tid >> 7) + n at key position tid & 127 (k, q, a) and the value entries of its
@@ -1547,249 +1862,6 @@ __device__ __forceinline__ void requant_row(uint8_t* seg, int row, int jg, const
 __device__ __forceinline__ void wave_sync_lds() {
   wait_lgkm();
   __builtin_amdgcn_wave_barrier();
-}
-
-// Compensator tokens (LeapQuant abstract: the largest outliers kept as a few
-// high-precision tokens that share the real tokens' update path): the m nonzero entries
-// of largest |S| (equal magnitudes: smaller flat index i * 128 + j, j logical) are
-// written out largest first and set to 0 before the refit. Candidates are the entries at
-// or above T0, the m-th largest of the 64 lane-quad maxima (m <= 16) or of the 256
-// per-thread maxima (so at least m entries reach it); up to kCandCap of them are ranked
-// in LDS. More candidates (many equal magnitudes) take an exact bisection over the
-// magnitude bits and then over the flat index.
-constexpr int kCandCap = 1024;
-constexpr int kTokMax = kCompMax;
-constexpr uint32_t kTokEmpty = 0xFFFFu;
-struct CompLds {
-  uint2 cand[kCandCap];  // (value bits, flat index)
-  uint32_t qm[kThreads];  // lane-quad (or per-thread) maxima of the magnitude bits
-  uint2 tok[kTokMax];
-  uint32_t n, T0;
-  uint32_t part[2][4];
-};
-static_assert(sizeof(CompLds) <= sizeof(ChunkLds::qpl), "selection scratch fits");
-
-// sum over the work-group (one barrier; `r` alternates the partial slots)
-__device__ __forceinline__ uint32_t block_sum_u32(uint32_t x, uint32_t (*part)[4], int r) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  if ((threadIdx.x & 63) == 0) part[r & 1][threadIdx.x >> 6] = x;
-  block_sync();
-  return part[r & 1][0] + part[r & 1][1] + part[r & 1][2] + part[r & 1][3];
-}
-
-__device__ __forceinline__ void comp_select_chunk(float (&S)[2][4][8], const ChunkArgs& A,
-                                                  ChunkLds& L, int u) {
-  CompLds& C = *reinterpret_cast<CompLds*>(&L.qpl[0][0][0]);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rg = lane & 15, jg = lane >> 4;
-  const uint32_t m = (uint32_t)A.m;
-  // logical key channels of this thread's 32 positions, four per word
-  uint32_t jp[8];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint2 x = *reinterpret_cast<const uint2*>(&L.jperm[32 * s + 8 * jg]);
-    jp[2 * s] = x.x;
-    jp[2 * s + 1] = x.y;
-  }
-  auto key = [&](int h, int s, int e) { return __float_as_uint(S[h][s][e]) & 0x7FFFFFFFu; };
-  auto flat = [&](int h, int s, int e) {
-    return (uint32_t)((32 * w + 16 * h + rg) * kD) + ((jp[2 * s + (e >> 2)] >> (8 * (e & 3))) & 0xFFu);
-  };
-  uint32_t tmax = 0;
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tmax = max(tmax, key(h, s, e));
-  const bool quads = m <= 16;
-  if (quads) {
-    tmax = max(tmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tmax, 0xB1, 0xF, 0xF, false));
-    tmax = max(tmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)tmax, 0x4E, 0xF, 0xF, false));
-    if ((lane & 3) == 0) C.qm[tid >> 2] = tmax;
-  } else {
-    C.qm[tid] = tmax;
-  }
-  if (tid == 0) {
-    C.n = 0;
-    C.T0 = 0;
-  }
-  block_sync();
-  // T0: the largest maximum that at least m of the maxima reach
-  if (quads) {
-    if (w == 0) {
-      const uint32_t x = C.qm[lane];
-      uint32_t ge = 0;
-#pragma unroll 16
-      for (int j = 0; j < 64; ++j)
-        ge += (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)x, j) >= x);
-      const uint32_t t0 = wave_max_u32(ge >= m ? x : 0u);
-      if (lane == 0) C.T0 = t0;
-    }
-  } else {
-    // wave w counts for the maxima 64 w + lane against all 256
-    const uint32_t x = C.qm[tid];
-    const uint32_t y0 = C.qm[lane], y1 = C.qm[64 + lane], y2 = C.qm[128 + lane],
-                   y3 = C.qm[192 + lane];
-    uint32_t ge = 0;
-#pragma unroll 16
-    for (int j = 0; j < 64; ++j)
-      ge += (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y0, j) >= x) +
-            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y1, j) >= x) +
-            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y2, j) >= x) +
-            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y3, j) >= x);
-    const uint32_t t0 = wave_max_u32(ge >= m ? x : 0u);
-    if (lane == 0) atomicMax(&C.T0, t0);
-  }
-  block_sync();
-  // candidates: |S| >= T0 and nonzero (T0 raised to the smallest positive magnitude).
-  // The wave counts its candidates, takes one range of slots, then writes them in order.
-  const float T0f = __uint_as_float(max(C.T0, 1u));
-  {
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          cnt += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(fabsf(S[h][s][e]) >= T0f));
-    uint32_t base = 0;
-    if (lane == 0 && cnt) base = atomicAdd(&C.n, cnt);
-    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool c = fabsf(S[h][s][e]) >= T0f;
-          const uint64_t mk = __builtin_amdgcn_ballot_w64(c);
-          if (mk) {
-            const uint32_t slot =
-                base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
-                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-            if (c && slot < (uint32_t)kCandCap)
-              C.cand[slot] = make_uint2(__float_as_uint(S[h][s][e]), flat(h, s, e));
-            base += (uint32_t)__builtin_popcountll(mk);
-          }
-        }
-  }
-  block_sync();
-  uint32_t n = C.n;
-  if (n > (uint32_t)kCandCap) {
-    // the m-th largest magnitude T (n > kCandCap >= m nonzero entries exist), then the
-    // flat-index cut among the entries of magnitude T
-    int r = 0;
-    uint32_t T = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) cnt += (uint32_t)(key(h, s, e) >= c);
-      if (block_sum_u32(cnt, C.part, r++) >= m) T = c;
-    }
-    uint32_t gt = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gt += (uint32_t)(key(h, s, e) > T);
-    const uint32_t need = m - block_sum_u32(gt, C.part, r++);
-    uint32_t lo = 0, hi = kD * kD - 1;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            cnt += (uint32_t)(key(h, s, e) == T && flat(h, s, e) <= mid);
-      if (block_sum_u32(cnt, C.part, r++) >= need) hi = mid;
-      else lo = mid + 1;
-    }
-    if (tid == 0) C.n = 0;
-    block_sync();
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t kk = key(h, s, e);
-          if (kk >= T && (kk > T || flat(h, s, e) <= lo)) {
-            const uint32_t slot = atomicAdd(&C.n, 1u);
-            C.cand[slot] = make_uint2(__float_as_uint(S[h][s][e]), flat(h, s, e));
-          }
-        }
-    block_sync();
-    n = C.n;  // == m
-  }
-  // rank the candidates; the first m are the tokens, in order. G threads (adjacent lanes)
-  // share a candidate, each scanning every G-th entry of the list; the list is padded to a
-  // multiple of 8 G with zero keys, which rank below every candidate.
-  uint32_t G = 1;
-  while (G < 64 && 2 * G * n <= (uint32_t)kThreads) G *= 2;
-  const uint32_t nP = (n + 8 * G - 1) / (8 * G) * (8 * G);
-  for (uint32_t x = n + tid; x < nP; x += kThreads) C.cand[x] = make_uint2(0u, 0xFFFFFFFFu);
-  block_sync();
-  const uint32_t part = (uint32_t)tid & (G - 1);
-  for (uint32_t c0 = 0; c0 < n; c0 += kThreads / G) {
-    const uint32_t c = c0 + (uint32_t)tid / G;
-    uint2 me = make_uint2(0u, 0u);
-    uint32_t rk = 0;
-    if (c < n) {
-      me = C.cand[c];
-      const uint32_t km = me.x & 0x7FFFFFFFu;
-      for (uint32_t d = part; d < nP; d += 8 * G) {
-        uint2 ot[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) ot[x] = C.cand[d + x * G];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const uint32_t ko = ot[x].x & 0x7FFFFFFFu;
-          rk += (uint32_t)(ko > km || (ko == km && ot[x].y < me.y));
-        }
-      }
-    }
-    for (uint32_t o = 1; o < G; o <<= 1) rk += __shfl_xor(rk, (int)o);
-    if (c < n && part == 0 && rk < m) C.tok[rk] = me;
-  }
-  block_sync();
-  const uint32_t nv = min(n, m);
-  if ((uint32_t)tid < m) {
-    const size_t o = (size_t)u * m + tid;
-    const bool valid = (uint32_t)tid < nv;
-    A.tok_idx[o] = valid ? (uint16_t)C.tok[tid].y : (uint16_t)kTokEmpty;
-    A.tok_val[o] = valid ? __uint_as_float(C.tok[tid].x) : 0.0f;
-  }
-  if (nv > 0) {
-    // the selected entries: above the last token's magnitude, or equal to it at a flat
-    // index up to the last token's
-    const uint2 last = C.tok[nv - 1];
-    const uint32_t kl = last.x & 0x7FFFFFFFu;
-    const float klf = __uint_as_float(kl);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool c = fabsf(S[h][s][e]) >= klf;
-          if (__builtin_amdgcn_ballot_w64(c)) {
-            const uint32_t kk = key(h, s, e);
-            if (c && (kk > kl || flat(h, s, e) <= last.y)) S[h][s][e] = 0.0f;
-          }
-        }
-  }
-  block_sync();  // the scratch is reused by the refit
 }
 
 template <int GATE>
@@ -1842,46 +1914,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       for (int e = 0; e < 8; ++e) S[h][s][e] = (f[e] - bias) * (R[e] * c);
     }
   }
-  // the compensator tokens rejoin the state (their residual entries dequantize to 0):
-  // each token is placed by one thread, then every thread adds those it owns
+  // the compensator tokens rejoin the state
   if (A.m > 0) {
     block_sync();  // jinv
-    const int m4 = (A.m + 3) & ~3;
-    if (tid < m4) {
-      uint32_t at = 0xFFFFFFFFu;
-      float val = 0.0f;
-      if (tid < A.m) {
-        const uint32_t ix = A.tok_idx[(size_t)u * A.m + tid];
-        if (ix < (uint32_t)(kD * kD)) {
-          const int i = (int)(ix >> 7), p = L.jinv[ix & (kD - 1)];
-          const uint32_t owner = (uint32_t)((i >> 5) * 64 + (i & 15) + 16 * ((p >> 3) & 3));
-          const uint32_t slot = (uint32_t)(((i >> 4) & 1) * 32 + (p >> 5) * 8 + (p & 7));
-          at = owner << 8 | slot;
-          val = A.tok_val[(size_t)u * A.m + tid];
-        }
-      }
-      L.tok_at[tid] = at;
-      L.tok_v[tid] = val;
-    }
-    block_sync();
-    for (int t = 0; t < m4; t += 4) {
-      const uint4 at4 = *reinterpret_cast<const uint4*>(&L.tok_at[t]);
-      const uint32_t ats[4] = {at4.x, at4.y, at4.z, at4.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if ((ats[c] >> 8) == (uint32_t)tid) {
-          const float val = L.tok_v[t + c];
-          const int slot = (int)(ats[c] & 63u);
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (32 * h + 8 * s + e == slot) S[h][s][e] += val;
-        }
-      }
-    }
+    comp_scatter<ChunkLayout>(*reinterpret_cast<float(*)[64]>(&S[0][0][0]), A.m,
+                              A.tok_idx + (size_t)u * A.m, A.tok_val + (size_t)u * A.m, nullptr,
+                              L.tok_at, L.tok_v, L.jinv);
   }
   }
   const int pl = tid & (kD - 1), half = tid >> 7;
@@ -2184,7 +2222,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   }
   block_sync();
 
-  if (A.m > 0) comp_select_chunk(S, A, L, u);
+  if (A.m > 0)
+    comp_select<ChunkLayout>(*reinterpret_cast<float(*)[64]>(&S[0][0][0]), A.m,
+                             A.tok_idx + (size_t)u * A.m, A.tok_val + (size_t)u * A.m,
+                             *reinterpret_cast<CompLds*>(&L.qpl[0][0][0]), L.jperm);
 
   // refit + requantize (the decode step's rule). Key-row absmax: the lane's two rows, the
   // 16 lanes of its DPP row (same positions), then the four waves.
@@ -2336,15 +2377,23 @@ hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, floa
 
 hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed, float* rs,
                          float* cs, uint8_t* buf, const float* q, const float* k, const float* v,
-                         const float* a, const float* b, float* o, hipStream_t s) {
+                         const float* a, const float* b, float* o, int m, uint16_t* tok_idx,
+                         float* tok_val, hipStream_t s) {
   if (p.n_unit == 0) return hipSuccess;
-  WinArgs A{p.meta, p.n_head, W, t, p.req_bytes, packed, rs, cs, buf, q, k, v, a, b, o};
+  WinArgs A{p.meta, p.n_head, W, t, p.req_bytes, packed, rs, cs, buf, q, k, v, a, b, o,
+            m, tok_idx, tok_val};
   if (gate == GDN) {
     hipLaunchKernelGGL(k_window_token<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
-    if (t == W - 1) hipLaunchKernelGGL(k_window_fold<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    if (t == W - 1) {
+      if (m > 0) hipLaunchKernelGGL((k_window_fold<GDN, true>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
+      else hipLaunchKernelGGL((k_window_fold<GDN, false>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    }
   } else {
     hipLaunchKernelGGL(k_window_token<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
-    if (t == W - 1) hipLaunchKernelGGL(k_window_fold<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    if (t == W - 1) {
+      if (m > 0) hipLaunchKernelGGL((k_window_fold<KDA, true>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
+      else hipLaunchKernelGGL((k_window_fold<KDA, false>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    }
   }
   return hipGetLastError();
 }

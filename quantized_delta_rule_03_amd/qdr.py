@@ -29,7 +29,8 @@ RULE_STEP, RULE_KEYROW, RULE_TENSOR = 0, 1, 2  # scale rules (QDR_RULE_*)
 SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize_state",
            "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk", "qdr_dequantize_state",
            "qdr_damp_select", "qdr_damp_bytes", "qdr_damp_init", "qdr_damp_quantize", "qdr_damp_step",
-           "qdr_damp_dequantize", "qdr_comp_quantize", "qdr_comp_chunk", "qdr_comp_dequantize",
+           "qdr_damp_dequantize", "qdr_comp_quantize", "qdr_comp_chunk", "qdr_comp_window",
+           "qdr_comp_dequantize",
            "qdr_last_error")
 
 
@@ -83,6 +84,7 @@ def lib():
             "qdr_dequantize_state": [D, P, P, P, P, P, P],
             "qdr_comp_quantize": [D, P, P, P, P, i32, P, P, P, P],
             "qdr_comp_chunk": [D, P, P, P, P, i32, P, P, i32, P, P, P, P, P, P, P],
+            "qdr_comp_window": [D, P, P, P, P, i32, P, P, P, i32, P, P, P, P, P, P, P],
             "qdr_comp_dequantize": [D, P, P, P, P, i32, P, P, P, P],
         }
         for name, args in sigs.items():
@@ -217,6 +219,14 @@ def comp_chunk(L: Layout, meta, packed, row_scale, col_scale, m, tok_idx, tok_va
                                 _stream(stream)), "qdr_comp_chunk")
 
 
+def comp_window(L: Layout, meta, packed, row_scale, col_scale, m, tok_idx, tok_val, window_buf,
+                t, q, k, v, a, b, o, stream=None):
+    _check(lib().qdr_comp_window(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                 _ptr(col_scale), int(m), _ptr(tok_idx), _ptr(tok_val),
+                                 _ptr(window_buf), int(t), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                 _ptr(b), _ptr(o), _stream(stream)), "qdr_comp_window")
+
+
 def comp_dequantize(L: Layout, meta, packed, row_scale, col_scale, m, tok_idx, tok_val, S_out,
                     stream=None):
     _check(lib().qdr_comp_dequantize(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
@@ -303,6 +313,10 @@ class StatePool:
     def comp_chunk(self, q, k, v, a, b, o, stream=None):
         comp_chunk(self.layout, self.meta, self.packed, self.row_scale, self.col_scale, self.m,
                    self.tok_idx, self.tok_val, int(b.shape[0]), q, k, v, a, b, o, stream)
+
+    def comp_window_token(self, t, q, k, v, a, b, o, stream=None):
+        comp_window(self.layout, self.meta, self.packed, self.row_scale, self.col_scale, self.m,
+                    self.tok_idx, self.tok_val, self.window_buf, t, q, k, v, a, b, o, stream)
 
     def comp_dequantize(self, S_out=None, stream=None):
         import torch

@@ -157,6 +157,14 @@ def test_comp_validation():
     d, keep = _desc(rule=qdr.RULE_KEYROW)
     rc = L.qdr_comp_quantize(ctypes.byref(d), P, P, P, P, 4, P, P, P, None)
     assert rc == qdr.QDR_EUNSUPPORTED and "QDR_RULE_STEP" in qdr.last_error()
+    d, keep = _desc(window=8)
+    rc = L.qdr_comp_window(ctypes.byref(d), P, P, P, P, 4, P, P, P, 8, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED and "t = 8" in qdr.last_error()
+    rc = L.qdr_comp_window(ctypes.byref(d), P, P, P, P, 4, None, P, P, 0, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EINVAL and "tok_idx is NULL" in qdr.last_error()
+    d, keep = _desc()
+    rc = L.qdr_comp_window(ctypes.byref(d), P, P, P, P, 4, P, P, P, 0, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED and "no window mode" in qdr.last_error()
     # nothing to do: zero requests or T = 0 with no buffers at all
     d, keep = _desc(n_req=0)
     assert L.qdr_comp_quantize(ctypes.byref(d), P, None, None, None, 4, None, None, None,

@@ -1,12 +1,12 @@
 """GPU parity of the compensator tokens (qdr_comp_quantize / qdr_comp_chunk /
-qdr_comp_dequantize) against the oracle.
+qdr_comp_window / qdr_comp_dequantize) against the oracle.
 
 Quantize and dequantize take the same fp32 inputs on both sides, so they are compared
 bit for bit (packed codes, scales, token indices and values), including the cases that
 drive the kernel's two selection paths: few candidates ranked in LDS, and many equal
-magnitudes (a constant-magnitude state) that take the exact bisection. A chunk runs the
-fp32 chunk arithmetic on the GPU and the fp64 window recurrence in the oracle, so it is
-compared teacher-forced at the chunk bar: readouts rel-L2 <= 1e-4; the same token set
+magnitudes (a constant-magnitude state) that take the exact bisection. A chunk (or a
+window of per-token calls) runs fp32 arithmetic on the GPU and the fp64 window recurrence
+in the oracle, so it is compared teacher-forced at the chunk and window bar: readouts rel-L2 <= 1e-4; the same token set
 (or, at a near-tie of magnitudes, differences only among entries within 1e-5 of the cut)
 with values to 1e-5; codes within 1 LSB on <= 1e-4 of entries; scales to 1e-5.
 """
@@ -215,5 +215,104 @@ def test_comp_chunk_m0_is_the_plain_chunk(torch_cuda):
         else:
             gpu.chunk(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], o)
         outs.append((o.cpu().numpy(), *gpu.to_host()))
+    for x, y in zip(*outs):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def run_comp_windows(torch, w, n_req, n_head, bits, m, W, n_windows, S0, name):
+    """Window mode with tokens: W per-token calls (the last one folds), teacher-forced
+    against the oracle's window with tokens from the GPU's state at each window start."""
+    from quantized_delta_rule_03_amd import qdr
+
+    gpu = qdr.StatePool(n_req, n_head, w.gate, bits, window=W)
+    ref = oracle.Pool(n_req, n_head, bits)
+    ref.comp_quantize(S0, m)
+    gpu.load_host(ref.packed, ref.row_scale, ref.col_scale)
+    gpu.comp_load_host(ref.tok_idx, ref.tok_val)
+    worst_o, worst_flip, worst_lsb, ties = 0.0, 0.0, 0, 0
+    o = torch.empty((n_req, n_head, 128), dtype=torch.float32, device="cuda")
+    for c in range(n_windows):
+        toks = []
+        for t in range(W):
+            inp = wl.step_inputs(w, c * W + t, n_req=n_req)
+            toks.append({k: np.ascontiguousarray(v[:, :n_head]) for k, v in inp.items()})
+        stack = {k: np.ascontiguousarray(np.stack([x[k] for x in toks])) for k in toks[0]}
+        print(f"[{name}] window {c}: W={W} m={m} n_req={n_req} n_head={n_head}", flush=True)
+        tf = gpu_to_oracle(gpu, bits)
+        tf.tok_idx, tf.tok_val = [x.copy() for x in gpu.comp_to_host()]
+        o_tf = tf.comp_window(w.gate, stack["q"], stack["k"], stack["v"], stack["a"],
+                              stack["b"])
+        ref.comp_window(w.gate, stack["q"], stack["k"], stack["v"], stack["a"], stack["b"])
+        dev = to_dev(stack)
+        for t in range(W):
+            gpu.comp_window_token(t, dev["q"][t], dev["k"][t], dev["v"][t], dev["a"][t],
+                                  dev["b"][t], o)
+            og = o.cpu().numpy()
+            assert np.isfinite(og).all(), name
+            worst_o = max(worst_o, rel_l2(og, o_tf[t]))
+        gi, gv = gpu.comp_to_host()
+        same = token_sets_agree(gi.reshape(-1, m), gv.reshape(-1, m),
+                                tf.tok_idx.reshape(-1, m), tf.tok_val.reshape(-1, m), name)
+        if not same:
+            ties += 1
+            continue
+        g = gpu_to_oracle(gpu, bits)
+        lsb, frac = compare_codes(g.packed, tf.packed, tf)
+        worst_lsb, worst_flip = max(worst_lsb, lsb), max(worst_flip, frac)
+        assert np.allclose(g.row_scale, tf.row_scale, rtol=1e-5, atol=0), name
+        assert np.allclose(g.col_scale, tf.col_scale, rtol=1e-5, atol=0), name
+    drift = rel_l2(gpu.comp_dequantize().cpu().numpy(), ref.comp_dequantize())
+    print(f"[{name}] windows={n_windows} W={W} m={m} worst o rel-L2 tf={worst_o:.2e} "
+          f"worst flips tf={worst_flip:.2e} (max {worst_lsb} LSB) near-tie windows={ties} "
+          f"drift={drift:.2e}", flush=True)
+    assert worst_o <= O_REL_L2, name
+    assert worst_lsb <= 1 and worst_flip <= CODE_FLIP_FRAC, name
+    assert ties < n_windows, name
+    assert drift <= DRIFT_REL_L2, name
+
+
+def test_comp_window_kda_8bit_prewarmed(torch_cuda):
+    w = wl.WORKLOADS[4]
+    n_req = 2
+    S0 = spikes(prewarmed_state(w, n_req), 15)
+    run_comp_windows(torch_cuda, w, n_req, w.n_head, bits_for(w), 16, w.window, 2, S0,
+                     "comp window kda 8-bit W=64")
+
+
+def test_comp_window_gdn_mixed_widths(torch_cuda):
+    w = wl.WORKLOADS[1]
+    H = 8
+    rng = np.random.default_rng(16)
+    S0 = spikes((0.1 * rng.standard_normal((1, H, 128, 128))).astype(np.float32), 17)
+    run_comp_windows(torch_cuda, w, 1, H, bits_for(w, n_head=H), 64, 16, 3, S0,
+                     "comp window gdn mixed W=16 m=64")
+
+
+def test_comp_window_m0_is_the_plain_window(torch_cuda):
+    from quantized_delta_rule_03_amd import qdr
+
+    w = wl.WORKLOADS[2]
+    H, W = 4, 12
+    bits = bits_for(w, n_head=H)
+    rng = np.random.default_rng(18)
+    S0 = (0.1 * rng.standard_normal((1, H, 128, 128))).astype(np.float32)
+    toks = [to_dev({k: np.ascontiguousarray(v[:, :H]) for k, v in
+                    wl.step_inputs(w, t, n_req=1).items()}) for t in range(W)]
+    outs = []
+    for comp in (False, True):
+        gpu = qdr.StatePool(1, H, w.gate, bits, window=W)
+        gpu.quantize(torch_cuda.from_numpy(S0).cuda())
+        o = torch_cuda.empty((1, H, 128), dtype=torch_cuda.float32, device="cuda")
+        if comp:
+            gpu.comp_enable(0)
+        got = []
+        for t in range(W):
+            x = toks[t]
+            if comp:
+                gpu.comp_window_token(t, x["q"], x["k"], x["v"], x["a"], x["b"], o)
+            else:
+                gpu.window_token(t, x["q"], x["k"], x["v"], x["a"], x["b"], o)
+            got.append(o.cpu().numpy())
+        outs.append((np.stack(got), *gpu.to_host()))
     for x, y in zip(*outs):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
