@@ -179,9 +179,9 @@ int qdr_decode_chunk(const qdr_desc *desc, const void *meta, void *packed, float
  * largest first (equal magnitudes: smaller flat index i*dk + j first; j is the logical key
  * channel), and are set to 0 in the residual, which the STEPQuant rule quantizes.
  * Unused slots hold index QDR_TOK_EMPTY and value 0. The stored state is the dequantized
- * residual plus the tokens; a chunk starts from it, so the tokens go through the same
- * gated delta updates as the rest of the state, and the tokens are selected afresh from
- * the fp32 state at the chunk's end.
+ * residual plus the tokens; a window (one qdr_comp_chunk call, or W qdr_comp_window calls)
+ * starts from it, so the tokens go through the same gated delta updates as the rest of the
+ * state, and the tokens are selected afresh from the fp32 state at the window's end.
  * tok_idx: uint16 [n_req][n_head][m] (flat index i*128 + j); tok_val: fp32, same shape;
  * both caller-owned device buffers, 16-byte aligned. 0 <= m <= QDR_COMP_MAX; m = 0 is the
  * plain mode. Only QDR_RULE_STEP. Errors: all codes; QDR_EINVAL for m out of range;
