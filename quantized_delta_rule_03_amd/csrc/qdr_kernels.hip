@@ -1,4 +1,5 @@
-// qdr_kernels.hip -- gfx950 kernels of libqdr: init, quantize, dequantize, decode step.
+// qdr_kernels.hip -- gfx950 kernels of libqdr: init, quantize, dequantize, the decode step,
+// window mode (token calls and the fold), chunk mode, compensator tokens.
 //
 // Work decomposition. One work-group of 256 threads (4 wave64) owns one (request, head)
 // unit at a time. Wave w owns segment w of the tile, i.e. physical key positions
@@ -18,7 +19,8 @@
 //   dequant + gate   S' = fl(code * G_ij), G_ij = fl(cf_j * rf_i) (the entry's gated step)
 //   prediction       u_i = fl32(rf_i * sum_j code_ij (cf_j k_j)) in fp64
 //   delta            w_i = fl(b * fl(v_i - u_i)),  S_new = fma(w_i, k_j, S')
-//   readout          o_i = sum_j S_new_ij q_j (fp32, fixed order)
+//   readout          o_i = S_new q as rf_i sum_j code_ij (cf_j q_j) + w_i (k . q) in fp64,
+//                    rounded once (compared within tolerance: S_new's entries are rounded)
 //   refit            A_j = max_i |S_new_ij| (1 if 0), R_j = A_j / Qmax_j, invA = 1/A_j,
 //                    y = fl(S_new * invA), c_i = max_j |y| (1 if 0), M = fl(Qmax * (1/c_i))
 //   requant          field = RNE(y*M) + 2^(b-1), taken from fma(y, M, 2^23 + 2^(b-1))
