@@ -207,7 +207,8 @@ int qdr_comp_chunk(const qdr_desc *desc, const void *meta, void *packed, float *
  * entries of the window's start state (their contributions to the prediction and the
  * readout through the gated key and query); at t = W-1 the fold adds them to the state,
  * selects new tokens and requantizes the residual (in place on all of packed, scales and
- * tokens). Errors: as qdr_decode_window and the token checks above. */
+ * tokens). m and the token buffers must be the same for every call of a window; the tokens
+ * change only at t = W-1. Errors: as qdr_decode_window and the token checks above. */
 int qdr_comp_window(const qdr_desc *desc, const void *meta, void *packed, float *row_scale,
                     float *col_scale, int32_t m, uint16_t *tok_idx, float *tok_val,
                     void *window_buf, int32_t t, const float *q, const float *k, const float *v,
