@@ -420,9 +420,10 @@ constexpr int kTileMax = 16384;  // 128 x 128 codes at 8 bits
 
 // Exact dot products on the matrix cores. The prediction needs
 //   U_i = sum_j code_ij K_j,  K_j = cf_j k_j (exact in fp64),
-// to fp64 accuracy. Per segment s, K is written in balanced base-128 fixed point
-// relative to a power of two above the segment's max |K|:
-//   K_j = 2^Es sum_{t<8} d_jt 128^-(t+1) + e_j,  d in [-64, 64],  |e_j| <= 2^(Es-57).
+// to fp64 accuracy. Per segment s, K is written in base-128 fixed point relative to a
+// power of two above the segment's max |K|: N_j = RNE(K_j 2^(56-Es)), |N_j| < 2^55, and
+//   K_j = 2^(Es-56) sum_{t<8} d_jt 128^(7-t) + e_j,  |e_j| <= 2^(Es-57),
+// with 7-bit digits d (the top one signed, in [-64, 63]; the others in [0, 127]).
 // Then U_i = sum_s 2^(Es-56) sum_t 128^(7-t) D_ist with D_ist = sum_j code_ij d_jt,
 // exact int32 sums formed by v_mfma_i32_16x16x32_i8 (A = digit planes x positions,
 // B = positions x rows). The readout uses eight digit planes of Q_j = cf_j q_j the same
@@ -444,12 +445,12 @@ constexpr int kFS = kD + 4;  // float slot stride
 constexpr int kDS = kD + 2;  // double slot stride
 
 struct StepWork {
-  float cf[kD];  // column factor, physical order
+  float cf[kD];  // column factor / s (s: the code operand's scale), physical order
   float rf[kD];  // row factor
   float kp[kD];  // k, physical order
   float w[kD];
   float invA[kD];
-  float invc[kD];
+  float invc[kD];    // 1/c_i, or M_i = Qmax fl(1/c_i) when the width is uniform
   double osum[kD];  // rf_i-free readout sums from phase 2
   int8_t dig[4][kPlanes][4][8];  // [segment][plane][jg][operand byte]
   double scale_u[4], scale_o[4], kq[4];
@@ -613,8 +614,10 @@ __device__ __forceinline__ int half_max_i32(int x) {
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  // every lane's source is valid for the quad permutes and row rotations used here, so
+  // the old value is never selected; passing the source itself saves a zero move
+  const int lo = __builtin_amdgcn_update_dpp((int)u, (int)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(u >> 32), (int)(u >> 32), CTRL, 0xF, 0xF, false);
   return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
@@ -642,7 +645,8 @@ __device__ __forceinline__ void prep(const VecIn& vin, StepWork& W, int w, int l
   const float kk = vin.k[j], qq = vin.q[j];
   const float cf = (GATE == KDA) ? vin.a[j] * vin.R[p] : vin.R[p];
   if (half == 0) {
-    W.cf[p] = cf;
+    // the update's column factor cf / s (s = 1, 16, 4 at 8, 4, 6 bits: exact)
+    W.cf[p] = cf * (Bw == 8 ? 1.0f : (Bw == 4 ? 0.0625f : 0.25f));
     W.kp[p] = kk;
   } else {
     W.rf[p] = (GATE == GDN) ? vin.ag * vin.C[p] : vin.C[p];
@@ -651,15 +655,21 @@ __device__ __forceinline__ void prep(const VecIn& vin, StepWork& W, int w, int l
   int e = -2000;
   if (X != 0.0) (void)frexp(X, &e);
   const int E = half_max_i32(e) + 1;  // max |X| over the half < 2^(E-1)
-  double y = ldexp(X, -E);
-  int8_t* dst = &W.dig[w][8 * half][pl >> 3][operand_byte(Bw, pl & 7)];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    y *= 128.0;
-    const double r = rint(y);
-    y -= r;
-    dst[t * 32] = (int8_t)(int)r;  // plane stride: 4 x 8 bytes
-  }
+  // N = RNE(X 2^(56-E)), |N| < 2^55: an fp64 integer, since X = cf k has at most 48
+  // significant bits. Split N = h 2^28 + l (0 <= l < 2^28), then each into 7-bit digits
+  // (the top one signed): plane t carries the digit of weight 128^(7-t).
+  const double N = rint(ldexp(X, 56 - E));
+  const double hd = floor(N * 0x1p-28);
+  const int h = (int)hd, l = (int)fma(-hd, 268435456.0, N);
+  int8_t* dst = &W.dig[w][8 * half][pl >> 3][operand_byte(Bw, pl & 7)];  // plane stride 32 B
+  dst[0] = (int8_t)(h >> 21);
+  dst[32] = (int8_t)((h >> 14) & 127);
+  dst[64] = (int8_t)((h >> 7) & 127);
+  dst[96] = (int8_t)(h & 127);
+  dst[128] = (int8_t)(l >> 21);
+  dst[160] = (int8_t)((l >> 14) & 127);
+  dst[192] = (int8_t)((l >> 7) & 127);
+  dst[224] = (int8_t)(l & 127);
   const double kq = half_sum_f64(half ? 0.0 : (double)kk * (double)qq);
   // the code operands are s*code with s = 1, 16, 4 for 8, 4, 6 bits
   const int ls = Bw == 8 ? 0 : (Bw == 4 ? 4 : 2);
@@ -780,15 +790,15 @@ __device__ __forceinline__ void plane_sums(const StepWork& W, double* upart, con
 
 // Phase 3 for one code width: dequantize + gate and apply the rank-one update,
 //   S'_ij = fl(code_ij G_ij), G_ij = fl(cf_j rf_i),  S_new_ij = fma(w_i, k_j, S'_ij).
-// The code operand holds s*code, so the column factor enters as cf / s (exact).
+// The code operand holds s*code, so the column factor enters as cf / s (exact), which
+// prep stored in W.cf.
 template <int B>
 __device__ __forceinline__ void update_phase(const StepWork& W, int rg, int p0, const long (&op)[8],
                                              float (&s)[8][8]) {
-  constexpr float inv_s = 1.0f / (float)code_scale<B>();
   float cfs[8], km[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    cfs[m] = W.cf[p0 + m] * inv_s;
+    cfs[m] = W.cf[p0 + m];
     km[m] = W.kp[p0 + m];
   }
 #pragma unroll
@@ -980,7 +990,8 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
 #pragma unroll
       for (int g = 0; g < 16; ++g) cm = fmaxf(cm, W.part.cpart[g * kFS + i]);
       if (cm == 0.0f) cm = 1.0f;
-      W.invc[i] = 1.0f / cm;
+      // one width for the whole tile: M = fl(Qmax fl(1/c_i)) once per row here
+      W.invc[i] = B ? (float)((1 << (B - 1)) - 1) * (1.0f / cm) : 1.0f / cm;
     }
   }
   block_sync();  // B4
@@ -989,7 +1000,8 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   const float qmax = (float)((1 << (Bw - 1)) - 1);
   float M[8];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) M[rr] = (RULE == RULE_STEP) ? qmax * W.invc[rg + 16 * rr] : qmax;
+  for (int rr = 0; rr < 8; ++rr)
+    M[rr] = (RULE == RULE_STEP) ? (B ? W.invc[rg + 16 * rr] : qmax * W.invc[rg + 16 * rr]) : qmax;
   uint8_t* gseg = A.packed + cur.toff + sg.off;
   QDR_WIDTH_DISPATCH(B, Bw, (requant_store<BB>(gseg, rg, jg, s, M)));
   if (rg < 8) A.Rs[uo + p0 + rpos] = Rkeep;
