@@ -615,9 +615,9 @@ template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
   // every lane's source is valid for the quad permutes and row rotations used here, so
-  // the old value is never selected; passing the source itself saves a zero move
-  const int lo = __builtin_amdgcn_update_dpp((int)u, (int)u, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp((int)(u >> 32), (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  // no old value is needed (a plain DPP move, no zero-initialised destination)
+  const int lo = __builtin_amdgcn_mov_dpp((int)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(u >> 32), CTRL, 0xF, 0xF, false);
   return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
@@ -732,8 +732,10 @@ __device__ __forceinline__ long code_operand(Raw raw, int jg, const Sel6& sl) {
     const uint32_t lo = raw.lo ^ 0x80808080u, hi = raw.hi ^ 0x80808080u;
     return (long)(((uint64_t)hi << 32) | lo);
   } else if constexpr (B == 4) {
-    const uint32_t x = ((jg & 1) ? raw.hi : raw.lo) ^ 0x88888888u;  // two's complement nibbles
-    const uint32_t ev = (x << 4) & 0xF0F0F0F0u, od = x & 0xF0F0F0F0u;
+    // each nibble moved to the top of its byte, then the bias bit flipped
+    const uint32_t x = (jg & 1) ? raw.hi : raw.lo;
+    const uint32_t ev = ((x << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+    const uint32_t od = (x & 0xF0F0F0F0u) ^ 0x80808080u;
     return (long)(((uint64_t)od << 32) | ev);
   } else {
     const uint32_t p0 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p0), 4, 2);
@@ -746,7 +748,14 @@ __device__ __forceinline__ long code_operand(Raw raw, int jg, const Sel6& sl) {
   }
 }
 
+// One row's codes from the LDS slot (B is a compile-time width at every call): 4 bits
+// reads only the lane's own word and returns it as both halves, so that the odd/even
+// select of code_operand folds away.
 __device__ __forceinline__ Raw lds_row(const uint8_t* seg, int B, int i, int jg) {
+  if (B == 4) {
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(seg + i * 16 + 4 * jg);
+    return {x, x};
+  }
   const uint32_t* pr = reinterpret_cast<const uint32_t*>(seg + i * 4 * B + row_load_off(B, jg));
   return {pr[0], pr[1]};
 }
