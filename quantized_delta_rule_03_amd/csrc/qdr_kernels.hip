@@ -1344,12 +1344,19 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   }
 }
 
-// Split an fp32 value into three bf16 parts whose sum is exact.
+// Split an fp32 value into three bf16 parts whose sum is exact: each part is the top
+// 8 significant bits of what is left (truncation: the bf16 is the upper half of the fp32
+// pattern), so every subtraction is exact and the last part has at most 8 bits.
+__device__ __forceinline__ __bf16 bf16_hi(float x) {
+  return __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(x) >> 16));
+}
 __device__ __forceinline__ void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
-  h = (__bf16)x;
-  const float r1 = x - (float)h;
-  m = (__bf16)r1;
-  l = (__bf16)(r1 - (float)m);
+  const float hf = __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
+  const float r1 = x - hf;
+  const float mf = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+  h = bf16_hi(hf);
+  m = bf16_hi(mf);
+  l = bf16_hi(r1 - mf);
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
