@@ -456,7 +456,7 @@ struct StepWork {
   double scale_u[4], scale_o[4], kq[4];
   uint32_t tmax[4];  // per-wave state absmax (per-tensor rule)
   union {
-    double upart[16 * kDS];  // per (wave, jg) combined digit-plane sums
+    double upart[8 * kDS];   // per (wave, K or Q) combined digit-plane sums
     float cpart[16 * kFS];   // per (wave, jg) partial value-column absmax
   } part;
 };
@@ -621,6 +621,14 @@ __device__ __forceinline__ double dpp_f64(double x) {
   return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
+// the value of lane ^ 16 (within each half of the wave)
+__device__ __forceinline__ double swap16_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_ds_swizzle((int)u, 0x401F);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(u >> 32), 0x401F);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
 // sum over the 32 lanes of one half of the wave; lanes 0 and 32 end with the sum taken
 // in a fixed tree order
 __device__ __forceinline__ double half_sum_f64(double x) {
@@ -762,8 +770,9 @@ __device__ __forceinline__ Raw lds_row(const uint8_t* seg, int B, int i, int jg)
 
 // Phase 1 for one code width: the lane's code operands of its 8 rows (kept for the
 // update) and the digit-plane sums of the prediction and the readout, combined per
-// lane (4 planes of one row per 16-row block) into upart. The operands carry the
-// factor code_scale<B>(), which the segment's sum scales remove.
+// lane (4 planes of one row per 16-row block), then with the partner lane's other 4
+// planes, into upart[(2 w + K/Q) * kDS + row]. The operands carry the factor
+// code_scale<B>(), which the segment's sum scales remove.
 template <int B>
 __device__ __forceinline__ void plane_sums_raw(const StepWork& W, double* upart, const Raw (&raw)[8],
                                                int w, int rg, int jg, long (&op)[8]) {
@@ -780,11 +789,19 @@ __device__ __forceinline__ void plane_sums_raw(const StepWork& W, double* upart,
     asm volatile("" : "+v"(lo), "+v"(hi));
     op[rr] = (long)(((uint64_t)hi << 32) | lo);
   }
+  double c[8];
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
     // D[plane 4jg+t][row rg of block rr] for t = 0..3
     const v4i d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a_op, op[rr], zero, 0, 0, 0);
-    upart[(4 * w + jg) * kDS + rg + 16 * rr] = combine4(d);
+    const double x = combine4(d);
+    // lanes jg and jg ^ 1 hold the high (planes 0-3) and low (4-7) parts of one row's K
+    // (jg < 2) or Q sum; the even lane forms hi 2^28 + lo (one rounding)
+    c[rr] = fma(x, 268435456.0, swap16_f64(x));
+  }
+  if (!(jg & 1)) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) upart[(2 * w + (jg >> 1)) * kDS + rg + 16 * rr] = c[rr];
   }
 }
 
@@ -928,14 +945,14 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
       double U = 0.0;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        U += W.scale_u[s] * fma(up[(4 * s) * kDS], 268435456.0, up[(4 * s + 1) * kDS]);
+        U += W.scale_u[s] * up[(2 * s) * kDS];
       const float uu = (float)((double)W.rf[i] * U);
       W.w[i] = vin.b * (vin.v[i] - uu);
     } else {
       double O = 0.0;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        O += W.scale_o[s] * fma(up[(4 * s + 2) * kDS], 268435456.0, up[(4 * s + 3) * kDS]);
+        O += W.scale_o[s] * up[(2 * s + 1) * kDS];
       W.osum[i] = O;
     }
   }
@@ -1233,13 +1250,13 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
       double U = 0.0;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        U += L.W.scale_u[s] * fma(up[(4 * s) * kDS], 268435456.0, up[(4 * s + 1) * kDS]);
+        U += L.W.scale_u[s] * up[(2 * s) * kDS];
       L.xs[i] = (float)((double)L.W.rf[i] * U);
     } else {
       double O = 0.0;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        O += L.W.scale_o[s] * fma(up[(4 * s + 2) * kDS], 268435456.0, up[(4 * s + 3) * kDS]);
+        O += L.W.scale_o[s] * up[(2 * s + 1) * kDS];
       L.W.osum[i] = O;
     }
   }
