@@ -140,9 +140,18 @@ __device__ __forceinline__ void store_row(uint8_t* seg, int row, int jg, const u
     *reinterpret_cast<uint32_t*>(seg + row * 16 + jg * 4) =
         perm_b32(perm_b32(p3, p2, 0x0c0c0400u), perm_b32(p1, p0, 0x0c0c0400u), 0x05040100u);
   } else {
-    // 24-bit groups of 4 fields; the exponent bits of t (>= bit 23) never reach bits 0..23
-    const uint32_t g0 = (t[3] << 18) | (t[2] << 12) | (t[1] << 6) | t[0];
-    const uint32_t g1 = (t[7] << 18) | (t[6] << 12) | (t[5] << 6) | t[4];
+    // 24-bit groups of 4 fields, three shift-or steps each (the empty asm keeps the
+    // compiler from re-associating them into four instructions); the exponent bits of t
+    // (bits 24, 25, 27, 30 of 2^23 + field) never reach bits 0..23 of a group
+    auto group = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+      uint32_t x = (d << 6) | c;
+      asm volatile("" : "+v"(x));
+      x = (x << 6) | b;
+      asm volatile("" : "+v"(x));
+      return (x << 6) | a;
+    };
+    const uint32_t g0 = group(t[0], t[1], t[2], t[3]);
+    const uint32_t g1 = group(t[4], t[5], t[6], t[7]);
     // even jg: dword at +0, short at +4; odd jg: short at +0, dword at +2 (no branch)
     uint8_t* dst = seg + row * 24 + jg * 6;
     const uint32_t par = (uint32_t)(jg & 1);
@@ -535,10 +544,11 @@ __device__ __forceinline__ Seg seg_from(uint32_t sb, int w) {
 }
 
 // Byte of an 8-position group at which position m sits in the MFMA code operand:
-// natural order for 8 and 6 bits; even positions then odd ones for 4 bits (that is
-// how the nibble pairs separate into bytes).
+// natural order for 8 bits; even positions then odd ones for 4 bits (that is how the
+// nibble pairs separate into bytes); for 6 bits the first two positions of each group
+// of four trade places (the order in which code_operand<6> extracts the fields).
 __device__ __forceinline__ int operand_byte(int B, int m) {
-  return B == 4 ? ((m & 1) ? 4 + (m >> 1) : (m >> 1)) : m;
+  return B == 4 ? ((m & 1) ? 4 + (m >> 1) : (m >> 1)) : (B == 6 && !(m & 2) ? m ^ 1 : m);
 }
 
 // One lane's share of the next unit, held in registers until it is written to LDS.
@@ -712,17 +722,16 @@ __device__ __forceinline__ uint32_t shl16x2(uint32_t x, uint16_t a, uint16_t b) 
 
 // Byte selectors that unpack one lane's eight 6-bit fields from the 8 bytes it loads
 // (its 6 bytes start at byte 0 for even jg, byte 2 for odd jg). For a 24-bit group
-// g = bytes (c0, c1, c2): P = (c0 c1 | c1 c2) shifted right by (4, 2) per 16-bit half
-// puts fields 1 and 2 in bits 2-7 of bytes 0 and 2; Q = (c0 0 | c2 0) shifted left by
-// (2, 0) puts fields 0 and 3 there; one more byte select interleaves them.
+// g = bytes (c0, c1, c2), U = (c0 c1 | c1 c2) as two 16-bit halves: U shifted right by
+// (4, 2) puts fields 1 and 2 in bits 2-7 of bytes 0 and 2, U shifted left by (10, 0)
+// puts fields 0 and 3 in bits 2-7 of bytes 1 and 3; one byte select takes those four.
 struct Sel6 {
-  uint32_t p0, q0, p1, q1;
+  uint32_t p0, p1;
 };
 
 __device__ __forceinline__ Sel6 sel6_for(int jg) {
   const uint32_t o = (jg & 1) ? 0x02020202u : 0u;
-  return {0x02010100u + o, 0x0C020C00u + (o & 0x00FF00FFu), 0x05040403u + o,
-          0x0C050C03u + (o & 0x00FF00FFu)};
+  return {0x02010100u + o, 0x05040403u + o};
 }
 
 // Codes of one row as signed bytes s*code in the byte order of operand_byte, where
@@ -746,12 +755,15 @@ __device__ __forceinline__ long code_operand(Raw raw, int jg, const Sel6& sl) {
     const uint32_t od = (x & 0xF0F0F0F0u) ^ 0x80808080u;
     return (long)(((uint64_t)od << 32) | ev);
   } else {
-    const uint32_t p0 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p0), 4, 2);
-    const uint32_t q0 = shl16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.q0), 2, 0);
-    const uint32_t p1 = shr16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.p1), 4, 2);
-    const uint32_t q1 = shl16x2(__builtin_amdgcn_perm(raw.hi, raw.lo, sl.q1), 2, 0);
-    const uint32_t lo = (__builtin_amdgcn_perm(p0, q0, 0x02060400u) & 0xFCFCFCFCu) ^ 0x80808080u;
-    const uint32_t hi = (__builtin_amdgcn_perm(p1, q1, 0x02060400u) & 0xFCFCFCFCu) ^ 0x80808080u;
+    const uint32_t u0 = __builtin_amdgcn_perm(raw.hi, raw.lo, sl.p0);
+    const uint32_t u1 = __builtin_amdgcn_perm(raw.hi, raw.lo, sl.p1);
+    // bytes [field 1, field 0, field 2, field 3] of each group, low 2 bits then cleared
+    const uint32_t lo =
+        (__builtin_amdgcn_perm(shl16x2(u0, 10, 0), shr16x2(u0, 4, 2), 0x07020500u) & 0xFCFCFCFCu) ^
+        0x80808080u;
+    const uint32_t hi =
+        (__builtin_amdgcn_perm(shl16x2(u1, 10, 0), shr16x2(u1, 4, 2), 0x07020500u) & 0xFCFCFCFCu) ^
+        0x80808080u;
     return (long)(((uint64_t)hi << 32) | lo);
   }
 }
