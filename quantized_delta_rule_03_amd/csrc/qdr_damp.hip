@@ -40,6 +40,13 @@ struct DampLds {
   float part[4][kD];  // per-wave key-row absmax
 };
 
+// a ^ b ^ k in one gfx950 three-input bit operation (truth table 0x96), k uniform
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC11): ten rounds of two 32x32 -> 64-bit
 // products on the counter, the key advanced by the Weyl constants between rounds.
 __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
@@ -53,8 +60,8 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
     const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
     const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    const uint32_t n0 = hi1 ^ c1 ^ k0;
-    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    const uint32_t n0 = xor3(hi1, c1, k0);
+    const uint32_t n2 = xor3(hi0, c3, k1);
     c0 = n0;
     c1 = lo1;
     c2 = n2;
