@@ -231,6 +231,44 @@ def test_mixed_width_heads_and_special_inputs(torch_cuda):
     assert traj.worst_flip_tf <= CODE_FLIP_FRAC
 
 
+def test_sparse_and_tiny_keys_and_queries(torch_cuda):
+    """Keys and queries with whole zero segments, single nonzero positions and values down
+    to fp32 subnormals next to normal ones in one segment: the per-segment fixed-point
+    scale of the exact dot products must keep every term the fp32 results can see."""
+    bits = np.stack([np.full(128, b, np.uint8) for b in (4, 6, 8)])
+    rng = np.random.default_rng(17)
+    n_req = 3
+    S0 = rng.standard_normal((n_req, 3, 128, 128)).astype(np.float32)
+    gpu = make_pool(n_req, 3, 0, bits)
+    ref = oracle.Pool(n_req, 3, bits)
+    ref.quantize(S0)
+    gpu.load_host(ref.packed, ref.row_scale, ref.col_scale)
+    traj = Trajectory(gpu, ref, 0)
+    for t in range(6):
+        k = rng.standard_normal((n_req, 3, 128)).astype(np.float32)
+        q = rng.standard_normal((n_req, 3, 128)).astype(np.float32)
+        # request 0: segments 0-1 zero; segment 2 mixes 1, 1e-30 and subnormals
+        k[0, :, :64] = 0.0
+        k[0, :, 64:70] = [1.0, 1e-30, 1e-40, -3e-39, 1e-20, -1.0]
+        q[0, :, :32] = 0.0
+        q[0, :, 32:36] = [1e-38, -1e-44, 5e-39, 1.0]
+        # request 1: one nonzero key per segment, a query spanning 1e-20 .. 1e3
+        k[1] = 0.0
+        for pos, val in ((5, 0.5), (40, -1e-12), (77, 0.25), (120, 3e-8)):
+            k[1, :, pos] = val
+        q[1] = (q[1] * np.logspace(-20, 3, 128)).astype(np.float32)
+        nrm = np.linalg.norm(k.astype(np.float64), axis=-1, keepdims=True)
+        k = np.where(nrm > 0, k / np.maximum(nrm, 1e-300), k).astype(np.float32)
+        inp = {"q": q, "k": k,
+               "v": rng.standard_normal((n_req, 3, 128)).astype(np.float32),
+               "a": rng.uniform(0.5, 1, (n_req, 3)).astype(np.float32),
+               "b": rng.uniform(0, 1, (n_req, 3)).astype(np.float32)}
+        traj.step(inp)
+    report("sparse / tiny keys and queries", traj)
+    assert traj.worst_o_tf <= O_REL_L2 and traj.worst_lsb_tf <= 1
+    assert traj.worst_flip_tf <= CODE_FLIP_FRAC
+
+
 def test_deterministic(torch_cuda):
     torch = torch_cuda
     w = wl.WORKLOADS[1]
