@@ -10,7 +10,8 @@
 //    i.e. one contiguous 64*b-byte block (512 B at 8 bits).
 //  - Key-row (column) absmax stays inside a wave: in-lane over 8 rows, then across the
 //    16 lanes of one DPP row. Value-row reductions (prediction, readout, value-column
-//    absmax) go through LDS over the 16 (wave, jg) partials of a row.
+//    absmax) go through LDS: 8 (wave, K or Q) partial sums or 16 (wave, jg) partial
+//    maxima per row.
 //  - The decode step is persistent: a grid of (CUs x resident groups) work-groups walks
 //    the units, and each group issues the loads of its next unit's codes and vectors
 //    before computing the current one, so HBM reads stay in flight during the compute.
@@ -421,7 +422,7 @@ __global__ void __launch_bounds__(kThreads) k_dequantize(const void* meta, int n
 //   B1 phase 2          u, w (waves 0-1) and the readout sum (waves 2-3) per row
 //   B2 phase 3          the next unit's inputs to LDS; o; dequantize + gate + update;
 //                       key-row absmax in the wave; normalise; per-row partial
-//                       value-column maxima
+//                       value-column maxima (at raised wave priority)
 //   B3 phase 4          value-column scales (two waves, alternating per unit)
 //   B4 phase 5          requantize, pack and store the segment; store the scales
 // ------------------------------------------------------------------------------
@@ -448,8 +449,9 @@ struct VecIn {
   uint8_t perm[kD];         // physical position -> logical key channel
 };
 
-// Partial arrays: 16 slots (wave, jg) of one value per row; slot strides are padded so
-// that the four jg slots written by one instruction fall in different LDS banks.
+// Partial arrays: 8 slots (wave, K or Q) or 16 slots (wave, jg) of one value per row;
+// slot strides are padded so that the slots written by one instruction fall in different
+// LDS banks.
 constexpr int kFS = kD + 4;  // float slot stride
 constexpr int kDS = kD + 2;  // double slot stride
 
