@@ -690,7 +690,18 @@ __device__ __forceinline__ void prep(const VecIn& vin, StepWork& W, int w, int l
   dst[160] = (int8_t)((l >> 14) & 127);
   dst[192] = (int8_t)((l >> 7) & 127);
   dst[224] = (int8_t)(l & 127);
-  const double kq = half_sum_f64(half ? 0.0 : (double)kk * (double)qq);
+  // k.q over all 128 channels on wave 3 only (the readout adds the four slots; the
+  // others hold 0): two products per lane, then a fixed tree over the wave
+  double kq = 0.0;
+  if (w == 3) {
+    const double pr = fma((double)vin.k[lane + 64], (double)vin.q[lane + 64],
+                          (double)vin.k[lane] * (double)vin.q[lane]);
+    const double hs = half_sum_f64(pr);
+    const uint64_t h0 = (uint64_t)__double_as_longlong(hs);
+    const uint32_t lo32 = (uint32_t)__builtin_amdgcn_readlane((int)h0, 32);
+    const uint32_t hi32 = (uint32_t)__builtin_amdgcn_readlane((int)(h0 >> 32), 32);
+    kq = hs + __longlong_as_double((long long)(((uint64_t)hi32 << 32) | lo32));
+  }
   // the code operands are s*code with s = 1, 16, 4 for 8, 4, 6 bits
   const int ls = Bw == 8 ? 0 : (Bw == 4 ? 4 : 2);
   if (lane == 0) {
