@@ -130,11 +130,11 @@ __device__ __forceinline__ int8_t* code_word(int8_t* crow, int seg, int q) {
 // floor(127 2^24 y + r) >> 24 (floor of a floor quotient), and 127 2^24 y + r is one fp64
 // fma with the same single rounding as the unscaled fp64 sum (exact for |y| >= 2^-23; no
 // integer is crossed below that); y is clamped to [-1, 1] first, which leaves the clamped
-// result unchanged and keeps the floor inside int32.
-__device__ __forceinline__ int sr_code(float y, uint32_t r24) {
+// result unchanged and keeps the floor inside int32. sr_scaled returns the scaled floor;
+// the code is its top byte (>> 24).
+__device__ __forceinline__ int sr_scaled(float y, uint32_t r24) {
   const float yc = fminf(fmaxf(y, -1.0f), 1.0f);
-  const double t = floor(fma((double)yc, 2130706432.0, (double)r24));  // 127 * 2^24
-  return (int)t >> 24;
+  return (int)floor(fma((double)yc, 2130706432.0, (double)r24));  // 127 * 2^24
 }
 
 // ranges and requantization of the register-held half rows, stored in place
@@ -183,15 +183,17 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
   for (int b = 0; b < 14; ++b) {
     const uint4 r = philox4x32_10((uint32_t)(i * 32 + base / 4 + b), (uint32_t)u, s0, s1, k0, k1);
     const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-    uint32_t word = 0;
+    // the codes are the top bytes of the scaled floors: byte selects pack four
+    uint32_t t[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * b + e;  // position base + j
       const float sv = seg ? Sr[8 + j] : (j < 48 ? Sr[16 + j] : x[j - 48]);
       const float y = sv * L.invA[base + j];
-      word |= ((uint32_t)(uint8_t)(int8_t)sr_code(y, rw[e] >> 8)) << (8 * e);
+      t[e] = (uint32_t)sr_scaled(y, rw[e] >> 8);
     }
-    wd[b] = word;
+    wd[b] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(t[3], t[2], 0x0C0C0703u),
+                                  __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0703u), 0x05040100u);
   }
   int8_t* crow = A.codes + ((size_t)u * kD + i) * kI;
   if (seg == 0) {
