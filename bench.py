@@ -382,7 +382,64 @@ def cpu_baseline(w, bits, threads: int, n_req: int, steps: int):
             "kind": "oracle",
             "sample": f"{steps} steps x {n_req} requests x {w.n_head} heads "
                       f"({updates} state updates) of the same workload, oracle on "
-                      f"{threads} host threads, {dt:.2f} s wall"}
+                      f"{threads} host thread{'s' if threads > 1 else ''}, {dt:.2f} s wall"}
+
+
+def host_threads() -> int:
+    """Host threads for the multi-threaded baseline: the CPUs this process may run on,
+    capped at 16 (one GPU's share of a shared GPU host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baselines(w, bits, args):
+    """The oracle timed twice on the host: one thread over a small sample, and all usable
+    host threads over the larger one. The multi-threaded figure is the reported value."""
+    threads = host_threads()
+    log(f"cpu baseline: oracle on 1 thread, {args.cpu1_requests} requests x "
+        f"{args.cpu1_steps} steps")
+    one = cpu_baseline(w, bits, 1, args.cpu1_requests, args.cpu1_steps)
+    log(f"cpu baseline: oracle on {threads} threads, {args.cpu_requests} requests x "
+        f"{args.cpu_steps} steps")
+    many = cpu_baseline(w, bits, threads, args.cpu_requests, args.cpu_steps)
+    many["nproc"] = os.cpu_count()
+    many["single_thread"] = one
+    return many
+
+
+def probe_clock_mhz(torch, qdr, dev, iters=40000):
+    """Engine clock sustained under full VALU load (8 work-groups per CU of a dependent
+    fp32 fma chain): shader-clock cycles over constant-rate ticks."""
+    n_block = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.zeros((n_block, 4), dtype=torch.int64, device=dev)
+    qdr.probe_clock(out, iters)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    return float(o[:, 0].sum() / o[:, 1].sum() * qdr.probe_wall_rate() / 1e6)
+
+
+def probe_copy_gbps(torch, qdr, dev, nbytes: int, reps: int = 10):
+    """Achievable HBM read+write bandwidth: a streaming copy of nbytes (read nbytes, write
+    nbytes) on the probe kernel, mean over reps timed copies after two untimed ones."""
+    n = (nbytes // 16) * 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        qdr.probe_copy(src, dst, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for s_, e_ in ev:
+        s_.record(stream)
+        qdr.probe_copy(src, dst, stream)
+        e_.record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev])) / 1e3
+    del src, dst
+    return 2.0 * n * 4 / t / 1e9
 
 
 def main():
@@ -396,6 +453,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=1024)
     ap.add_argument("--cpu-steps", type=int, default=24)
+    ap.add_argument("--cpu1-requests", type=int, default=128)
+    ap.add_argument("--cpu1-steps", type=int, default=8)
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the clock and copy-bandwidth probes")
     ap.add_argument("--workload",
                     choices=["serving", "window", "chunk", "comp", "compare", "damp"],
                     default="serving",
@@ -449,6 +510,7 @@ def main():
     def launch(inp):
         pool.step(inp["q"], inp["k"], inp["v"], a, inp["b"], o, stream=stream)
 
+    clock_before = None if args.no_probes else probe_clock_mhz(torch, qdr, dev, iters=10000)
     for t in range(args.warmup):
         launch(inputs[t])
     torch.cuda.synchronize()
@@ -472,6 +534,17 @@ def main():
     achieved = nbytes / avg_kern_s / 1e9
     log(f"step kernel: mean {kern_ms.mean()*1e3:.1f} us, median {np.median(kern_ms)*1e3:.1f} us; "
         f"{achieved:.0f} GB/s algorithmic ({100*achieved/HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    probes = None
+    if not args.no_probes:
+        clock_after = probe_clock_mhz(torch, qdr, dev)
+        del inputs
+        copy_gbps = probe_copy_gbps(torch, qdr, dev, nbytes // 2)
+        probes = {"copy_gbps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
+                  "copy_bytes_each_way": (nbytes // 2 // 16) * 16,
+                  "clock_mhz_before_warmup": clock_before, "clock_mhz_after": clock_after}
+        log(f"probes: streaming copy {copy_gbps:.0f} GB/s (step at {100*achieved/copy_gbps:.1f}% "
+            f"of it); engine clock {clock_before:.0f} MHz before warm-up, {clock_after:.0f} MHz "
+            f"after the timed steps")
 
     prof = profile_record()
     traffic = float(prof["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in prof else None
@@ -480,14 +553,12 @@ def main():
         lane_ops = float(prof["SQ_INSTS_VALU"]) * 64
         valu = {"lane_ops_per_launch": lane_ops, "achieved": lane_ops / avg_kern_s,
                 "peak": VALU_PEAK_LANE_OPS, "unit": "lane-ops/s",
-                "frac": lane_ops / avg_kern_s / VALU_PEAK_LANE_OPS}
+                "frac": lane_ops / avg_kern_s / VALU_PEAK_LANE_OPS,
+                "lane_ops_per_entry": lane_ops / (n_unit * 128 * 128)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
-        log(f"cpu baseline: oracle on {threads} threads, {args.cpu_requests} requests x "
-            f"{args.cpu_steps} steps")
-        cpu = cpu_baseline(w, bits, threads, args.cpu_requests, args.cpu_steps)
+        cpu = cpu_baselines(w, bits, args)
 
     out = {
         "metric": METRIC,
@@ -511,7 +582,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_step<GDN>", "bytes_per_launch": nbytes,
-                     "avg_launch_us": avg_kern_s * 1e6},
+                     "avg_launch_us": avg_kern_s * 1e6,
+                     "median_launch_us": float(np.median(kern_ms)) * 1e3},
+        "probes": probes,
         "valu": valu,
         "cpu_baseline": cpu,
     }

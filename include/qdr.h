@@ -235,9 +235,10 @@ int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *pac
  *   meta  [n_head][128]                 physical position -> key channel (written by init)
  * Physical positions 0..15 are the selected channels, 16..127 the others, each in
  * increasing channel order. One decode step: S'_ij = fl(f32(h) a_j) or fl(code fl(a_j R_j));
- * u_i = fl32(s0 + s1) with s0, s1 the fp64 sums of S'_ij k_j over positions 0..63 and
- * 64..127 in position order; w_i = fl(b fl(v_i - u_i)); S_new = fma(w_i, k_j, S'_ij); o the
- * same sums with S_new and q; then binary16 (round to nearest even) for the selected
+ * u_i = S' k and o_i = S_new q accumulated in fp64 and rounded once to fp32 (the products
+ * are exact in fp64; the order of the fp64 sums is the kernel's, so u and o can differ from
+ * another fp64 order in the last fp32 bit on rare ties); w_i = fl(b fl(v_i - u_i));
+ * S_new = fma(w_i, k_j, S'_ij); then binary16 (round to nearest even) for the selected
  * channels and, for the others, A_j = max_i |S_ij| (1 if 0), R_j = fl(A_j/127),
  * y = fl(S fl(1/A_j)), code = clamp(floor(y*127 + u), +-127) evaluated in fp64 with u the
  * top 24 bits (times 2^-24) of word position%4 of Philox4x32-10 (Salmon et al., SC11) for
@@ -271,6 +272,28 @@ int qdr_damp_step(const qdr_damp_desc *desc, const void *meta, void *half, void 
 /* readback S [n_req][n_head][128][128] (logical key order): f32(h) or fl(code R_j) */
 int qdr_damp_dequantize(const qdr_damp_desc *desc, const void *meta, const void *half,
                         const void *codes, const float *R, float *S, void *stream);
+
+/* ---- measurement helpers (not part of the decode path) -----------------------------
+ * The freedom251 page's checklist under "How to decide for a deployment" asks for the
+ * update kernel to be measured on the deployment's own hardware; these two kernels give
+ * the reference points such a measurement is read against.
+ *
+ * qdr_probe_copy: a streaming copy of `bytes` bytes from src to dst (device pointers,
+ * 16-byte aligned, bytes a multiple of 16, non-overlapping), 16-byte loads and stores.
+ * Timed by the caller (events on `stream`), 2*bytes / time is the achievable HBM
+ * read+write bandwidth. Errors: QDR_EINVAL, QDR_EHIP (text in qdr_probe_last_error).
+ *
+ * qdr_probe_clock: n_block work-groups of 256 threads each run `iters` iterations of a
+ * dependent fp32 fma chain; thread 0 of block b writes out[4b] = shader-clock cycles and
+ * out[4b+1] = ticks of the constant-rate counter elapsed over the block's run (out: device
+ * [n_block][4] uint64, caller-owned). Sum(out[4b]) / Sum(out[4b+1]) * qdr_probe_wall_rate
+ * is the engine clock sustained under full VALU load. Errors: QDR_EINVAL, QDR_EHIP.
+ *
+ * qdr_probe_wall_rate: HOST output, the constant-rate counter's frequency in Hz. */
+int qdr_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+int qdr_probe_clock(unsigned long long *out, int32_t n_block, int32_t iters, void *stream);
+int qdr_probe_wall_rate(double *hz);
+const char *qdr_probe_last_error(void);
 
 /* Text of the last error on the calling thread ("" if none). Never NULL. */
 const char *qdr_last_error(void);

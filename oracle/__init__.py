@@ -439,6 +439,30 @@ class Pool:
             raise RuntimeError("oref_window_pool failed")
         return o
 
+    def window_threads(self, gate, q, k, v, a, b, threads=8):
+        """``window`` over all units, split into contiguous unit ranges on host threads
+        (disjoint ranges, so the results are those of ``window``)."""
+        from concurrent.futures import ThreadPoolExecutor
+
+        n_unit = self.n_req * self.n_head
+        q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        W = b.shape[0]
+        o = np.zeros((W, self.n_req, self.n_head, self.dv), np.float32)
+        cuts = np.linspace(0, n_unit, max(1, min(threads, n_unit)) + 1).astype(int)
+
+        def run(i):
+            return lib().oref_window_pool(self.n_req, self.n_head, self.dv, self.dk, gate,
+                                          _p(self.bits), _p(self.packed), _p(self.row_scale),
+                                          _p(self.col_scale), W, _p(q), _p(k), _p(v), _p(a),
+                                          _p(b), _p(o), int(cuts[i]), int(cuts[i + 1]))
+
+        with ThreadPoolExecutor(len(cuts) - 1) as ex:
+            rcs = list(ex.map(run, range(len(cuts) - 1)))
+        if any(rcs):
+            raise RuntimeError("oref_window_pool failed")
+        return o
+
 
 # ---------------------------------------------------------------------------
 # DAMP-style storage variant (see qdr_oracle.h)

@@ -851,10 +851,9 @@ void oref_damp_step(int dv, int gate, const uint8_t *perm, uint16_t *half, int8_
                     float b, float *o, uint64_t seed, uint32_t unit, uint64_t step) {
     const int NI = 128 - OREF_DAMP_HALF;
     float *Sp = (float *)malloc(sizeof(float) * (size_t)dv * 128);
-    float kp[128], qp[128], gp[128];
+    float kp[128], gp[128];
     for (int p = 0; p < 128; ++p) {
         kp[p] = k[perm[p]];
-        qp[p] = q[perm[p]];
         gp[p] = (gate == OREF_KDA) ? a[perm[p]] : a[0];
     }
     /* gated dequantization: fp16 channels fl(h * a_j); INT8 channels fl(code * fl(a_j R_j)) */
@@ -865,19 +864,22 @@ void oref_damp_step(int dv, int gate, const uint8_t *perm, uint16_t *half, int8_
                     ? oref_f16_to_f32(half[(size_t)i * OREF_DAMP_HALF + p]) * gp[p]
                     : (float)codes[(size_t)i * NI + (p - OREF_DAMP_HALF)] *
                           (gp[p] * R[p - OREF_DAMP_HALF]);
+    int pos[128]; /* physical position of logical key channel j */
+    for (int p = 0; p < 128; ++p) pos[perm[p]] = p;
     for (int i = 0; i < dv; ++i) {
-        /* u = S' k: two fp64 partial sums over the position halves, in position order */
-        double s0 = 0.0, s1 = 0.0;
-        for (int p = 0; p < 64; ++p) s0 += (double)Sp[(size_t)i * 128 + p] * (double)kp[p];
-        for (int p = 64; p < 128; ++p) s1 += (double)Sp[(size_t)i * 128 + p] * (double)kp[p];
-        const float u = (float)(s0 + s1);
+        /* u = S' k: one fp64 sum over the key channels j = 0..127 in logical order */
+        double su = 0.0;
+        for (int j = 0; j < 128; ++j)
+            su += (double)Sp[(size_t)i * 128 + pos[j]] * (double)k[j];
+        const float u = (float)su;
         const float w = b * (v[i] - u);
         for (int p = 0; p < 128; ++p)
             Sp[(size_t)i * 128 + p] = fmaf(w, kp[p], Sp[(size_t)i * 128 + p]);
-        double t0 = 0.0, t1 = 0.0;
-        for (int p = 0; p < 64; ++p) t0 += (double)Sp[(size_t)i * 128 + p] * (double)qp[p];
-        for (int p = 64; p < 128; ++p) t1 += (double)Sp[(size_t)i * 128 + p] * (double)qp[p];
-        o[i] = (float)(t0 + t1);
+        /* o = S_new q, the same way */
+        double so = 0.0;
+        for (int j = 0; j < 128; ++j)
+            so += (double)Sp[(size_t)i * 128 + pos[j]] * (double)q[j];
+        o[i] = (float)so;
     }
     damp_requant(dv, Sp, half, codes, R, seed, unit, step);
     free(Sp);

@@ -189,12 +189,12 @@ int oref_comp_window_pool(int n_req, int n_head, int dv, int dk, int gate, const
  * INT8 with one range per key row and stochastic rounding. Physical positions 0..15 are
  * the selected channels, 16..127 the others, each in increasing channel order
  * (perm[p] = logical channel). Storage per unit: half[dv][16], codes[dv][112], R[112].
- * Contract (shared with the GPU variant):
+ * Arithmetic:
  *   dequantize   S = f32(h) (selected) or fl(code * R_j)
  *   gate         S' = fl(f32(h) * a_j) or fl(code * fl(a_j * R_j))   (GDN: a_j = a)
- *   u_i          fl32(s0 + s1), s0 / s1 = fp64 sums of S'_ip k_p over positions 0..63 /
- *                64..127 in position order; w_i = fl(b fl(v_i - u_i));
- *                S_new = fma(w_i, k_p, S'_ip); o_i the same sums with S_new and q
+ *   u_i          fl32(sum_j S'_ij k_j), one fp64 sum over the key channels j = 0..127 in
+ *                logical order; w_i = fl(b fl(v_i - u_i)); S_new = fma(w_i, k_j, S'_ij);
+ *                o_i = fl32(sum_j S_new_ij q_j), the same way
  *   requantize   selected: binary16 round-to-nearest-even; others: A_j = max_i |S_ij|
  *                (1 if 0), R_j = fl(A_j/127), y = fl(S * fl(1/A_j)),
  *                code = clamp(floor(y*127 + u), +-127) in fp64, u = uniform [0, 1):

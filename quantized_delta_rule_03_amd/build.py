@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqdr.so")
-SOURCES = ["qdr_kernels.hip", "qdr_damp.hip", "qdr_api.cpp"]
+SOURCES = ["qdr_kernels.hip", "qdr_damp.hip", "qdr_probe.hip", "qdr_api.cpp"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

@@ -501,7 +501,7 @@ struct UnitIter {
 // One unit's addressing, wave-uniform.
 struct UnitInfo {
   uint32_t un;    // r * n_head + h: offset of the unit's vectors and scales / 128
-  uint32_t toff;  // byte offset of the tile in the pool
+  uint64_t toff;  // byte offset of the tile in the pool (pools may exceed 4 GiB)
   uint32_t sb;    // byte s = width of segment s
   uint32_t h;
 };
@@ -524,7 +524,7 @@ __device__ __forceinline__ UnitInfo unit_info(const StepArgs& A, const UnitIter&
   const uint32_t hb = (uint32_t)(sizeof(MetaHeader) + (size_t)h * sizeof(MetaHead)) / 4;
   UnitInfo u;
   u.un = (uint32_t)(it.r * A.n_head + h);
-  u.toff = (uint32_t)it.r * A.req_bytes + meta_dword(A.meta, hb);  // MetaHead::tile_off
+  u.toff = (uint64_t)it.r * A.req_bytes + meta_dword(A.meta, hb);  // MetaHead::tile_off
   u.sb = meta_dword(A.meta, hb + 2);                                // MetaHead::seg_bits
   u.h = (uint32_t)h;
   return u;
@@ -570,9 +570,12 @@ struct Prefetch {
 // (branches would merge the pending-load state of the prefetch registers at their
 // joins and force early waits):
 //   wave 0: k (lanes 0-31), q (32-63)    wave 1: v, R
-//   wave 2: C, a (KDA only)              wave 3: KDA position map (lanes 0-7); b, a (GDN)
-__device__ __forceinline__ bool vec_lane_active(int gate, int w, int lane) {
-  return w < 2 || (w == 2 && (gate == KDA || lane < 32)) || (w == 3 && gate == KDA && lane < 8);
+//   wave 2: C, a (KDA only)              wave 3: position map (lanes 0-7); b, a (GDN)
+// The position map (physical position -> key channel) is read by KDA and by the
+// mixed-width kernel (B == 0), whose heads may order their channels by width; a head of
+// a single width keeps the logical order.
+__device__ __forceinline__ bool vec_lane_active(int gate, bool perm, int w, int lane) {
+  return w < 2 || (w == 2 && (gate == KDA || lane < 32)) || (w == 3 && perm && lane < 8);
 }
 
 template <int GATE, int B>
@@ -593,7 +596,7 @@ __device__ __forceinline__ void issue_prefetch(const StepArgs& A, const UnitInfo
   const uintptr_t off = w == 3 ? (uintptr_t)lane * 16
                                : ((uintptr_t)u.un * kD + (uintptr_t)(lane & 31) * 4) * 4;
   const uintptr_t base = lane >= 32 ? hi : lo;
-  if (vec_lane_active(GATE, w, lane)) f.vec = *(gu32x4_ptr)(base + off);
+  if (vec_lane_active(GATE, GATE == KDA || B == 0, w, lane)) f.vec = *(gu32x4_ptr)(base + off);
   if (w == 3 && lane < (GATE == GDN ? 2 : 1))
     f.sc = *(gf32_ptr)((lane ? pa : (uintptr_t)A.b) + (uintptr_t)u.un * 4);
 }
@@ -611,7 +614,8 @@ __device__ __forceinline__ void commit_prefetch(const UnitInfo& u, int w, int la
   if (nchunk > 3) dst[192] = f.t3;
   // lanes 32-63 of waves 0-2 land in the array after the first one (q, R, a)
   float* vdst = w == 0 ? vin.k : (w == 1 ? vin.v : (w == 2 ? vin.C : reinterpret_cast<float*>(vin.perm)));
-  if (vec_lane_active(GATE, w, lane)) reinterpret_cast<u32x4*>(vdst)[lane] = f.vec;
+  if (vec_lane_active(GATE, GATE == KDA || B == 0, w, lane))
+    reinterpret_cast<u32x4*>(vdst)[lane] = f.vec;
   if (w == 3 && lane < (GATE == GDN ? 2 : 1)) (&vin.b)[lane] = f.sc;
 }
 
@@ -657,11 +661,11 @@ __device__ __forceinline__ double half_sum_f64(double x) {
 
 // Prep of wave w's segment: lanes 0-31 take K = cf k at position 32w + lane, lanes
 // 32-63 take Q = cf q there (and the row factor of value row 32w + lane - 32).
-template <int GATE>
+template <int GATE, bool PERM>
 __device__ __forceinline__ void prep(const VecIn& vin, StepWork& W, int w, int lane, int Bw) {
   const int half = lane >> 5, pl = lane & 31;
   const int p = 32 * w + pl;
-  const int j = (GATE == KDA) ? (int)vin.perm[p] : p;
+  const int j = PERM ? (int)vin.perm[p] : p;
   const float kk = vin.k[j], qq = vin.q[j];
   const float cf = (GATE == KDA) ? vin.a[j] * vin.R[p] : vin.R[p];
   if (half == 0) {
@@ -953,7 +957,7 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   const int p0 = 32 * w + 8 * jg;
   const size_t uo = (size_t)cur.un * kD;
 
-  prep<GATE>(vin, W, w, lane, Bw);
+  prep<GATE, GATE == KDA || B == 0>(vin, W, w, lane, Bw);
   wait_lgkm();
   __builtin_amdgcn_wave_barrier();
 
@@ -1209,7 +1213,7 @@ __device__ __forceinline__ UnitInfo win_unit_of(const void* meta, int n_head, ui
   const uint32_t hb = (uint32_t)(sizeof(MetaHeader) + (size_t)h * sizeof(MetaHead)) / 4;
   UnitInfo x;
   x.un = (uint32_t)u;
-  x.toff = (uint32_t)r * req_bytes + meta_dword(meta, hb);
+  x.toff = (uint64_t)r * req_bytes + meta_dword(meta, hb);
   x.sb = meta_dword(meta, hb + 2);
   x.h = (uint32_t)h;
   return x;
@@ -1267,7 +1271,7 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   if (tid < kD) L.qp[tid] = L.vin.q[L.vin.perm[tid]];
 
   // 2. exact S0 (g_t k_t), S0 (g_t q_t): digit planes of cf k and cf q, cf = fl(g_t R)
-  prep<KDA>(L.vin, L.W, w, lane, Bw);
+  prep<KDA, true>(L.vin, L.W, w, lane, Bw);
   wait_lgkm();
   __builtin_amdgcn_wave_barrier();
   long op[8];

@@ -30,8 +30,8 @@ SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize
            "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk", "qdr_dequantize_state",
            "qdr_damp_select", "qdr_damp_bytes", "qdr_damp_init", "qdr_damp_quantize", "qdr_damp_step",
            "qdr_damp_dequantize", "qdr_comp_quantize", "qdr_comp_chunk", "qdr_comp_window",
-           "qdr_comp_dequantize",
-           "qdr_last_error")
+           "qdr_comp_dequantize", "qdr_probe_copy", "qdr_probe_clock", "qdr_probe_wall_rate",
+           "qdr_probe_last_error", "qdr_last_error")
 
 
 class QdrError(RuntimeError):
@@ -86,6 +86,9 @@ def lib():
             "qdr_comp_chunk": [D, P, P, P, P, i32, P, P, i32, P, P, P, P, P, P, P],
             "qdr_comp_window": [D, P, P, P, P, i32, P, P, P, i32, P, P, P, P, P, P, P],
             "qdr_comp_dequantize": [D, P, P, P, P, i32, P, P, P, P],
+            "qdr_probe_copy": [P, P, ctypes.c_size_t, P],
+            "qdr_probe_clock": [P, i32, i32, P],
+            "qdr_probe_wall_rate": [ctypes.POINTER(ctypes.c_double)],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -93,6 +96,8 @@ def lib():
             fn.restype = ctypes.c_int
         L.qdr_last_error.argtypes = []
         L.qdr_last_error.restype = ctypes.c_char_p
+        L.qdr_probe_last_error.argtypes = []
+        L.qdr_probe_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -409,3 +414,30 @@ class DampState:
     def to_host(self):
         return (self.half.cpu().numpy().view(np.uint16), self.codes.cpu().numpy(),
                 self.R.cpu().numpy())
+
+
+# ---- measurement helpers --------------------------------------------------------------
+
+def probe_copy(src, dst, stream=None):
+    """Streaming copy of src into dst (same byte size, device tensors) on the probe kernel."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("probe_copy: src and dst differ in size")
+    rc = lib().qdr_probe_copy(_ptr(src), _ptr(dst), n, _stream(stream))
+    if rc != QDR_OK:
+        raise QdrError(rc, "qdr_probe_copy", lib().qdr_probe_last_error().decode())
+
+
+def probe_clock(out, iters: int, stream=None):
+    """Clock probe: out is a device int64 tensor [n_block, 4]."""
+    rc = lib().qdr_probe_clock(_ptr(out), int(out.shape[0]), int(iters), _stream(stream))
+    if rc != QDR_OK:
+        raise QdrError(rc, "qdr_probe_clock", lib().qdr_probe_last_error().decode())
+
+
+def probe_wall_rate() -> float:
+    hz = ctypes.c_double()
+    rc = lib().qdr_probe_wall_rate(ctypes.byref(hz))
+    if rc != QDR_OK:
+        raise QdrError(rc, "qdr_probe_wall_rate", lib().qdr_probe_last_error().decode())
+    return float(hz.value)

@@ -78,20 +78,21 @@ def to_dev(inp, device="cuda"):
     return {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in inp.items()}
 
 
-def prewarmed_state(w: wl.Workload, n_req: int, seed=0) -> np.ndarray:
+def prewarmed_state(w: wl.Workload, n_req: int, seed=0, r0: int = 0) -> np.ndarray:
     """Pre-warm reading: ``w.prewarm_steps`` steps of the unquantized fp64 recurrence from
     zero on the pre-warm input stream, then every selected key channel (column) and value
-    row scaled by 10 (oracle arithmetic only). Returns fp32 S [n_req, n_head, 128, 128]."""
+    row scaled by 10 (oracle arithmetic only), for requests [r0, r0 + n_req). Returns fp32
+    S [n_req, n_head, 128, 128]."""
     S = np.zeros((n_req, w.n_head, 128, 128), np.float64)
     for t in range(w.prewarm_steps):
-        inp = wl.prewarm_inputs(w, t, seed, n_req)
+        inp = wl.prewarm_inputs(w, t, seed, n_req, r0=r0)
         for r in range(n_req):
             for h in range(w.n_head):
                 a = inp["a"][r, h]
                 Su = S[r, h]
                 oracle.recur_fp64(Su, w.gate, inp["q"][r, h], inp["k"][r, h], inp["v"][r, h],
                                   a, inp["b"][r, h])
-    key_sel, val_sel = wl.outlier_masks(w, seed, n_req)
+    key_sel, val_sel = wl.outlier_masks(w, seed, n_req, r0=r0)
     S = S * np.where(key_sel, 10.0, 1.0)[:, :, None, :]
     S = S * np.where(val_sel, 10.0, 1.0)[:, :, :, None]
     return S.astype(np.float32)

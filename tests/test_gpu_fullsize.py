@@ -9,7 +9,7 @@ grid and persistence over the whole pool included).
   8-bit, one call of T = 64 tokens;
 * window mode, the same shape, one window of W = 64 token calls and the fold;
 * the DAMP-style variant, 1024 requests x 32 GDN heads, two steps from the initial state
-  (bit-exact: the stochastic rounding is keyed by the unit index, which the sample keeps).
+  (the stochastic rounding is keyed by the unit index, which the sample keeps).
 
 Inputs: full-size tensors drawn on the device by the seeded generator, with the sampled
 requests' slices overwritten by the host generator's values for those requests (so the
@@ -169,6 +169,7 @@ def test_damp_full_size_sampled(torch_cuda):
     o = torch.empty((w.n_req, H, 128), device="cuda")
     units = [(r * H, (r + 1) * H) for r in SAMPLE3]
     print(f"[full damp] {w.n_req}x{H} units, sample {SAMPLE3}", flush=True)
+    worst_o = 0.0
     for t in range(1, 3):
         inp = wl.step_inputs(w, t)
         dev = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in inp.items()}
@@ -179,10 +180,22 @@ def test_damp_full_size_sampled(torch_cuda):
                           u0=u0, u1=u1)
             o_ref[u0 // H] = oo[u0 // H]
         og = o.cpu().numpy()
-        assert np.array_equal(og[SAMPLE3].view(np.uint32), o_ref[SAMPLE3].view(np.uint32)), t
+        worst_o = max(worst_o, rel_l2(og[SAMPLE3], o_ref[SAMPLE3]))
     half, codes, R = gpu.to_host()
+    n_flip = n_half = n_codes = 0
+    exact = True
     for u0, u1 in units:
-        assert np.array_equal(half[u0:u1], ref.half[u0:u1])
-        assert np.array_equal(codes[u0:u1], ref.codes[u0:u1])
-        assert np.array_equal(R[u0:u1].view(np.uint32), ref.R[u0:u1].view(np.uint32))
-    print("[full damp] sampled units bit-exact after 2 steps", flush=True)
+        d = np.abs(codes[u0:u1].astype(np.int32) - ref.codes[u0:u1].astype(np.int32))
+        assert d.max() <= 1
+        n_flip += int((d > 0).sum())
+        n_codes += d.size
+        n_half += int((half[u0:u1] != ref.half[u0:u1]).sum())
+        np.testing.assert_allclose(R[u0:u1], ref.R[u0:u1], rtol=1e-6)
+        exact = exact and not d.any() and np.array_equal(R[u0:u1].view(np.uint32),
+                                                         ref.R[u0:u1].view(np.uint32))
+    exact = exact and n_half == 0
+    print(f"[full damp] worst o rel-L2 {worst_o:.2e}; codes differ on {n_flip / n_codes:.2e}, "
+          f"binary16 values on {n_half} entries; bit-exact={exact}", flush=True)
+    assert worst_o <= O_REL_L2
+    assert n_flip / n_codes <= CODE_FLIP_FRAC
+    assert n_half / n_codes <= CODE_FLIP_FRAC

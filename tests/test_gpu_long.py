@@ -1,0 +1,223 @@
+"""Parity over the configs' stated lengths, at full size, on sampled requests (GPU).
+
+Slow state drift only shows up far into a run (dev.to page, "What I'd actually measure"),
+so these tests run the configurations over their own lengths in the launches the
+benchmark times, and compare a few sampled requests (every head of each) with the oracle:
+
+* the KDA layer (256 requests x 32 heads, mixed 8/6/4-bit key channels per head): the
+  whole pool in one launch per step, so each persistent work-group walks many units of
+  mixed widths; the sampled requests start from the pre-warmed outlier states; 64 steps;
+* the serving shape (1024 requests x 32 GDN heads, mixed 8/6/4-bit heads): all 128 steps;
+* the windowed shape (256 requests x 32 KDA heads, 8-bit, W = 64): 16 windows (1024
+  tokens), in window mode (one call per token) and in chunk mode (one call per window).
+
+Each step (window) is checked teacher-forced -- the oracle stepped from the GPU's own state
+of the sampled requests -- against the bar (codes within 1 LSB on <= 1e-4 of entries, o
+rel-L2 <= 1e-4), and the free-running trajectories of the sampled requests are compared
+(dequantized-state drift <= 1e-3 rel-L2 after 256 steps or tokens, the horizon the bar is
+stated for; the windowed runs report it every 256 tokens up to 1024). Window and chunk mode
+fold in bf16 parts on the matrix cores, which moves ~1e-5 of the codes per window by one
+LSB, and a quantized recurrence carries such differences forward and grows them, as any
+two roundings of it do.
+
+Inputs: full-size device tensors from the seeded device generator, with the sampled
+requests' slices overwritten by the host generator's values for those requests, so the
+oracle reads exactly what the GPU reads.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parity_tools import (CODE_FLIP_FRAC, DRIFT_REL_L2, O_REL_L2, bits_for, compare_codes,
+                          prewarmed_state, rel_l2)
+from quantized_delta_rule_03_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_delta_rule_03_amd import qdr
+
+    qdr.lib()
+    return torch
+
+
+def sampled_state(gpu, sample, bits) -> oracle.Pool:
+    """The GPU pool's state of the sampled requests as an oracle pool."""
+    L = gpu.layout
+    packed = gpu.packed[:L.packed_bytes].view(L.n_req, L.req_bytes)[sample].cpu().numpy()
+    p = oracle.Pool(len(sample), L.n_head, bits, rule=L.rule)
+    p.packed[:] = packed
+    p.row_scale[:] = gpu.row_scale[sample].cpu().numpy()
+    p.col_scale[:] = gpu.col_scale[sample].cpu().numpy()
+    return p
+
+
+def load_sampled(gpu, ref, sample):
+    """Write the oracle pool's state into the sampled requests' slots of the GPU pool."""
+    import torch
+
+    L = gpu.layout
+    view = gpu.packed[:L.packed_bytes].view(L.n_req, L.req_bytes)
+    idx = torch.tensor(sample, device=gpu.device)
+    view[idx] = torch.from_numpy(ref.packed).to(gpu.device)
+    gpu.row_scale[idx] = torch.from_numpy(ref.row_scale).to(gpu.device)
+    gpu.col_scale[idx] = torch.from_numpy(ref.col_scale).to(gpu.device)
+
+
+def step_inputs_sampled(torch, w, t, sample, a_dev, seed=7):
+    """Full-size device inputs of step t with the sampled requests' host values."""
+    d = wl.device_step_inputs(w, t, "cuda", seed=seed)
+    d["a"] = a_dev
+    host = {k: [] for k in "qkvab"}
+    idx = torch.tensor(sample, device="cuda")
+    per = [wl.step_inputs(w, t, n_req=1, r0=r) for r in sample]
+    for k in "qkvab":
+        host[k] = np.ascontiguousarray(np.concatenate([h[k] for h in per]))
+        if k != "a":
+            d[k][idx] = torch.from_numpy(host[k]).cuda()
+    return d, host
+
+
+def run_steps(torch, w, bits, sample, steps, S0_sample=None, name=""):
+    from quantized_delta_rule_03_amd import qdr
+
+    gpu = qdr.StatePool(w.n_req, w.n_head, w.gate, bits)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    gpu.quantize(0.1 * torch.randn((w.n_req, w.n_head, 128, 128), generator=g, device="cuda"))
+    ref = oracle.Pool(len(sample), w.n_head, bits)
+    if S0_sample is None:
+        ref.quantize(np.zeros((len(sample), w.n_head, 128, 128), np.float32))
+    else:
+        ref.quantize(S0_sample)
+    load_sampled(gpu, ref, sample)
+    a_dev = torch.from_numpy(wl.static_gate(w)).cuda()
+    o = torch.empty((w.n_req, w.n_head, 128), dtype=torch.float32, device="cuda")
+    worst_o_tf = worst_o_free = worst_frac = 0.0
+    worst_lsb = 0
+    print(f"[{name}] {w.n_req}x{w.n_head} units, {steps} steps, sample {sample}", flush=True)
+    for t in range(steps):
+        dev, host = step_inputs_sampled(torch, w, t, sample, a_dev)
+        tf = sampled_state(gpu, sample, bits)
+        gpu.step(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], o)
+        og = o[torch.tensor(sample, device="cuda")].cpu().numpy()
+        args = (w.gate, host["q"], host["k"], host["v"], host["a"], host["b"])
+        o_tf = tf.step_threads(*args, threads=16)
+        after = sampled_state(gpu, sample, bits)
+        lsb, frac = compare_codes(after.packed, tf.packed, tf)
+        worst_lsb, worst_frac = max(worst_lsb, lsb), max(worst_frac, frac)
+        worst_o_tf = max(worst_o_tf, rel_l2(og, o_tf))
+        o_free = ref.step_threads(*args, threads=16)
+        worst_o_free = max(worst_o_free, rel_l2(og, o_free))
+        if (t + 1) % 16 == 0:
+            print(f"[{name}] step {t + 1}: worst o rel-L2 tf {worst_o_tf:.2e}, codes max "
+                  f"{worst_lsb} LSB on {worst_frac:.2e}", flush=True)
+    assert torch.isfinite(o).all()
+    final = sampled_state(gpu, sample, bits)
+    drift = rel_l2(final.dequantize(), ref.dequantize())
+    lsb_free, frac_free = compare_codes(final.packed, ref.packed, ref)
+    print(f"[{name}] worst o rel-L2 tf={worst_o_tf:.2e} free={worst_o_free:.2e}; teacher-forced "
+          f"codes max {worst_lsb} LSB on {worst_frac:.2e}; free-running after {steps} steps: "
+          f"drift {drift:.2e}, codes differ on {frac_free:.2e} (max {lsb_free} LSB)", flush=True)
+    assert worst_o_tf <= O_REL_L2
+    assert worst_lsb <= 1 and worst_frac <= CODE_FLIP_FRAC
+    assert drift <= DRIFT_REL_L2
+
+
+def test_kda_layer_full_size_64_steps(torch_cuda):
+    """KDA layer at full size: mixed per-channel widths take the mixed-width persistent
+    kernel over 8192 units; two sampled requests start from pre-warmed outlier states."""
+    w = wl.WORKLOADS[2]
+    bits = bits_for(w)
+    assert not all(len(set(b)) == 1 for b in bits)  # mixed widths inside the heads
+    sample = [3, 200]
+    S0 = np.concatenate([prewarmed_state(w, 1, r0=r) for r in sample])
+    run_steps(torch_cuda, w, bits, sample, 64, S0_sample=S0, name="kda layer full size")
+
+
+def test_serving_full_size_128_steps(torch_cuda):
+    """The serving shape over all 128 steps of its run, four sampled requests."""
+    w = wl.WORKLOADS[3]
+    bits = bits_for(w)
+    run_steps(torch_cuda, w, bits, [0, 333, 700, 1023], 128, name="serving 128 steps")
+
+
+def window_tokens(torch, w, t0, W, sample, a_dev, seed=7):
+    dev, host = [], []
+    for t in range(t0, t0 + W):
+        d, h = step_inputs_sampled(torch, w, t, sample, a_dev, seed)
+        dev.append(d)
+        host.append(h)
+    hs = {k: np.ascontiguousarray(np.stack([h[k] for h in host])) for k in "qkvab"}
+    return dev, hs
+
+
+@pytest.mark.parametrize("mode", ["window", "chunk"])
+def test_windowed_full_size_16_windows(torch_cuda, mode):
+    """The windowed shape over 16 windows of 64 tokens (1024 tokens), two sampled
+    requests, in window mode (a call per token, the fold at the last) and chunk mode."""
+    from quantized_delta_rule_03_amd import qdr
+
+    torch = torch_cuda
+    w = wl.WORKLOADS[4]
+    W = w.window
+    bits = bits_for(w)
+    sample = [5, 250]
+    gpu = qdr.StatePool(w.n_req, w.n_head, w.gate, bits, window=W if mode == "window" else 0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    gpu.quantize(0.1 * torch.randn((w.n_req, w.n_head, 128, 128), generator=g, device="cuda"))
+    rng = np.random.default_rng(41)
+    S0 = (0.1 * rng.standard_normal((len(sample), w.n_head, 128, 128))).astype(np.float32)
+    ref = oracle.Pool(len(sample), w.n_head, bits)
+    ref.quantize(S0)
+    load_sampled(gpu, ref, sample)
+    a_dev = torch.from_numpy(wl.static_gate(w)).cuda()
+    idx = torch.tensor(sample, device="cuda")
+    worst_o = worst_frac = 0.0
+    worst_lsb = 0
+    drifts = []
+    n_win = 16
+    print(f"[windowed {mode}] {w.n_req}x{w.n_head} units, {n_win} windows of {W}, "
+          f"sample {sample}", flush=True)
+    for win in range(n_win):
+        dev, host = window_tokens(torch, w, win * W, W, sample, a_dev)
+        tf = sampled_state(gpu, sample, bits)
+        args = (w.gate, host["q"], host["k"], host["v"], host["a"], host["b"])
+        o_tf = tf.window_threads(*args, threads=16)
+        ref.window_threads(*args, threads=16)
+        if mode == "window":
+            o = torch.empty((w.n_req, w.n_head, 128), dtype=torch.float32, device="cuda")
+            og = []
+            for t in range(W):
+                d = dev[t]
+                gpu.window_token(t, d["q"], d["k"], d["v"], d["a"], d["b"], o)
+                og.append(o[idx].cpu().numpy())
+            og = np.stack(og)
+        else:
+            x = {k: torch.stack([d[k] for d in dev]).contiguous() for k in "qkvab"}
+            o = torch.empty((W, w.n_req, w.n_head, 128), dtype=torch.float32, device="cuda")
+            gpu.chunk(x["q"], x["k"], x["v"], x["a"], x["b"], o)
+            og = o[:, idx].cpu().numpy()
+            del x
+        worst_o = max(worst_o, max(rel_l2(og[t], o_tf[t]) for t in range(W)))
+        after = sampled_state(gpu, sample, bits)
+        lsb, frac = compare_codes(after.packed, tf.packed, tf)
+        worst_lsb, worst_frac = max(worst_lsb, lsb), max(worst_frac, frac)
+        if (win + 1) % 4 == 0:
+            drift = rel_l2(after.dequantize(), ref.dequantize())
+            drifts.append(drift)
+            print(f"[windowed {mode}] window {win + 1}: worst o rel-L2 tf {worst_o:.2e}, codes "
+                  f"max {worst_lsb} LSB on {worst_frac:.2e}; free-running drift after "
+                  f"{(win + 1) * W} tokens {drift:.2e}", flush=True)
+    assert worst_o <= O_REL_L2
+    assert worst_lsb <= 1 and worst_frac <= CODE_FLIP_FRAC
+    # the drift bar is stated for 256 tokens; beyond it the free-running pair keeps
+    # diverging as any two roundings of a quantized recurrence do (reported above)
+    assert drifts[0] <= DRIFT_REL_L2

@@ -231,6 +231,33 @@ def test_mixed_width_heads_and_special_inputs(torch_cuda):
     assert traj.worst_flip_tf <= CODE_FLIP_FRAC
 
 
+def test_gdn_heads_with_mixed_channel_widths(torch_cuda):
+    """GDN gate on heads whose key channels have mixed widths (a per-channel bit map): the
+    physical key order of such a head is not the logical one, so the step must read k, q
+    through the head's position map, as quantize and dequantize do."""
+    rng = np.random.default_rng(23)
+    n_head, n_req = 4, 3
+    bits = oracle.assign_bits(1, np.exp(rng.uniform(0, 9, (n_head, 128))), 128)
+    S0 = rng.standard_normal((n_req, n_head, 128, 128)).astype(np.float32)
+    gpu = make_pool(n_req, n_head, 0, bits)
+    ref = oracle.Pool(n_req, n_head, bits)
+    ref.quantize(S0)
+    gpu.load_host(ref.packed, ref.row_scale, ref.col_scale)
+    traj = Trajectory(gpu, ref, 0)
+    for t in range(8):
+        k = rng.standard_normal((n_req, n_head, 128))
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q = rng.standard_normal((n_req, n_head, 128))
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        inp = {"q": q.astype(np.float32), "k": k.astype(np.float32),
+               "v": rng.standard_normal((n_req, n_head, 128)).astype(np.float32),
+               "a": rng.uniform(0.5, 1, (n_req, n_head)).astype(np.float32),
+               "b": rng.uniform(0, 1, (n_req, n_head)).astype(np.float32)}
+        traj.step(inp)
+    report("gdn, mixed channel widths", traj)
+    assert_bar(traj)
+
+
 def test_sparse_and_tiny_keys_and_queries(torch_cuda):
     """Keys and queries with whole zero segments, single nonzero positions and values down
     to fp32 subnormals next to normal ones in one segment: the per-segment fixed-point
