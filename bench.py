@@ -37,6 +37,7 @@ VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 PROFILE = os.path.join(ROOT, "profiles", "k_step_gdn_serving_1024x32.md")
 PROFILE_CHUNK = os.path.join(ROOT, "profiles", "k_chunk_kda_256x32_t64.md")
 PROFILE_COMP = os.path.join(ROOT, "profiles", "k_chunk_comp16_kda_256x32_t64.md")
+CLOCK_TRACE_PERIOD_S = 10e-6  # clock-trace sample spacing beside the timed launches
 COMP_TOKENS = 16  # compensator tokens per unit in the --workload comp line
 
 
@@ -159,12 +160,22 @@ def chunk_algorithmic_bytes(tile_bytes: int, n_unit: int, T: int, m: int = 0) ->
     return per_unit * n_unit
 
 
-def chunk_mfma_flops(n_unit: int, T: int) -> float:
-    """Matrix-core FLOPs of one chunk call as the kernel schedules them: per unit and
-    16-token sub-block, 624 v_mfma_f32_16x16x32_bf16 (S_r(gam k) and S_r(gam q): 96 per wave,
-    the wave's Gram partials: 12, the state update: 48; each 16x16x32x2 FLOPs, the six bf16
-    part products of the three-way operand split counted as issued) and 32
-    v_mfma_f32_16x16x4_f32 (readouts, 16x16x4x2 FLOPs each)."""
+def chunk_method_flops(n_unit: int, T: int) -> float:
+    """The matrix products the chunked form of the method needs per call, counted once (2
+    FLOPs per multiply-add): per unit and sub-block of C = 16 tokens, S_r(gam k) and
+    S_r(gam q) (2 x 128 x 128 x C), the two C x C Gram matrices over the 128 key channels,
+    the readout term B delta (C x C x 128) and the state update S += sum_t delta_t k_t^T
+    (128 x 128 x C)."""
+    n_sub = -(-T // 16)
+    C = 16
+    per_sub = 2 * (2 * 128 * 128 * C + 2 * C * C * 128 + C * C * 128 + 128 * 128 * C)
+    return float(n_unit) * n_sub * per_sub
+
+
+def chunk_issued_flops(n_unit: int, T: int) -> float:
+    """Matrix-core FLOPs as the kernel issues them: per unit and 16-token sub-block, 624
+    v_mfma_f32_16x16x32_bf16 (each fp32 operand split into three bf16 parts, six part
+    products per operand pair) and 32 v_mfma_f32_16x16x4_f32."""
     n_sub = -(-T // 16)
     return float(n_unit) * n_sub * (624 * 16 * 16 * 32 * 2 + 32 * 16 * 16 * 4 * 2)
 
@@ -225,9 +236,12 @@ def bench_chunk(args, torch, qdr, wl, dev, m=0):
         f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
     prof = profile_record(PROFILE_COMP if m else PROFILE_CHUNK)
     traffic = float(prof["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in prof else None
-    flops = chunk_mfma_flops(n_unit, T)
-    mfma = {"flops_per_call": flops, "achieved": flops / chunk_s, "peak": BF16_MFMA_PEAK,
-            "unit": "FLOP/s", "frac": flops / chunk_s / BF16_MFMA_PEAK}
+    flops = chunk_method_flops(n_unit, T)
+    issued = chunk_issued_flops(n_unit, T)
+    mfma = {"method_flops_per_call": flops, "achieved": flops / chunk_s,
+            "peak": BF16_MFMA_PEAK, "unit": "FLOP/s", "frac": flops / chunk_s / BF16_MFMA_PEAK,
+            "issued_flops_per_call": issued,
+            "issued_frac": issued / chunk_s / BF16_MFMA_PEAK}
     valu = None
     if "SQ_INSTS_VALU" in prof:
         lane_ops = float(prof["SQ_INSTS_VALU"]) * 64
@@ -303,6 +317,69 @@ def bench_compare(args, torch, qdr, wl, dev):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name + " (rules)", "n_req": w.n_req, "n_head": w.n_head},
         "rules": rules,
+    }
+
+
+def bench_layers(args, torch, qdr, wl, dev):
+    """The decode step on the two layer configurations: the GDN layer (64 requests x 32
+    heads, 8/6/4-bit heads, from the zero state) and the KDA layer (256 requests x 32
+    heads, 8/6/4-bit key channels per head, from a seeded Gaussian state with outlier rows
+    and columns: the timing does not depend on the values). Their working sets (58.7 MB
+    and 239 MB) fit the 256 MB last-level cache, so these lines are flagged cache-resident
+    (the GDN one is also close to launch-bound): not HBM measurements."""
+    out = []
+    for wid in (1, 2):
+        w = wl.WORKLOADS[wid]
+        bits = qdr.assign_bits(w.gate, wl.halflives(w, args.seed))
+        pool = qdr.StatePool(w.n_req, w.n_head, w.gate, bits, device=dev)
+        if wid == 2:
+            g = torch.Generator(device=dev)
+            g.manual_seed(args.seed)
+            S0 = torch.randn((w.n_req, w.n_head, 128, 128), generator=g, device=dev)
+            S0[:, :, :, ::97] *= 10.0
+            S0[:, :, ::89, :] *= 10.0
+            pool.quantize(S0)
+            del S0
+        a = torch.from_numpy(wl.static_gate(w, args.seed)).to(dev)
+        n_in = 8
+        inputs = [wl.device_step_inputs(w, t, dev, args.seed) for t in range(n_in)]
+        o = torch.empty((w.n_req, w.n_head, 128), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+        for t in range(max(3, args.warmup)):
+            x = inputs[t % n_in]
+            pool.step(x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
+        torch.cuda.synchronize()
+        steps = max(20, args.steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            x = inputs[i % n_in]
+            ev[i][0].record(stream)
+            pool.step(x["q"], x["k"], x["v"], a, x["b"], o, stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        us = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev])) * 1e3
+        nbytes = algorithmic_bytes(pool.layout, w.n_unit, w.gate)
+        gbps = nbytes / (us / 1e6) / 1e9
+        log(f"{w.name}: {us:.1f} us per step (kernel), {wall * 1e6 / steps:.1f} us wall; "
+            f"{gbps:.0f} GB/s algorithmic (cache-resident working set {nbytes / 1e6:.1f} MB)")
+        out.append({"workload": w.name, "n_req": w.n_req, "n_head": w.n_head,
+                    "units": w.n_unit, "us_per_step_kernel": us,
+                    "us_per_step_wall": wall * 1e6 / steps,
+                    "state_updates_per_s": w.n_unit / (wall / steps),
+                    "gbps_algorithmic": gbps, "bytes_per_step": nbytes,
+                    "cache_resident": True, "steps": steps})
+        del pool, inputs
+    return {
+        "metric": "decode-step time on the GDN and KDA layer configurations (cache-resident)",
+        "value": out[0]["state_updates_per_s"], "unit": "state-updates/s (GDN layer)",
+        "n_gpus": 1, "steps": out[0]["steps"], "warmup": max(3, args.warmup),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gdn_32h_b64_mixed + kda_32h_b256_mixed_prewarm (layers)"},
+        "layers": out,
     }
 
 
@@ -410,10 +487,12 @@ def cpu_baselines(w, bits, args):
     return many
 
 
-def probe_clock_mhz(torch, qdr, dev, iters=40000):
-    """Engine clock sustained under full VALU load (8 work-groups per CU of a dependent
-    fp32 fma chain): shader-clock cycles over constant-rate ticks."""
-    n_block = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+def probe_clock_mhz(torch, qdr, dev, iters=40000, n_block=None):
+    """Engine clock: shader-clock cycles over constant-rate ticks while work-groups run a
+    dependent fp32 fma chain. Default: 8 work-groups per CU (full VALU load); n_block=1
+    samples the clock the chip is running at (one CU, about 15 us)."""
+    if n_block is None:
+        n_block = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
     out = torch.zeros((n_block, 4), dtype=torch.int64, device=dev)
     qdr.probe_clock(out, iters)
     torch.cuda.synchronize()
@@ -421,7 +500,23 @@ def probe_clock_mhz(torch, qdr, dev, iters=40000):
     return float(o[:, 0].sum() / o[:, 1].sum() * qdr.probe_wall_rate() / 1e6)
 
 
-def probe_copy_gbps(torch, qdr, dev, nbytes: int, reps: int = 10):
+def clock_trace_summary(tr, wall_hz: float, kern_s: float) -> dict:
+    """Engine clock from a clock trace ([n][2]: shader-clock counter, constant-rate
+    counter): over the whole trace, its first and last fifth, and the lowest 0.5 ms
+    window; coverage = trace span over the summed timed launch durations."""
+    cyc = np.diff(tr[:, 0].astype(np.float64))
+    tick = np.diff(tr[:, 1].astype(np.float64))
+    mhz = lambda c, t: float(c.sum() / t.sum() * wall_hz / 1e6)
+    n = len(cyc)
+    f = max(1, n // 5)
+    win = max(1, int(round(0.5e-3 * wall_hz / max(1.0, float(np.median(tick))))))
+    lows = [mhz(cyc[i:i + win], tick[i:i + win]) for i in range(0, max(1, n - win + 1), win)]
+    return {"mean": mhz(cyc, tick), "first_fifth": mhz(cyc[:f], tick[:f]),
+            "last_fifth": mhz(cyc[-f:], tick[-f:]), "min_0p5ms": min(lows),
+            "coverage": float(tick.sum() / wall_hz / kern_s), "samples": n + 1}
+
+
+def probe_copy_gbps(torch, qdr, dev, nbytes: int, reps: int = 20):
     """Achievable HBM read+write bandwidth: a streaming copy of nbytes (read nbytes, write
     nbytes) on the probe kernel, mean over reps timed copies after two untimed ones."""
     n = (nbytes // 16) * 4
@@ -458,13 +553,14 @@ def main():
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the clock and copy-bandwidth probes")
     ap.add_argument("--workload",
-                    choices=["serving", "window", "chunk", "comp", "compare", "damp"],
+                    choices=["serving", "window", "chunk", "comp", "compare", "damp", "layers"],
                     default="serving",
                     help="serving: the decode-step metric (default); window: window mode "
                          "(one call per token); chunk: chunk mode (one call per window); "
                          "comp: chunk mode with compensator tokens; "
                          "compare: the decode step under each scale rule; damp: the "
-                         "DAMP-style storage variant")
+                         "DAMP-style storage variant; layers: the GDN and KDA layer "
+                         "configurations (cache-resident working sets)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode step has "
@@ -494,6 +590,9 @@ def main():
     if args.workload == "damp":
         print(json.dumps(bench_damp(args, torch, qdr, wl, dev)), flush=True)
         return
+    if args.workload == "layers":
+        print(json.dumps(bench_layers(args, torch, qdr, wl, dev)), flush=True)
+        return
     w = wl.WORKLOADS[3]
     bits = qdr.assign_bits(w.gate, wl.halflives(w, args.seed))
     pool = qdr.StatePool(w.n_req, w.n_head, w.gate, bits, device=dev)
@@ -510,15 +609,33 @@ def main():
     def launch(inp):
         pool.step(inp["q"], inp["k"], inp["v"], a, inp["b"], o, stream=stream)
 
-    clock_before = None if args.no_probes else probe_clock_mhz(torch, qdr, dev, iters=10000)
+    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.warmup)]
     for t in range(args.warmup):
+        wev[t][0].record(stream)
         launch(inputs[t])
+        wev[t][1].record(stream)
     torch.cuda.synchronize()
+    warm_us = [s_.elapsed_time(e_) * 1e3 for s_, e_ in wev]
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    trace = mon = None
+    if not args.no_probes:
+        # the engine clock while the timed steps run: one sampling wave on a second stream
+        # (it fits beside the step's three work-groups per CU and sleeps between samples),
+        # sized to end within the timed region even if every timed launch is as fast as the
+        # fastest warm-up launch
+        wall_hz = qdr.probe_wall_rate()
+        period = max(1, int(round(wall_hz * CLOCK_TRACE_PERIOD_S)))
+        est_us = min(warm_us) if warm_us else 200.0
+        n_sample = max(2, min(1 << 20, int(0.8 * est_us * args.steps * 1e-6 * wall_hz / period)))
+        trace = torch.zeros((n_sample, 2), dtype=torch.int64, device=dev)
+        mon = torch.cuda.Stream(device=dev)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
+    if trace is not None:
+        qdr.probe_clock_trace(trace, period, mon)
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
@@ -536,15 +653,22 @@ def main():
         f"{achieved:.0f} GB/s algorithmic ({100*achieved/HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
     probes = None
     if not args.no_probes:
-        clock_after = probe_clock_mhz(torch, qdr, dev)
+        clock = clock_trace_summary(trace.cpu().numpy(), wall_hz, float(kern_ms.sum()) / 1e3)
+        if clock["coverage"] > 1.0:
+            log("warning: the clock trace outlasted the timed launches; wall time includes it")
+        # the remaining probes run after the timed region, so they cannot change it
+        clock_load = probe_clock_mhz(torch, qdr, dev)
         del inputs
         copy_gbps = probe_copy_gbps(torch, qdr, dev, nbytes // 2)
         probes = {"copy_gbps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
                   "copy_bytes_each_way": (nbytes // 2 // 16) * 16,
-                  "clock_mhz_before_warmup": clock_before, "clock_mhz_after": clock_after}
+                  "clock_mhz_timed": clock, "clock_mhz_full_valu_load": clock_load,
+                  "warmup_launch_us": [round(x, 1) for x in warm_us]}
         log(f"probes: streaming copy {copy_gbps:.0f} GB/s (step at {100*achieved/copy_gbps:.1f}% "
-            f"of it); engine clock {clock_before:.0f} MHz before warm-up, {clock_after:.0f} MHz "
-            f"after the timed steps")
+            f"of it); engine clock during the timed steps {clock['mean']:.0f} MHz (first "
+            f"fifth {clock['first_fifth']:.0f}, last fifth {clock['last_fifth']:.0f}, lowest "
+            f"0.5 ms {clock['min_0p5ms']:.0f}) over {100*clock['coverage']:.0f}% of the timed "
+            f"kernel time; {clock_load:.0f} MHz under full VALU load")
 
     prof = profile_record()
     traffic = float(prof["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in prof else None

@@ -33,7 +33,13 @@
  *    the calling thread) except qdr_desc.bits and the host arrays of qdr_assign_bits /
  *    qdr_state_bytes, which are HOST pointers. Device arrays must be 16-byte aligned
  *    and contiguous in the stated layout. The caller owns every buffer and the stream;
- *    the library allocates, frees and synchronizes nothing on these paths.
+ *    the library allocates and frees nothing. Only qdr_init_state and qdr_damp_init
+ *    synchronize (the stream, once, after copying their small host-built metadata
+ *    table); every other call only enqueues work.
+ *  - Host cost per call: the descriptor's bit map is validated and summarised once and
+ *    the summary kept (the last 8 distinct maps, compared in full on every call, so an
+ *    edited map is never taken for a cached one); a decode call with a known map does no
+ *    per-head work and no heap allocation on the host.
  *  - stream: a hipStream_t passed as void* (NULL = the null stream). All device work
  *    is enqueued asynchronously on it in call order.
  *  - Non-finite inputs are undefined behaviour and are not checked.
@@ -102,7 +108,11 @@ typedef struct qdr_desc {
 int qdr_assign_bits(int32_t gate, int32_t n_head, int32_t dk, const double *halflife,
                     uint8_t *bits_out);
 
-/* Sizes of the caller-owned buffers for a descriptor (HOST outputs, any may be NULL):
+/* Sizes of the caller-owned buffers for a descriptor (HOST outputs, any may be NULL).
+ * The state is kept as per-request packed pages (freedom251 page, section "Memory and
+ * speed gains are implementation-specific"), and its footprint counts the codes, the
+ * scales and the precision map (the same page's checklist under "How to decide for a
+ * deployment"):
  *   packed  -- n_req * req_bytes bytes (codes)
  *   scales  -- bytes of ONE of row_scale / col_scale (n_req*n_head*128*4)
  *   meta    -- bytes of the device metadata table written by qdr_init_state
@@ -111,9 +121,11 @@ int qdr_assign_bits(int32_t gate, int32_t n_head, int32_t dk, const double *half
 int qdr_state_bytes(const qdr_desc *desc, size_t *packed, size_t *scales, size_t *meta,
                     size_t *window_buf);
 
-/* Initialise: write the metadata table (per-head tile offsets, segment widths and the
- * physical key order) and the zero state (every code 0, R_j = 1/Qmax_j, c_i = 1),
- * i.e. the state that qdr_quantize_state gives for S = 0. Errors: all codes. */
+/* Initialise: write the metadata table -- the precision map as the kernels read it
+ * (per-head tile offsets, segment widths and the physical key order; freedom251 page,
+ * checklist under "How to decide for a deployment") -- and the zero state (every code 0,
+ * R_j = 1/Qmax_j, c_i = 1), i.e. the state that qdr_quantize_state gives for S = 0.
+ * Copies the table from the host and synchronizes `stream` once. Errors: all codes. */
 int qdr_init_state(const qdr_desc *desc, void *packed, float *row_scale, float *col_scale,
                    void *meta, void *stream);
 
@@ -221,7 +233,9 @@ int qdr_comp_dequantize(const qdr_desc *desc, const void *meta, const void *pack
                         void *stream);
 
 /* Read back the dequantized state S_hat_ij = fl(code_ij * fl(R_j*c_i)) as
- * S_out [n_req][n_head][dv][dk] (logical key order). Errors: all codes. */
+ * S_out [n_req][n_head][dv][dk] (logical key order): the state the STEPQuant abstract's
+ * key-row and value-column scales represent, each code times its entry's step. For
+ * checking and inspection; not on the decode path. Errors: all codes. */
 int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *packed,
                          const float *row_scale, const float *col_scale, float *S_out,
                          void *stream);
@@ -241,8 +255,9 @@ int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *pac
  * S_new = fma(w_i, k_j, S'_ij); then binary16 (round to nearest even) for the selected
  * channels and, for the others, A_j = max_i |S_ij| (1 if 0), R_j = fl(A_j/127),
  * y = fl(S fl(1/A_j)), code = clamp(floor(y*127 + u), +-127) evaluated in fp64 with u the
- * top 24 bits (times 2^-24) of word position%4 of Philox4x32-10 (Salmon et al., SC11) for
- * counter (row*32 + position/4, unit, step low, step high) and key (seed low, seed high);
+ * byte position%16 (little-endian across the four words, times 2^-8) of Philox4x32-10
+ * (Salmon et al., SC11) for counter (row*8 + position/16, unit, step low, step high) and
+ * key (seed low, seed high), i.e. one generator block per 16 codes of a row;
  * unit = request*n_head + head. The caller passes a fresh step per call. Errors: as for
  * the main format; QDR_EUNSUPPORTED if a head does not select exactly 16 channels. */
 typedef struct qdr_damp_desc {
@@ -258,7 +273,8 @@ typedef struct qdr_damp_desc {
 int qdr_damp_select(int32_t gate, int32_t n_head, const double *halflife, uint8_t *sel_out);
 int qdr_damp_bytes(const qdr_damp_desc *desc, size_t *half, size_t *codes, size_t *scales,
                    size_t *meta);
-/* write meta and the zero state (codes 0, binary16 zeros, R = 1/127); synchronizes once */
+/* write meta and the zero state (codes 0, binary16 zeros, R = 1/127); copies the position
+ * map from the host and synchronizes `stream` once */
 int qdr_damp_init(const qdr_damp_desc *desc, void *meta, void *half, void *codes, float *R,
                   void *stream);
 /* quantize a caller fp32 state S [n_req][n_head][128][128] (logical key order) */
@@ -289,13 +305,26 @@ int qdr_damp_dequantize(const qdr_damp_desc *desc, const void *meta, const void 
  * [n_block][4] uint64, caller-owned). Sum(out[4b]) / Sum(out[4b+1]) * qdr_probe_wall_rate
  * is the engine clock sustained under full VALU load. Errors: QDR_EINVAL, QDR_EHIP.
  *
+ * qdr_probe_clock_trace: one wave that, on `stream`, writes n_sample pairs out[2i] =
+ * shader-clock counter, out[2i+1] = constant-rate counter, sample i taken at the first
+ * reading at least i*period constant-rate ticks after its start (it sleeps in between, so
+ * it can run on a second stream beside the kernels being timed; it holds one wave and
+ * under 16 registers, and ends after n_sample*period ticks whatever else runs). The
+ * difference of two samples' first words over that of their second words times
+ * qdr_probe_wall_rate is the engine clock over that interval. out: device [n_sample][2]
+ * uint64, caller-owned; 1 <= n_sample <= 2^20, 1 <= period <= 2^24.
+ * Errors: QDR_EINVAL, QDR_EHIP.
+ *
  * qdr_probe_wall_rate: HOST output, the constant-rate counter's frequency in Hz. */
 int qdr_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 int qdr_probe_clock(unsigned long long *out, int32_t n_block, int32_t iters, void *stream);
+int qdr_probe_clock_trace(unsigned long long *out, int32_t n_sample, int32_t period,
+                          void *stream);
 int qdr_probe_wall_rate(double *hz);
 const char *qdr_probe_last_error(void);
 
-/* Text of the last error on the calling thread ("" if none). Never NULL. */
+/* Text of the last error on the calling thread ("" if none), set by every entry point
+ * that returns a negative code. Never NULL. */
 const char *qdr_last_error(void);
 
 #ifdef __cplusplus

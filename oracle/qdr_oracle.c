@@ -772,16 +772,18 @@ float oref_f16_to_f32(uint16_t h) {
     return (float)(sign ? -v : v);
 }
 
-/* uniform in [0, 1) for state entry (i, p) of a unit at a step: the top 24 bits of word
- * p mod 4 of the Philox block for the counter (i*32 + p/4, unit, step low, step high),
- * key = seed (one block serves four consecutive positions of a row) */
+/* uniform in [0, 1) for state entry (i, p) of a unit at a step: byte p mod 16 (little-endian
+ * across the four words) of the Philox block for the counter (i*8 + p/16, unit, step low,
+ * step high), key = seed, times 2^-8 (one block serves sixteen consecutive positions of a
+ * row) */
 static double damp_uniform(uint64_t seed, uint32_t unit, uint64_t step, int i, int p) {
-    const uint32_t ctr[4] = {(uint32_t)(i * 32 + p / 4), unit, (uint32_t)step,
+    const uint32_t ctr[4] = {(uint32_t)(i * 8 + p / 16), unit, (uint32_t)step,
                              (uint32_t)(step >> 32)};
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     uint32_t out[4];
     oref_philox4x32_10(ctr, key, out);
-    return ldexp((double)(out[p % 4] >> 8), -24);
+    const uint32_t byte = (out[(p / 4) % 4] >> (8 * (p % 4))) & 0xFFu;
+    return ldexp((double)byte, -8);
 }
 
 int oref_damp_perm(int dk, const uint8_t *sel, uint8_t *perm) {

@@ -198,8 +198,8 @@ int oref_comp_window_pool(int n_req, int n_head, int dv, int dk, int gate, const
  *   requantize   selected: binary16 round-to-nearest-even; others: A_j = max_i |S_ij|
  *                (1 if 0), R_j = fl(A_j/127), y = fl(S * fl(1/A_j)),
  *                code = clamp(floor(y*127 + u), +-127) in fp64, u = uniform [0, 1):
- *                the top 24 bits of word p mod 4 of Philox4x32-10 for counter
- *                (i*32 + p/4, unit, step lo, step hi) and key seed. */
+ *                byte p mod 16 (little-endian over the four words) of Philox4x32-10 for
+ *                counter (i*8 + p/16, unit, step lo, step hi) and key seed, times 2^-8. */
 #define OREF_DAMP_HALF 16
 
 void oref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);

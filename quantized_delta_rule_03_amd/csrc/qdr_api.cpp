@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -12,6 +13,12 @@
 #include "qdr_internal.h"
 
 namespace {
+
+#define CHECK(expr)        \
+  do {                     \
+    int rc_ = (expr);      \
+    if (rc_) return rc_;   \
+  } while (0)
 
 thread_local std::string g_err;
 
@@ -74,7 +81,7 @@ struct Geometry {
   int n_class[3] = {0, 0, 0};
 };
 
-int check_desc(const qdr_desc* d, Geometry* g) {
+int check_scalars(const qdr_desc* d) {
   if (!d) return fail(QDR_EINVAL, "desc is NULL");
   if (d->n_req < 0) return fail(QDR_EINVAL, "n_req = %d < 0", d->n_req);
   if (d->n_head < 1 || d->n_head > 1024)
@@ -90,6 +97,11 @@ int check_desc(const qdr_desc* d, Geometry* g) {
     return fail(QDR_EINVAL, "rule = %d is not a QDR_RULE_* value", d->rule);
   if ((long long)d->n_req * d->n_head > (1LL << 31) - 1)
     return fail(QDR_EINVAL, "n_req * n_head overflows");
+  return QDR_OK;
+}
+
+int check_desc(const qdr_desc* d, Geometry* g) {
+  CHECK(check_scalars(d));
   if (g) {
     g->heads.resize(d->n_head);
     g->off.resize(d->n_head);
@@ -120,6 +132,54 @@ int check_desc(const qdr_desc* d, Geometry* g) {
   return QDR_OK;
 }
 
+// What the launches need from a bit map: the request stride and the width classes.
+struct Summary {
+  uint32_t req_bytes = 0;
+  bool uniform = true;
+  int n_class[3] = {0, 0, 0};
+};
+
+// Summaries of the last few validated bit maps. A call whose bit map equals a cached one
+// (compared in full, so an edited map is never mistaken for a cached one) skips the
+// per-head layout pass and allocates nothing; a miss validates the map, summarises it
+// and replaces the oldest entry.
+struct CacheEntry {
+  int32_t n_head = 0;
+  std::vector<uint8_t> bits;
+  Summary sum;
+};
+constexpr int kCacheEntries = 8;
+std::mutex g_cache_mu;
+CacheEntry g_cache[kCacheEntries];
+int g_cache_next = 0;
+
+int check_desc_summary(const qdr_desc* d, Summary* out) {
+  CHECK(check_scalars(d));
+  const size_t nb = (size_t)d->n_head * qdr::kD;
+  {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (const CacheEntry& e : g_cache)
+      if (e.n_head == d->n_head && memcmp(e.bits.data(), d->bits, nb) == 0) {
+        *out = e.sum;
+        return QDR_OK;
+      }
+  }
+  Geometry g;
+  CHECK(check_desc(d, &g));
+  Summary sm;
+  sm.req_bytes = g.req_bytes;
+  sm.uniform = g.uniform;
+  for (int c = 0; c < 3; ++c) sm.n_class[c] = g.n_class[c];
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  CacheEntry& e = g_cache[g_cache_next];
+  g_cache_next = (g_cache_next + 1) % kCacheEntries;
+  e.n_head = d->n_head;
+  e.bits.assign(d->bits, d->bits + nb);
+  e.sum = sm;
+  *out = sm;
+  return QDR_OK;
+}
+
 int check_ptr(const void* p, const char* name, bool required) {
   if (!p) return required ? fail(QDR_EINVAL, "%s is NULL", name) : QDR_OK;
   if (reinterpret_cast<uintptr_t>(p) & 15u)
@@ -127,13 +187,7 @@ int check_ptr(const void* p, const char* name, bool required) {
   return QDR_OK;
 }
 
-#define CHECK(expr)        \
-  do {                     \
-    int rc_ = (expr);      \
-    if (rc_) return rc_;   \
-  } while (0)
-
-qdr::Pool pool_of(const qdr_desc* d, const void* meta, const Geometry& g) {
+qdr::Pool pool_of(const qdr_desc* d, const void* meta, const Summary& g) {
   qdr::Pool p;
   p.meta = meta;
   p.n_head = d->n_head;
@@ -189,8 +243,8 @@ int qdr_assign_bits(int32_t gate, int32_t n_head, int32_t dk, const double* half
 
 int qdr_state_bytes(const qdr_desc* d, size_t* packed, size_t* scales, size_t* meta,
                     size_t* window_buf) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   const size_t n_unit = (size_t)d->n_req * d->n_head;
   if (packed) *packed = (size_t)d->n_req * g.req_bytes;
   if (scales) *scales = n_unit * qdr::kD * sizeof(float);
@@ -238,15 +292,19 @@ int qdr_init_state(const qdr_desc* d, void* packed, float* row_scale, float* col
   hipError_t e = hipMemcpyAsync(meta, host.data(), host.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_status(e, "qdr_init_state: metadata copy");
-  return hip_status(qdr::launch_init(pool_of(d, meta, g), static_cast<uint8_t*>(packed),
+  Summary sm;
+  sm.req_bytes = g.req_bytes;
+  sm.uniform = g.uniform;
+  for (int c = 0; c < 3; ++c) sm.n_class[c] = g.n_class[c];
+  return hip_status(qdr::launch_init(pool_of(d, meta, sm), static_cast<uint8_t*>(packed),
                                      row_scale, col_scale, s),
                     "qdr_init_state: launch");
 }
 
 int qdr_quantize_state(const qdr_desc* d, const void* meta, const float* S, void* packed,
                        float* row_scale, float* col_scale, void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   const bool any = d->n_req > 0;
   CHECK(check_ptr(meta, "meta", true));
   CHECK(check_ptr(S, "S", any));
@@ -261,8 +319,8 @@ int qdr_quantize_state(const qdr_desc* d, const void* meta, const float* S, void
 int qdr_dequantize_state(const qdr_desc* d, const void* meta, const void* packed,
                          const float* row_scale, const float* col_scale, float* S_out,
                          void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   const bool any = d->n_req > 0;
   CHECK(check_ptr(meta, "meta", true));
   CHECK(check_ptr(packed, "packed", any));
@@ -278,8 +336,8 @@ int qdr_dequantize_state(const qdr_desc* d, const void* meta, const void* packed
 int qdr_decode_step(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
                     float* col_scale, const float* q, const float* k, const float* v,
                     const float* a, const float* b, float* o, void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   const bool any = d->n_req > 0;
   CHECK(check_ptr(meta, "meta", true));
   CHECK(check_ptr(packed, "packed", any));
@@ -301,8 +359,8 @@ int qdr_decode_window(const qdr_desc* d, const void* meta, void* packed, float* 
                       float* col_scale, void* window_buf, int32_t t, const float* q,
                       const float* k, const float* v, const float* a, const float* b,
                       float* o, void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   if (d->window < 1) return fail(QDR_EUNSUPPORTED, "desc->window = %d: no window mode", d->window);
   if (d->rule != QDR_RULE_STEP)
     return fail(QDR_EUNSUPPORTED, "window mode takes only QDR_RULE_STEP (rule = %d)", d->rule);
@@ -332,8 +390,8 @@ int qdr_decode_window(const qdr_desc* d, const void* meta, void* packed, float* 
 int qdr_decode_chunk(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
                      float* col_scale, int32_t T, const float* q, const float* k, const float* v,
                      const float* a, const float* b, float* o, void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   if (T < 0) return fail(QDR_EINVAL, "T = %d is negative", T);
   if (d->rule != QDR_RULE_STEP)
     return fail(QDR_EUNSUPPORTED, "chunk mode takes only QDR_RULE_STEP (rule = %d)", d->rule);
@@ -372,8 +430,8 @@ static int check_comp(const qdr_desc* d, int32_t m, bool any, const void* tok_id
 int qdr_comp_quantize(const qdr_desc* d, const void* meta, void* packed, float* row_scale,
                       float* col_scale, int32_t m, uint16_t* tok_idx, float* tok_val,
                       const float* S_in, void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   const bool any = d->n_req > 0;
   CHECK(check_comp(d, m, any, tok_idx, tok_val));
   CHECK(check_ptr(meta, "meta", true));
@@ -393,8 +451,8 @@ int qdr_comp_chunk(const qdr_desc* d, const void* meta, void* packed, float* row
                    float* col_scale, int32_t m, uint16_t* tok_idx, float* tok_val, int32_t T,
                    const float* q, const float* k, const float* v, const float* a,
                    const float* b, float* o, void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   if (T < 0) return fail(QDR_EINVAL, "T = %d is negative", T);
   const bool any = d->n_req > 0 && T > 0;
   CHECK(check_comp(d, m, any, tok_idx, tok_val));
@@ -419,8 +477,8 @@ int qdr_comp_window(const qdr_desc* d, const void* meta, void* packed, float* ro
                     float* col_scale, int32_t m, uint16_t* tok_idx, float* tok_val,
                     void* window_buf, int32_t t, const float* q, const float* k, const float* v,
                     const float* a, const float* b, float* o, void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   if (d->window < 1) return fail(QDR_EUNSUPPORTED, "desc->window = %d: no window mode", d->window);
   if (d->window > qdr::kWindowMax)
     return fail(QDR_EUNSUPPORTED, "desc->window = %d exceeds %d", d->window, qdr::kWindowMax);
@@ -450,8 +508,8 @@ int qdr_comp_dequantize(const qdr_desc* d, const void* meta, const void* packed,
                         const float* row_scale, const float* col_scale, int32_t m,
                         const uint16_t* tok_idx, const float* tok_val, float* S_out,
                         void* stream) {
-  Geometry g;
-  CHECK(check_desc(d, &g));
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
   const bool any = d->n_req > 0;
   CHECK(check_comp(d, m, any, tok_idx, tok_val));
   CHECK(check_ptr(meta, "meta", true));

@@ -6,17 +6,20 @@
 // 0..15), codes[128 rows][112] int8 (the other channels, positions 16..127), R[112] fp32
 // (one range per key row). perm[h][p] is the logical key channel at physical position p.
 //
-// Arithmetic contract (shared with the scalar reference, bit for bit):
+// Arithmetic (the scalar reference's, except for the order of the fp64 dot products):
 //   gate + dequantize  S'_ip = fl(f32(h_ip) * g_p) (p < 16), fl(code_ip * fl(g_p * R_p))
-//   u_i                fl32(s0 + s1), s0 and s1 the fp64 sums of S'_ip k_p over positions
-//                      0..63 and 64..127, each in position order
+//   u_i                fl32 of the fp64 sum of S'_ip k_p; each product is exact in fp64,
+//                      summed here as two half sums (positions 0..63 and 64..127, each in
+//                      position order) added, where the reference takes one sum in key
+//                      channel order: the fp32 results can differ on rare rounding ties
 //   delta / update     w_i = fl(b fl(v_i - u_i)), S_new = fma(w_i, k_p, S'_ip)
 //   readout            o_i from S_new and q as u_i from S' and k
 //   requantize         p < 16: binary16, round to nearest even; p >= 16: A_p = max_i
 //                      |S_ip| (1 if 0), R_p = fl(A_p/127), y = fl(S * fl(1/A_p)),
-//                      code = clamp(floor(y*127 + u), +-127) in fp64, u in [0, 1) = top 24
-//                      bits of word p%4 of the Philox4x32-10 block for the counter
-//                      (i*32 + p/4, unit, step lo, step hi) and key (seed lo, seed hi).
+//                      code = clamp(floor(y*127 + u), +-127) in fp64, u in [0, 1) = byte
+//                      p%16 (little-endian over the words) of the Philox4x32-10 block for
+//                      the counter (i*8 + p/16, unit, step lo, step hi) and key (seed lo,
+//                      seed hi), times 2^-8.
 //
 // Work decomposition: one work-group of 256 threads per unit. Thread t holds value row
 // t >> 1 at the 64 positions of half t & 1 in registers (the fp64 half sums of the
@@ -126,15 +129,14 @@ __device__ __forceinline__ int8_t* code_word(int8_t* crow, int seg, int q) {
   return crow + (seg ? 48 + 16 * q : 16 * (q - 1));
 }
 
-// floor(127 y + r 2^-24) clamped to [-127, 127]. Scaled by 2^24 it is
-// floor(127 2^24 y + r) >> 24 (floor of a floor quotient), and 127 2^24 y + r is one fp64
-// fma with the same single rounding as the unscaled fp64 sum (exact for |y| >= 2^-23; no
-// integer is crossed below that); y is clamped to [-1, 1] first, which leaves the clamped
-// result unchanged and keeps the floor inside int32. sr_scaled returns the scaled floor;
-// the code is its top byte (>> 24).
-__device__ __forceinline__ int sr_scaled(float y, uint32_t r24) {
+// floor(127 y + r 2^-8) clamped to [-127, 127], r the row's random byte. Scaled by 2^8 it is
+// floor(127 2^8 y + r) >> 8 (floor of a floor quotient), and 127 2^8 y + r is exact in
+// fp64 (at most 31 significant bits), as is the unscaled sum; y is clamped to [-1, 1]
+// first, which leaves the clamped result unchanged and keeps the floor inside int32.
+// sr_scaled returns the scaled floor; the code is its second byte (>> 8).
+__device__ __forceinline__ int sr_scaled(float y, uint32_t r8) {
   const float yc = fminf(fmaxf(y, -1.0f), 1.0f);
-  return (int)floor(fma((double)yc, 2130706432.0, (double)r24));  // 127 * 2^24
+  return (int)floor(fma((double)yc, 32512.0, (double)r8));  // 127 * 2^8
 }
 
 // ranges and requantization of the register-held half rows, stored in place
@@ -172,42 +174,35 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
     dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
   }
-  // the row's 112 INT8 positions split 56/56 over the pair: half 0 takes 16..71 (64..71
-  // from its partner's registers), half 1 takes 72..127; 14 Philox blocks each
-  float x[8];
+  // The row's 112 INT8 positions in Philox blocks of 16 (one block per 16 positions):
+  // half 0 takes blocks 1-4 (positions 16..79; 64..79 from its partner's registers), half 1
+  // blocks 5-7 (80..127). Each block's codes are packed and stored as 16 bytes.
+  float x[16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = __shfl_xor(Sr[e], 1);
-  const int base = seg ? 72 : kH;
-  uint32_t wd[14];
-#pragma unroll
-  for (int b = 0; b < 14; ++b) {
-    const uint4 r = philox4x32_10((uint32_t)(i * 32 + base / 4 + b), (uint32_t)u, s0, s1, k0, k1);
-    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-    // the codes are the top bytes of the scaled floors: byte selects pack four
-    uint32_t t[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 4 * b + e;  // position base + j
-      const float sv = seg ? Sr[8 + j] : (j < 48 ? Sr[16 + j] : x[j - 48]);
-      const float y = sv * L.invA[base + j];
-      t[e] = (uint32_t)sr_scaled(y, rw[e] >> 8);
-    }
-    wd[b] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(t[3], t[2], 0x0C0C0703u),
-                                  __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0703u), 0x05040100u);
-  }
+  for (int e = 0; e < 16; ++e) x[e] = __shfl_xor(Sr[e], 1);
   int8_t* crow = A.codes + ((size_t)u * kD + i) * kI;
-  if (seg == 0) {
-    uint4* d = reinterpret_cast<uint4*>(crow);
-    d[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    d[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
-    d[2] = make_uint4(wd[8], wd[9], wd[10], wd[11]);
-    *reinterpret_cast<uint2*>(crow + 48) = make_uint2(wd[12], wd[13]);
-  } else {
-    *reinterpret_cast<uint2*>(crow + 56) = make_uint2(wd[0], wd[1]);
-    uint4* d = reinterpret_cast<uint4*>(crow + 64);
-    d[0] = make_uint4(wd[2], wd[3], wd[4], wd[5]);
-    d[1] = make_uint4(wd[6], wd[7], wd[8], wd[9]);
-    d[2] = make_uint4(wd[10], wd[11], wd[12], wd[13]);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (seg == 1 && b == 3) break;  // half 1 has three blocks
+    const int blk = seg ? 5 + b : 1 + b;  // positions 16 blk .. 16 blk + 15
+    const uint4 r = philox4x32_10((uint32_t)(i * 8 + blk), (uint32_t)u, s0, s1, k0, k1);
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+    uint32_t wd[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // the codes are the second bytes of the scaled floors: byte selects pack four
+      uint32_t t[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * q + e;  // position 16 blk + j
+        const float sv = seg ? Sr[16 * b + 16 + j] : (b < 3 ? Sr[16 * b + 16 + j] : x[j]);
+        const float y = sv * L.invA[16 * blk + j];
+        t[e] = (uint32_t)sr_scaled(y, (rw[q] >> (8 * e)) & 0xFFu);
+      }
+      wd[q] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(t[3], t[2], 0x0C0C0501u),
+                                    __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0501u), 0x05040100u);
+    }
+    *reinterpret_cast<uint4*>(crow + 16 * (blk - 1)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
 }
 

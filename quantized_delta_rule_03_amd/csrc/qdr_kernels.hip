@@ -45,6 +45,37 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// 1/x, correctly rounded (the IEEE division): for x in [2^-126, 2^126) the hardware
+// reciprocal followed by one Newton step r = y + y(1 - xy) (two fmas) is exactly that --
+// checked on the GPU against the division for every fp32 pattern of that range; for
+// subnormal x, or x whose reciprocal is subnormal, the division itself runs (such
+// scales are rare, so the lanes almost never take that branch).
+__device__ __forceinline__ float recip_rn(float x) {
+  const float y = __builtin_amdgcn_rcpf(x);
+  const float e = fmaf(-x, y, 1.0f);
+  float r = fmaf(e, y, y);
+  if (__builtin_amdgcn_ballot_w64(!(x >= 0x1p-126f && x < 0x1p126f))) {
+    // a branch the wave skips when no lane needs it (the empty volatile asm keeps the
+    // compiler from evaluating the division unconditionally)
+    float xx = x;
+    asm volatile("" : "+v"(xx));
+    if (!(xx >= 0x1p-126f && xx < 0x1p126f)) r = 1.0f / xx;
+  }
+  return r;
+}
+
+// a / Qmax for Qmax = 2^(b-1) - 1 (b in {4, 6, 8}), correctly rounded: the product with
+// fl(1/Qmax) and one remainder correction, q = q0 + fl(1/Qmax)(a - q0 Qmax) (two fmas,
+// the remainder exact) -- equal to the IEEE division for every positive fp32 a and each
+// of the three Qmax (checked on the GPU over every fp32 pattern).
+__device__ __forceinline__ float div_qmax(float a, int b) {
+  const float q = b == 8 ? 127.0f : (b == 6 ? 31.0f : 7.0f);
+  const float iq = b == 8 ? 1.0f / 127.0f : (b == 6 ? 1.0f / 31.0f : 1.0f / 7.0f);
+  const float q0 = a * iq;
+  const float r = fmaf(-q0, q, a);
+  return fmaf(r, iq, q0);
+}
+
 struct Seg {
   int bits;
   uint32_t off;  // byte offset of the segment inside the tile
@@ -243,8 +274,8 @@ __device__ __forceinline__ void key_row_refit(const float (&s)[8][8], int rg, in
   // lanes rg and rg + 8 hold the same value for position p0 + (rg & 7); both store it
   const float Am = __uint_as_float(sel);
   const float A = (Am == 0.0f) ? 1.0f : Am;
-  Rs_u[p0 + (rg & 7)] = A / (float)((1 << (B - 1)) - 1);
-  invA_lds[p0 + (rg & 7)] = 1.0f / A;
+  Rs_u[p0 + (rg & 7)] = div_qmax(A, B);
+  invA_lds[p0 + (rg & 7)] = recip_rn(A);
 }
 
 // y = s * invA in place; per-row partial value-column absmax written to cpart.
@@ -341,8 +372,8 @@ __global__ void __launch_bounds__(kThreads) k_quantize(const void* meta, int n_h
     const float Aa = (Am == 0.0f) ? 1.0f : Am;
     if (threadIdx.x < kD) {
       const int p = threadIdx.x;
-      Rs[uo + p] = Aa / (float)((1 << (mh->seg_bits[p >> 5] - 1)) - 1);
-      L.invA[p] = 1.0f / Aa;
+      Rs[uo + p] = div_qmax(Aa, mh->seg_bits[p >> 5]);
+      L.invA[p] = recip_rn(Aa);
     }
   } else {
     key_row_refit(s, rg, p0, sg.bits, Rs + uo, L.invA);
@@ -357,7 +388,7 @@ __global__ void __launch_bounds__(kThreads) k_quantize(const void* meta, int n_h
       for (int g = 0; g < 16; ++g) cm = fmaxf(cm, L.cpart[g * kD + i]);
     if (cm == 0.0f) cm = 1.0f;
     Cs[uo + i] = cm;
-    L.invc[i] = 1.0f / cm;
+    L.invc[i] = recip_rn(cm);
   }
   __syncthreads();
   const float qmax = (float)((1 << (sg.bits - 1)) - 1);
@@ -553,70 +584,63 @@ __device__ __forceinline__ int operand_byte(int B, int m) {
   return B == 4 ? ((m & 1) ? 4 + (m >> 1) : (m >> 1)) : (B == 6 && !(m & 2) ? m ^ 1 : m);
 }
 
-// One lane's share of the next unit, held in registers until it is written to LDS.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) u32x4* gu32x4_ptr;
 typedef const __attribute__((address_space(1))) float* gf32_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// One lane's share of the next unit, held in registers until it is written to LDS.
-struct Prefetch {
-  u32x4 t0, t1, t2, t3;  // tile segment: 16 bytes of each 1 KB chunk
-  u32x4 vec;             // 16 bytes of an input vector (or of the KDA position map)
-  float sc;              // wave 3: lane 0 b, lane 1 the GDN gate
-};
-
-// Every wave issues the same instruction sequence; which arrays a wave and lane read
-// is chosen by address arithmetic and lane masks, not by branches on the wave index
-// (branches would merge the pending-load state of the prefetch registers at their
-// joins and force early waits):
-//   wave 0: k (lanes 0-31), q (32-63)    wave 1: v, R
-//   wave 2: C, a (KDA only)              wave 3: position map (lanes 0-7); b, a (GDN)
-// The position map (physical position -> key channel) is read by KDA and by the
-// mixed-width kernel (B == 0), whose heads may order their channels by width; a head of
-// a single width keeps the logical order.
-__device__ __forceinline__ bool vec_lane_active(int gate, bool perm, int w, int lane) {
-  return w < 2 || (w == 2 && (gate == KDA || lane < 32)) || (w == 3 && perm && lane < 8);
+// Loads straight from HBM into LDS (gfx950 LDS-direct global loads): lane l's `size`
+// bytes from its own address land at lds + l * size. No register holds the data; the
+// wave's vmcnt counts the load until it has landed.
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds, 4, 0, 0);
 }
 
-template <int GATE, int B>
-__device__ __forceinline__ void issue_prefetch(const StepArgs& A, const UnitInfo& u, int w, int lane,
-                                               Prefetch& f) {
+// The next unit's tile segment of wave w, 1 KB per wave-wide load, into the LDS tile
+// slot. Only wave w reads segment w of the slot, so a wave may start this as soon as its
+// own reads of the current segment are done -- except with mixed widths (B == 0), where
+// the next unit's segments may sit at other offsets than the current unit's, which
+// other waves may still be reading.
+template <int B>
+__device__ __forceinline__ void issue_tile(const StepArgs& A, const UnitInfo& u, int w, int lane,
+                                           uint8_t* tile) {
   const Seg sg = seg_from(u.sb, w);
   const int nchunk = (B ? B : sg.bits) >> 1;  // 512 * bits bytes in 1 KB chunks
-  const u32x4* src = reinterpret_cast<const u32x4*>(A.packed + u.toff + sg.off) + lane;
-  f.t0 = src[0];
-  f.t1 = src[64];
-  if (nchunk > 2) f.t2 = src[128];
-  if (nchunk > 3) f.t3 = src[192];
-  const uintptr_t pk = (uintptr_t)A.k, pq = (uintptr_t)A.q, pv = (uintptr_t)A.v;
-  const uintptr_t pr = (uintptr_t)A.Rs, pc = (uintptr_t)A.Cs, pa = (uintptr_t)A.a;
-  const uintptr_t pm = (uintptr_t)meta_heads(A.meta)[u.h].perm;
-  const uintptr_t lo = w == 0 ? pk : (w == 1 ? pv : (w == 2 ? pc : pm));
-  const uintptr_t hi = w == 0 ? pq : (w == 1 ? pr : (w == 2 ? pa : pm));
-  const uintptr_t off = w == 3 ? (uintptr_t)lane * 16
-                               : ((uintptr_t)u.un * kD + (uintptr_t)(lane & 31) * 4) * 4;
-  const uintptr_t base = lane >= 32 ? hi : lo;
-  if (vec_lane_active(GATE, GATE == KDA || B == 0, w, lane)) f.vec = *(gu32x4_ptr)(base + off);
-  if (w == 3 && lane < (GATE == GDN ? 2 : 1))
-    f.sc = *(gf32_ptr)((lane ? pa : (uintptr_t)A.b) + (uintptr_t)u.un * 4);
+  const uint8_t* src = A.packed + u.toff + sg.off + 16 * lane;
+  uint8_t* dst = tile + sg.off;
+  lds_load16(src, dst);
+  lds_load16(src + 1024, dst + 1024);
+  if (nchunk > 2) lds_load16(src + 2048, dst + 2048);
+  if (nchunk > 3) lds_load16(src + 3072, dst + 3072);
 }
 
-// Write a prefetched share to the LDS slot.
+// The next unit's input vectors into the LDS slot (once every wave has finished reading
+// the current ones). Wave w < 3 brings two consecutive VecIn arrays, lanes 0-31 the first
+// and 32-63 the second, 16 bytes each:
+//   wave 0: k, q      wave 1: v, R      wave 2: C, a (KDA only)
+//   wave 3: the position map (lanes 0-7) where the kernel reads it -- KDA, and mixed
+//           widths (B == 0), whose heads may order their channels by width (a head of a
+//           single width keeps the logical order) -- and, from lane 0, b and the GDN gate.
 template <int GATE, int B>
-__device__ __forceinline__ void commit_prefetch(const UnitInfo& u, int w, int lane, const Prefetch& f,
-                                                uint8_t* tile, VecIn& vin) {
-  const Seg sg = seg_from(u.sb, w);
-  const int nchunk = (B ? B : sg.bits) >> 1;
-  u32x4* dst = reinterpret_cast<u32x4*>(tile + sg.off) + lane;
-  dst[0] = f.t0;
-  dst[64] = f.t1;
-  if (nchunk > 2) dst[128] = f.t2;
-  if (nchunk > 3) dst[192] = f.t3;
-  // lanes 32-63 of waves 0-2 land in the array after the first one (q, R, a)
-  float* vdst = w == 0 ? vin.k : (w == 1 ? vin.v : (w == 2 ? vin.C : reinterpret_cast<float*>(vin.perm)));
-  if (vec_lane_active(GATE, GATE == KDA || B == 0, w, lane))
-    reinterpret_cast<u32x4*>(vdst)[lane] = f.vec;
-  if (w == 3 && lane < (GATE == GDN ? 2 : 1)) (&vin.b)[lane] = f.sc;
+__device__ __forceinline__ void issue_vectors(const StepArgs& A, const UnitInfo& u, int w, int lane,
+                                              VecIn& vin) {
+  constexpr bool PERM = GATE == KDA || B == 0;
+  if (w < 3) {
+    const float* first = w == 0 ? A.k : (w == 1 ? A.v : A.Cs);
+    const float* second = w == 0 ? A.q : (w == 1 ? A.Rs : A.a);
+    const float* src = (lane < 32 ? first : second) + (size_t)u.un * kD + 4 * (lane & 31);
+    if (w < 2 || GATE == KDA || lane < 32)
+      lds_load16(src, reinterpret_cast<float*>(&vin) + 2 * kD * w);
+  } else {
+    if (PERM && lane < 8) lds_load16(meta_heads(A.meta)[u.h].perm + 16 * lane, vin.perm);
+    if (lane == 0) {
+      lds_load4(A.b + u.un, &vin.b);
+      if (GATE == GDN) lds_load4(A.a + u.un, &vin.ag);
+    }
+  }
 }
 
 // max over the 32 lanes of one half of the wave
@@ -912,13 +936,14 @@ __device__ __forceinline__ float key_row_refit_rs(const float (&s)[8][8], int rg
   const float Am = __uint_as_float(b2 ? z[1] : z[0]);
   const float A = (Am == 0.0f) ? 1.0f : Am;
   const bool rlane = rg < 8;
-  const float r = (rlane ? A : 1.0f) / (rlane ? (float)((1 << (B - 1)) - 1) : A);
+  const float r = rlane ? div_qmax(A, B) : recip_rn(A);
   if (!rlane) invA_lds[p0 + pos] = r;
   return r;
 }
 
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07Fu); }
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 __device__ __forceinline__ void block_sync() {
   wait_lgkm();
   __builtin_amdgcn_s_barrier();
@@ -944,14 +969,14 @@ __device__ __forceinline__ void block_sync() {
   } while (0)
 
 // One unit. `odd` alternates the two waves that form the value-column scales. RULE is the
-// scale rule of the requantization (the comparison baselines keep c = 1).
+// scale rule of the requantization (the comparison baselines keep c = 1). `more`: there
+// is a next unit `nx`, whose tile and input vectors are brought into LDS during this one.
 template <int GATE, int B, int RULE>
 __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecIn& vin, StepWork& W,
-                                          const UnitInfo& cur, const UnitInfo& nx, int odd) {
+                                          const UnitInfo& cur, const UnitInfo& nx, bool more,
+                                          int odd) {
   const int tid = threadIdx.x;
   const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
-  Prefetch f;
-  issue_prefetch<GATE, B>(A, nx, w, lane, f);  // past the last unit: the current one again
   const Seg sg = seg_from(cur.sb, w);
   const int Bw = B ? B : sg.bits;
   const int p0 = 32 * w + 8 * jg;
@@ -964,7 +989,9 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   // 1. code operands and digit-plane sums (matrix cores)
   long op[8];
   QDR_WIDTH_DISPATCH(B, Bw, (plane_sums<BB>(W, W.part.upart, tile + sg.off, w, rg, jg, op)));
+  if (B != 0 && more) issue_tile<B>(A, nx, w, lane, tile);  // own segment read: reuse it
   block_sync();  // B1
+  if (B == 0 && more) issue_tile<B>(A, nx, w, lane, tile);  // every wave is past its reads
 
   // 2. per row: prediction u and delta w (waves 0-1), readout sum (waves 2-3)
   {
@@ -991,9 +1018,9 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
   // the latency-bound prep, matrix-core and scale phases). Measured: 4-5% per step.
   __builtin_amdgcn_s_setprio(1);
 
-  // 3. the next unit's inputs to LDS (every wave is past its last read of the slot);
-  //    readout; dequantize + gate + update; key-row refit inside the wave; normalise
-  commit_prefetch<GATE, B>(nx, w, lane, f, tile, vin);
+  // 3. the next unit's input vectors into LDS (every wave is past its last read of the
+  //    slot); readout; dequantize + gate + update; key-row refit inside the wave; normalise
+  if (more) issue_vectors<GATE, B>(A, nx, w, lane, vin);
   if (tid >= kD) {
     const int i = tid - kD;
     const double kq = ((W.kq[0] + W.kq[1]) + W.kq[2]) + W.kq[3];
@@ -1015,8 +1042,8 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
     block_sync();
     const float Am = __uint_as_float(max(max(W.tmax[0], W.tmax[1]), max(W.tmax[2], W.tmax[3])));
     const float Aa = (Am == 0.0f) ? 1.0f : Am;
-    const float ia = 1.0f / Aa;
-    Rkeep = Aa / (float)((1 << (Bw - 1)) - 1);
+    const float ia = recip_rn(Aa);
+    Rkeep = div_qmax(Aa, Bw);
     rpos = rg & 7;
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr)
@@ -1051,9 +1078,12 @@ __device__ __forceinline__ void step_unit(const StepArgs& A, uint8_t* tile, VecI
       for (int g = 0; g < 16; ++g) cm = fmaxf(cm, W.part.cpart[g * kFS + i]);
       if (cm == 0.0f) cm = 1.0f;
       // one width for the whole tile: M = fl(Qmax fl(1/c_i)) once per row here
-      W.invc[i] = B ? (float)((1 << (B - 1)) - 1) * (1.0f / cm) : 1.0f / cm;
+      W.invc[i] = B ? (float)((1 << (B - 1)) - 1) * recip_rn(cm) : recip_rn(cm);
     }
   }
+  // the next unit's input vectors, written by every wave, must have landed before the
+  // barrier that precedes their first reads
+  wait_vm();
   block_sync();  // B4
 
   // 5. requantize and store in place; scales
@@ -1072,11 +1102,18 @@ template <int GATE, int B, int RULE>
 __device__ __forceinline__ void step_run(const StepArgs& A, uint8_t* tile, VecIn& vin, StepWork& W,
                                          UnitIter it, int count) {
   UnitInfo cur = unit_info(A, it);
+  {
+    const int w = wave_id(), lane = threadIdx.x & 63;
+    issue_tile<B>(A, cur, w, lane, tile);
+    issue_vectors<GATE, B>(A, cur, w, lane, vin);
+    wait_vm();
+    block_sync();
+  }
   for (int n = 0; n < count; ++n) {
     advance(it);
-    const bool nx = n + 1 < count;
-    const UnitInfo u1 = nx ? unit_info(A, it) : cur;
-    step_unit<GATE, B, RULE>(A, tile, vin, W, cur, u1, n & 1);
+    const bool more = n + 1 < count;
+    const UnitInfo u1 = more ? unit_info(A, it) : cur;
+    step_unit<GATE, B, RULE>(A, tile, vin, W, cur, u1, more, n & 1);
     cur = u1;
   }
 }
@@ -1087,7 +1124,6 @@ k_step(StepArgs A) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileMax];
   __shared__ __attribute__((aligned(16))) VecIn vin;
   __shared__ __attribute__((aligned(16))) StepWork W;
-  const int lane = threadIdx.x & 63;
   // Work split. Uniform heads: the groups are partitioned among the width classes in
   // proportion to their units, and each group takes a contiguous run of its class
   // (one specialised loop per group). Otherwise: contiguous runs of all units.
@@ -1127,13 +1163,6 @@ k_step(StepArgs A) {
   if (k_begin >= k_end) return;  // uniform across the group
   it.r = k_begin / it.nc;
   it.hi = k_begin - it.r * it.nc;
-  {
-    const UnitInfo u0 = unit_info(A, it);
-    Prefetch f;
-    issue_prefetch<GATE, 0>(A, u0, wave_id(), lane, f);
-    commit_prefetch<GATE, 0>(u0, wave_id(), lane, f, tile, vin);
-    block_sync();
-  }
   const int count = k_end - k_begin;
   if constexpr (UNIFORM) {
     if (cls == 0) step_run<GATE, 8, RULE>(A, tile, vin, W, it, count);
@@ -1820,7 +1849,7 @@ k_window_fold(WinArgs A) {
 #pragma unroll
     for (int g = 0; g < 16; ++g) cm = fmaxf(cm, L.cpart[g * kFS + tid]);
     if (cm == 0.0f) cm = 1.0f;
-    L.invc[tid] = 1.0f / cm;
+    L.invc[tid] = recip_rn(cm);
   }
   __syncthreads();
   const float qmax = (float)((1 << (Bw - 1)) - 1);
@@ -2328,8 +2357,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     const float Am = fmaxf(fmaxf(kmax[p], kmax[kD + p]), fmaxf(kmax[2 * kD + p], kmax[3 * kD + p]));
     const float Aa = (Am == 0.0f) ? 1.0f : Am;
     const int bits = (int)((cur.sb >> (8 * (p >> 5))) & 0xFFu);
-    A.Rs[uo + p] = Aa / (float)((1 << (bits - 1)) - 1);
-    invA[p] = 1.0f / Aa;
+    A.Rs[uo + p] = div_qmax(Aa, bits);
+    invA[p] = recip_rn(Aa);
   }
   block_sync();
 #pragma unroll
@@ -2351,7 +2380,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     float cm = fmaxf(fmaxf(cpart[i], cpart[kD + i]), fmaxf(cpart[2 * kD + i], cpart[3 * kD + i]));
     if (cm == 0.0f) cm = 1.0f;
     A.Cs[uo + i] = cm;
-    invc[i] = 1.0f / cm;
+    invc[i] = recip_rn(cm);
   }
   block_sync();
 #pragma unroll

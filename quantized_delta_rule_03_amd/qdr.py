@@ -27,10 +27,12 @@ KDA = 1
 RULE_STEP, RULE_KEYROW, RULE_TENSOR = 0, 1, 2  # scale rules (QDR_RULE_*)
 
 SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize_state",
-           "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk", "qdr_dequantize_state",
+           "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk",
+           "qdr_dequantize_state",
            "qdr_damp_select", "qdr_damp_bytes", "qdr_damp_init", "qdr_damp_quantize", "qdr_damp_step",
            "qdr_damp_dequantize", "qdr_comp_quantize", "qdr_comp_chunk", "qdr_comp_window",
-           "qdr_comp_dequantize", "qdr_probe_copy", "qdr_probe_clock", "qdr_probe_wall_rate",
+           "qdr_comp_dequantize", "qdr_probe_copy", "qdr_probe_clock", "qdr_probe_clock_trace",
+           "qdr_probe_wall_rate",
            "qdr_probe_last_error", "qdr_last_error")
 
 
@@ -88,6 +90,7 @@ def lib():
             "qdr_comp_dequantize": [D, P, P, P, P, i32, P, P, P, P],
             "qdr_probe_copy": [P, P, ctypes.c_size_t, P],
             "qdr_probe_clock": [P, i32, i32, P],
+            "qdr_probe_clock_trace": [P, i32, i32, P],
             "qdr_probe_wall_rate": [ctypes.POINTER(ctypes.c_double)],
         }
         for name, args in sigs.items():
@@ -433,6 +436,14 @@ def probe_clock(out, iters: int, stream=None):
     rc = lib().qdr_probe_clock(_ptr(out), int(out.shape[0]), int(iters), _stream(stream))
     if rc != QDR_OK:
         raise QdrError(rc, "qdr_probe_clock", lib().qdr_probe_last_error().decode())
+
+
+def probe_clock_trace(out, period: int, stream=None):
+    """Clock trace: out is a device int64 tensor [n_sample, 2]; one sample every `period`
+    ticks of the constant-rate counter."""
+    rc = lib().qdr_probe_clock_trace(_ptr(out), int(out.shape[0]), int(period), _stream(stream))
+    if rc:
+        raise QdrError(rc, "qdr_probe_clock_trace", lib().qdr_probe_last_error().decode())
 
 
 def probe_wall_rate() -> float:

@@ -239,3 +239,29 @@ def test_errors_are_thread_local():
     t.join()
     assert seen["text"] == ""
     assert qdr.last_error() != ""
+
+
+def test_bit_map_summaries_are_never_stale():
+    """The ABI caches the summary of each validated bit map; a map edited in place (same
+    pointer) must be validated afresh, both when it turns invalid and when it changes the
+    sizes."""
+    lib = qdr.lib()
+    bits = np.full((4, 128), 8, np.uint8)
+    d, _ = _desc(n_req=3, n_head=4, bits=bits)
+    sz = [ctypes.c_size_t() for _ in range(4)]
+    assert lib.qdr_state_bytes(ctypes.byref(d), *[ctypes.byref(x) for x in sz]) == 0
+    assert sz[0].value == 3 * 4 * 16384
+    bits[1, :] = 4  # same pointer, other widths: head 1 now takes 8 KB
+    assert lib.qdr_state_bytes(ctypes.byref(d), *[ctypes.byref(x) for x in sz]) == 0
+    assert sz[0].value == 3 * (3 * 16384 + 8192)
+    bits[2, 5] = 5  # invalid width
+    assert lib.qdr_state_bytes(ctypes.byref(d), *[ctypes.byref(x) for x in sz]) == qdr.QDR_EUNSUPPORTED
+    bits[2, 5] = 8
+    assert lib.qdr_state_bytes(ctypes.byref(d), *[ctypes.byref(x) for x in sz]) == 0
+    # many distinct maps in turn (more than the cache holds), each sized correctly
+    for k in range(20):
+        b = np.full((2, 128), 8, np.uint8)
+        b[k % 2, : 32 * (1 + k % 3)] = 4
+        dk_, _ = _desc(n_req=1, n_head=2, bits=b)
+        assert lib.qdr_state_bytes(ctypes.byref(dk_), *[ctypes.byref(x) for x in sz]) == 0
+        assert sz[0].value == 16 * int(b.astype(np.int64).sum())

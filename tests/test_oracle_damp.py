@@ -138,10 +138,11 @@ def test_rounding_depends_on_seed_unit_and_step_only():
 
 
 def test_rounding_uses_the_documented_counter():
-    """Each INT8 code is floor(y*127 + u) with u the top 24 bits of word p mod 4 of the
-    Philox block for counter (i*32 + p/4, unit, step low, step high) and key seed (the
-    generator itself is pinned by its known answers above); checked entry by entry on a
-    unit past the first and a step above 2^32."""
+    """Each INT8 code is floor(y*127 + u) with u byte p mod 16 (little-endian across the
+    four words) of the Philox block for counter (i*8 + p/16, unit, step low, step high)
+    and key seed, times 2^-8 (the generator itself is pinned by its known answers above);
+    checked entry by entry on a unit past the first and a step above 2^32, at positions
+    that cover every word and byte of a block and the first and last block of a row."""
     n_req, H = 2, 2
     sel = sel_flags(H, 13)
     rng = np.random.default_rng(14)
@@ -149,16 +150,18 @@ def test_rounding_uses_the_documented_counter():
     seed, step = 0x0123456789ABCDEF, (5 << 32) + 77
     p = oracle.DampPool(n_req, H, sel, seed=seed)
     p.quantize(S, step=step)
-    for u, i, pos in [(3, 0, 16), (3, 5, 17), (3, 127, 127), (2, 64, 90), (1, 9, 40), (3, 33, 66)]:
+    cases = [(3, 0, 16), (3, 5, 17), (3, 127, 127), (2, 64, 90), (1, 9, 40), (3, 33, 66)]
+    cases += [(1, 7, pos) for pos in range(16, 32)] + [(2, 100, pos) for pos in range(112, 128)]
+    for u, i, pos in cases:
         r, h = divmod(u, H)
         j = int(p.perm[h][pos])
         col = S[r, h][:, j]
         A = np.abs(col).max()
         y = np.float32(col[i]) * (np.float32(1.0) / np.float32(A))
-        ctr = [i * 32 + pos // 4, u, step & 0xFFFFFFFF, step >> 32]
+        ctr = [i * 8 + pos // 16, u, step & 0xFFFFFFFF, step >> 32]
         key = [seed & 0xFFFFFFFF, seed >> 32]
-        word = int(oracle.philox4x32_10(ctr, key)[pos % 4])
-        uu = (word >> 8) / float(1 << 24)
+        word = int(oracle.philox4x32_10(ctr, key)[(pos // 4) % 4])
+        uu = ((word >> (8 * (pos % 4))) & 0xFF) / 256.0
         want = int(np.clip(np.floor(float(y) * 127.0 + uu), -127, 127))
         assert int(p.codes[u, i, pos - 16]) == want, (u, i, pos)
 
