@@ -37,6 +37,7 @@ VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 PROFILE = os.path.join(ROOT, "profiles", "k_step_gdn_serving_1024x32.md")
 PROFILE_CHUNK = os.path.join(ROOT, "profiles", "k_chunk_kda_256x32_t64.md")
 PROFILE_COMP = os.path.join(ROOT, "profiles", "k_chunk_comp16_kda_256x32_t64.md")
+PROFILE_WINDOW = os.path.join(ROOT, "profiles", "k_window_kda_256x32_w64.md")
 CLOCK_TRACE_PERIOD_S = 10e-6  # clock-trace sample spacing beside the timed launches
 COMP_TOKENS = 16  # compensator tokens per unit in the --workload comp line
 
@@ -133,6 +134,9 @@ def bench_window(args, torch, qdr, wl, dev):
     tokens = n_win * W
     log(f"window: {win_s * 1e6 / W:.1f} us per token (fold included); {achieved:.0f} GB/s "
         f"algorithmic ({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    # HBM bytes per window (W token dispatches and the fold) from the committed counters
+    prof = profile_record(PROFILE_WINDOW)
+    traffic = float(prof["traffic_bytes_per_call"]) if "traffic_bytes_per_call" in prof else None
     return {
         "metric": "token-updates/s (req x head), window mode W=64, 256-req KDA 8-bit",
         "value": n_unit * tokens / wall,
@@ -144,7 +148,7 @@ def bench_window(args, torch, qdr, wl, dev):
                    "dv": 128, "gate": "KDA per-channel, half-life log-uniform [1, 8192]",
                    "bits": "8 (uniform)", "window": W, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_window_token<KDA> + k_window_fold<KDA>",
                      "bytes_per_window": nbytes, "avg_window_us": win_s * 1e6},
         "cpu_baseline": None,

@@ -69,12 +69,16 @@ def main():
     ap.add_argument("--title", default="k_step, serving workload")
     ap.add_argument("--bench-log", default=None,
                     help="stderr of the traced bench run: its [bench] lines are quoted")
+    ap.add_argument("--per-call", default=None,
+                    help="kernel-name fragment whose dispatches mark one call of a multi-kernel "
+                         "sequence (e.g. the fold ending each window): traffic is then also "
+                         "given per call, all matched dispatches' bytes over that count")
     args = ap.parse_args()
     global KERNELS
     KERNELS = tuple(args.kernels.split(","))
     d = args.dir
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    label = KERNELS[0].rstrip("<")
+    label = " + ".join(k.rstrip("<") for k in KERNELS)
 
     lines = [f"# {args.title}", "", "Commands (run from the repository root):", ""]
     lines += [f"    {c}" for c in args.cmd]
@@ -109,6 +113,11 @@ def main():
         return
     fetch = counters(os.path.join(d, "fetch_counter_collection.csv"), is_step)["FETCH_SIZE"]
     write = counters(os.path.join(d, "write_counter_collection.csv"), is_step)["WRITE_SIZE"]
+    per_call = None
+    if args.per_call:
+        marks = lambda n: args.per_call in n
+        n_calls = len(counters(os.path.join(d, "fetch_counter_collection.csv"), marks)["FETCH_SIZE"])
+        per_call = (n_calls, sum(fetch), sum(write))
     cf = counters(os.path.join(d, "cfetch_counter_collection.csv"), is_copy)["FETCH_SIZE"]
     cw = counters(os.path.join(d, "cwrite_counter_collection.csv"), is_copy)["WRITE_SIZE"]
     f_fetch = args.copy_bytes / (statistics.mean(cf) * KIB)
@@ -128,6 +137,15 @@ def main():
                  f"write {f_write:.3f}.")
     lines.append(f"{label} HBM traffic per launch: {fetch_b / 1e6:.1f} MB read + "
                  f"{write_b / 1e6:.1f} MB written = {(fetch_b + write_b) / 1e6:.1f} MB.")
+    call_b = None
+    if per_call:
+        n_calls, fsum, wsum = per_call
+        call_f = fsum * KIB * f_fetch / n_calls
+        call_w = wsum * KIB * f_write / n_calls
+        call_b = call_f + call_w
+        lines.append(f"Per call ({n_calls} calls, each ending with one {args.per_call} "
+                     f"dispatch; all {len(fetch)} dispatches counted): {call_f / 1e6:.1f} MB "
+                     f"read + {call_w / 1e6:.1f} MB written = {call_b / 1e6:.1f} MB.")
     lines.append("")
 
     extra = sorted(f for f in os.listdir(d) if f.startswith("p") and f.endswith("_counter_collection.csv"))
@@ -147,6 +165,8 @@ def main():
     if avg_ns is not None:
         lines.append(f"avg_launch_ns: {avg_ns:.0f}")
     lines.append(f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}")
+    if call_b is not None:
+        lines.append(f"traffic_bytes_per_call: {call_b:.0f}")
     lines.append(f"fetch_scale: {f_fetch:.4f}")
     lines.append(f"write_scale: {f_write:.4f}")
     for name in sorted(means):
