@@ -167,6 +167,22 @@ int qdr_decode_window(const qdr_desc *desc, const void *meta, void *packed,
                       const float *q, const float *k, const float *v, const float *a,
                       const float *b, float *o, void *stream);
 
+/* qdr_decode_window for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same call, with the
+ * window buffer taken from a fixed 32 MiB device array of the library instead of a caller
+ * argument. No allocation happens in the call. The array is one per GPU, allocated with the
+ * library's code object and held until the process ends; it keeps the last call's contents,
+ * which is what carries a window from token to token (nothing in it needs clearing: token
+ * t = 0 ignores what it holds). Every call on one GPU shares it, so windows of different
+ * states must not interleave on a GPU, and calls on one GPU that overlap (other streams,
+ * other threads) race. Limit: n_req * n_head * (W * 1024 + 512) bytes <= 32 MiB (e.g.
+ * 508 units at W = 64); a larger pool returns QDR_EUNSUPPORTED with the sizes in the error
+ * text. Errors: as qdr_decode_window. */
+int qdr_decode_window_static(const qdr_desc *desc, const void *meta, void *packed,
+                             float *row_scale, float *col_scale, int32_t t, const float *q,
+                             const float *k, const float *v, const float *a, const float *b,
+                             float *o, void *stream);
+
 /* T known tokens for every unit in one call (teacher-forced replay, prefill, multi-token
  * verification): the chunked form of window mode (LeapQuant abstract: outputs from the
  * fixed low-bit state plus high-precision updates, one quantization at the end). The

@@ -221,6 +221,37 @@ void quartile(int n, const double* tau, uint8_t* out) {
 
 }  // namespace
 
+// ---- window mode without a caller workspace ---------------------------------------
+// The window buffer of qdr_decode_window_static: a fixed device array of the library
+// (one per GPU, held until the process ends), for callers that cannot allocate. Its
+// device address comes from hipGetSymbolAddress, once per device, and only that address
+// is handed to the kernels (the array's name is a host-side stand-in in host code).
+constexpr size_t kStaticWindowBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticWindowBytes];
+constexpr int kScratchDevices = 64;
+static void* g_scratch_ptr[kScratchDevices];
+static std::mutex g_scratch_mu;
+
+static int static_window_buffer(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "qdr_decode_window_static: hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(QDR_EUNSUPPORTED, "qdr_decode_window_static: device %d beyond %d", dev,
+                kScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                        "qdr_decode_window_static: hipGetSymbolAddress");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QDR_OK;
+}
+
 extern "C" {
 
 int qdr_assign_bits(int32_t gate, int32_t n_head, int32_t dk, const double* halflife,
@@ -385,6 +416,46 @@ int qdr_decode_window(const qdr_desc* d, const void* meta, void* packed, float* 
                                        static_cast<uint8_t*>(window_buf), q, k, v, a, b, o, 0,
                                        nullptr, nullptr, static_cast<hipStream_t>(stream)),
                     "qdr_decode_window: launch");
+}
+
+int qdr_decode_window_static(const qdr_desc* d, const void* meta, void* packed,
+                             float* row_scale, float* col_scale, int32_t t, const float* q,
+                             const float* k, const float* v, const float* a, const float* b,
+                             float* o, void* stream) {
+  Summary g;
+  CHECK(check_desc_summary(d, &g));
+  if (d->window < 1) return fail(QDR_EUNSUPPORTED, "desc->window = %d: no window mode", d->window);
+  if (d->rule != QDR_RULE_STEP)
+    return fail(QDR_EUNSUPPORTED, "window mode takes only QDR_RULE_STEP (rule = %d)", d->rule);
+  if (d->window > qdr::kWindowMax)
+    return fail(QDR_EUNSUPPORTED, "desc->window = %d exceeds %d", d->window, qdr::kWindowMax);
+  if (t < 0 || t >= d->window)
+    return fail(QDR_EUNSUPPORTED, "window position t = %d outside [0, %d)", t, d->window);
+  const size_t need = (size_t)d->n_req * d->n_head * qdr::window_unit_bytes(d->window);
+  if (need > kStaticWindowBytes)
+    return fail(QDR_EUNSUPPORTED,
+                "qdr_decode_window_static: the window buffer needs %zu bytes, more than the "
+                "library's static %zu bytes (use qdr_decode_window with a caller buffer)",
+                need, kStaticWindowBytes);
+  const bool any = d->n_req > 0;
+  CHECK(check_ptr(meta, "meta", true));
+  CHECK(check_ptr(packed, "packed", any));
+  CHECK(check_ptr(row_scale, "row_scale", any));
+  CHECK(check_ptr(col_scale, "col_scale", any));
+  CHECK(check_ptr(q, "q", any));
+  CHECK(check_ptr(k, "k", any));
+  CHECK(check_ptr(v, "v", any));
+  CHECK(check_ptr(a, "a", any));
+  CHECK(check_ptr(b, "b", any));
+  CHECK(check_ptr(o, "o", any));
+  if (!any) return ok();
+  void* buf = nullptr;
+  CHECK(static_window_buffer(&buf));
+  return hip_status(qdr::launch_window(pool_of(d, meta, g), d->gate, d->window, t,
+                                       static_cast<uint8_t*>(packed), row_scale, col_scale,
+                                       static_cast<uint8_t*>(buf), q, k, v, a, b, o, 0, nullptr,
+                                       nullptr, static_cast<hipStream_t>(stream)),
+                    "qdr_decode_window_static: launch");
 }
 
 int qdr_decode_chunk(const qdr_desc* d, const void* meta, void* packed, float* row_scale,

@@ -27,7 +27,7 @@ KDA = 1
 RULE_STEP, RULE_KEYROW, RULE_TENSOR = 0, 1, 2  # scale rules (QDR_RULE_*)
 
 SYMBOLS = ("qdr_assign_bits", "qdr_state_bytes", "qdr_init_state", "qdr_quantize_state",
-           "qdr_decode_step", "qdr_decode_window", "qdr_decode_chunk",
+           "qdr_decode_step", "qdr_decode_window", "qdr_decode_window_static", "qdr_decode_chunk",
            "qdr_dequantize_state",
            "qdr_damp_select", "qdr_damp_bytes", "qdr_damp_init", "qdr_damp_quantize", "qdr_damp_step",
            "qdr_damp_dequantize", "qdr_comp_quantize", "qdr_comp_chunk", "qdr_comp_window",
@@ -76,6 +76,7 @@ def lib():
             "qdr_quantize_state": [D, P, P, P, P, P, P],
             "qdr_decode_step": [D, P, P, P, P, P, P, P, P, P, P, P],
             "qdr_decode_window": [D, P, P, P, P, P, i32, P, P, P, P, P, P, P],
+            "qdr_decode_window_static": [D, P, P, P, P, i32, P, P, P, P, P, P, P],
             "qdr_decode_chunk": [D, P, P, P, P, i32, P, P, P, P, P, P, P],
             "qdr_damp_select": [i32, i32, P, P],
             "qdr_damp_bytes": [DD, sz, sz, sz, sz],
@@ -194,6 +195,14 @@ def decode_window(L: Layout, meta, packed, row_scale, col_scale, window_buf, t, 
                                    _ptr(col_scale), _ptr(window_buf), int(t), _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(a), _ptr(b), _ptr(o), _stream(stream)),
            "qdr_decode_window")
+
+
+def decode_window_static(L: Layout, meta, packed, row_scale, col_scale, t, q, k, v, a, b, o,
+                         stream=None):
+    _check(lib().qdr_decode_window_static(L.desc, _ptr(meta), _ptr(packed), _ptr(row_scale),
+                                          _ptr(col_scale), int(t), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(a), _ptr(b), _ptr(o), _stream(stream)),
+           "qdr_decode_window_static")
 
 
 def decode_chunk(L: Layout, meta, packed, row_scale, col_scale, T, q, k, v, a, b, o, stream=None):
