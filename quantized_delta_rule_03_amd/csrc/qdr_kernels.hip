@@ -1991,6 +1991,39 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     L.jperm[tid] = (uint8_t)j;
     L.jinv[j] = (uint8_t)tid;
   }
+  const int pl = tid & (kD - 1), half = tid >> 7;
+  const int jl = mh->identity ? pl : (int)mh->perm[pl];
+  // indices are clamped into range; tokens past T read as k = q = v = 0, a = 1, b = 0
+  auto issue = [&](int t0, ChunkPf& f) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int tt = t0 + 8 * half + n;
+      const bool in = tt < T;
+      const size_t ti = (size_t)(in ? tt : T - 1);
+      const size_t base = ti * ts + uo;
+      const float kk = A.k[base + jl], qq = A.q[base + jl];
+      const float aa = (GATE == KDA) ? A.a[base + jl] : A.a[ti * A.n_unit + u];
+      f.k[n] = in ? kk : 0.0f;
+      f.q[n] = in ? qq : 0.0f;
+      f.a[n] = in ? aa : 1.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = t0 + 4 * jg + r;
+        const bool in = tt < T;
+        const float vv = A.v[(size_t)(in ? tt : T - 1) * ts + uo + 32 * w + 16 * h + rg];
+        f.v[4 * h + r] = in ? vv : 0.0f;
+      }
+    const int tb = t0 + (tid & (kCB - 1));
+    const float bv = A.b[(size_t)(tb < T ? tb : T - 1) * A.n_unit + u];
+    f.b = tb < T ? bv : 0.0f;
+  };
+  // the first sub-block's inputs are requested before the state is read and
+  // dequantized, so that both loads are in flight together
+  ChunkPf pf;
+  if (T > 0) issue(0, pf);
   float S[2][4][8];
   if (A.S_in) {
     // a given fp32 state (logical key order), gathered into the register layout
@@ -2032,37 +2065,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
                               L.tok_at, L.tok_v, L.jinv);
   }
   }
-  const int pl = tid & (kD - 1), half = tid >> 7;
-  const int jl = mh->identity ? pl : (int)mh->perm[pl];
-  // indices are clamped into range; tokens past T read as k = q = v = 0, a = 1, b = 0
-  auto issue = [&](int t0, ChunkPf& f) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int tt = t0 + 8 * half + n;
-      const bool in = tt < T;
-      const size_t ti = (size_t)(in ? tt : T - 1);
-      const size_t base = ti * ts + uo;
-      const float kk = A.k[base + jl], qq = A.q[base + jl];
-      const float aa = (GATE == KDA) ? A.a[base + jl] : A.a[ti * A.n_unit + u];
-      f.k[n] = in ? kk : 0.0f;
-      f.q[n] = in ? qq : 0.0f;
-      f.a[n] = in ? aa : 1.0f;
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tt = t0 + 4 * jg + r;
-        const bool in = tt < T;
-        const float vv = A.v[(size_t)(in ? tt : T - 1) * ts + uo + 32 * w + 16 * h + rg];
-        f.v[4 * h + r] = in ? vv : 0.0f;
-      }
-    const int tb = t0 + (tid & (kCB - 1));
-    const float bv = A.b[(size_t)(tb < T ? tb : T - 1) * A.n_unit + u];
-    f.b = tb < T ? bv : 0.0f;
-  };
-  ChunkPf pf;
-  if (T > 0) issue(0, pf);
 
   for (int t0 = 0; t0 < T; t0 += kCB) {
     // A1. gate products over this thread's 8 tokens; the two halves exchange totals
