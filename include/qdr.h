@@ -94,7 +94,7 @@ typedef struct qdr_desc {
     int32_t gate;         /* QDR_GATE_GDN or QDR_GATE_KDA                           */
     const uint8_t *bits;  /* HOST [n_head][dk], each in {4,6,8}; per head, the count */
                           /* of channels of each width is a multiple of 32           */
-    int32_t window;       /* W >= 1 for qdr_decode_window, 0 otherwise               */
+    int32_t window;       /* 1 <= W <= 256 for qdr_decode_window, 0 otherwise       */
     int32_t rule;         /* QDR_RULE_*: scale rule of qdr_quantize_state and          */
                           /* qdr_decode_step; window and chunk mode take QDR_RULE_STEP */
 } qdr_desc;
@@ -161,7 +161,7 @@ int qdr_decode_step(const qdr_desc *desc, const void *meta, void *packed, float 
  * its own update. At t = W-1 the buffered updates are folded into the state and the
  * state is requantized once (same scale rule). window_buf is caller-owned, sized by
  * qdr_state_bytes; its contents at t = 0 are ignored. Errors: all codes;
- * QDR_EUNSUPPORTED if t is out of range or desc->window < 1. */
+ * QDR_EUNSUPPORTED if t is out of range, desc->window < 1 or desc->window > 256. */
 int qdr_decode_window(const qdr_desc *desc, const void *meta, void *packed,
                       float *row_scale, float *col_scale, void *window_buf, int32_t t,
                       const float *q, const float *k, const float *v, const float *a,

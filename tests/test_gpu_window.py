@@ -105,6 +105,16 @@ def test_window_edge_lengths(torch_cuda, W):
     run_windows(torch_cuda, w, 1, 4, bits, W, 2, S0, f"kda mixed W={W}")
 
 
+def test_window_longest(torch_cuda):
+    """The longest window the library takes (W = 256 tokens, the horizon the drift bar is
+    stated for): one window, the fold staging eight chunks of 32 buffered tokens."""
+    w = wl.WORKLOADS[2]
+    bits = bits_for(w, n_head=4)
+    rng = np.random.default_rng(6)
+    S0 = (0.1 * rng.standard_normal((1, 4, 128, 128))).astype(np.float32)
+    run_windows(torch_cuda, w, 1, 4, bits, 256, 1, S0, "kda mixed W=256")
+
+
 def test_window_zero_requests_is_noop(torch_cuda):
     from quantized_delta_rule_03_amd import qdr
 
