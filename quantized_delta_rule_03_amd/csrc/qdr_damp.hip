@@ -36,10 +36,18 @@ constexpr int KDA = 1;
 constexpr int kH = kDampHalf;     // binary16 channels
 constexpr int kI = kD - kDampHalf;  // INT8 channels
 
+// Per-position vectors in LDS. The two threads of a row read positions e and 64 + e of
+// one vector at once; 16 bytes of padding after position 63 put the two halves on
+// different banks (without it, 512 bytes apart, every such read is a bank conflict).
+constexpr int kPadF = 4;  // floats
+constexpr int kPadD = 2;  // doubles
+__device__ __forceinline__ int fidx(int p) { return p + (p >> 6) * kPadF; }
+__device__ __forceinline__ int didx(int p) { return p + (p >> 6) * kPadD; }
+
 struct DampLds {
-  double kd[kD], qd[kD];  // k, q in fp64 for the dot products
-  float kp[kD], cf[kD];
-  float invA[kD];
+  double kd[kD + kPadD], qd[kD + kPadD];  // k, q in fp64 for the dot products
+  float kp[kD + kPadF], cf[kD + kPadF];
+  float invA[kD + kPadF];
   float part[4][kD];  // per-wave key-row absmax
 };
 
@@ -160,7 +168,7 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
     const float m = fmaxf(fmaxf(L.part[0][p], L.part[1][p]), fmaxf(L.part[2][p], L.part[3][p]));
     const float Aa = (m == 0.0f) ? 1.0f : m;
     A.R[(size_t)u * kI + (p - kH)] = Aa / 127.0f;
-    L.invA[p] = 1.0f / Aa;
+    L.invA[fidx(p)] = 1.0f / Aa;
   }
   __syncthreads();
   const uint32_t k0 = (uint32_t)A.seed, k1 = (uint32_t)(A.seed >> 32);
@@ -196,7 +204,7 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * q + e;  // position 16 blk + j
         const float sv = seg ? Sr[16 * b + 16 + j] : (b < 3 ? Sr[16 * b + 16 + j] : x[j]);
-        const float y = sv * L.invA[16 * blk + j];
+        const float y = sv * L.invA[fidx(16 * blk + j)];
         t[e] = (uint32_t)sr_scaled(y, (rw[q] >> (8 * e)) & 0xFFu);
       }
       wd[q] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(t[3], t[2], 0x0C0C0501u),
@@ -214,11 +222,11 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
   if (tid < kD) {
     const int p = tid, j = A.perm[(size_t)h * kD + p];
     const float kv = A.k[uo + j];
-    L.kp[p] = kv;
-    L.kd[p] = kv;
-    L.qd[p] = A.q[uo + j];
+    L.kp[fidx(p)] = kv;
+    L.kd[didx(p)] = kv;
+    L.qd[didx(p)] = A.q[uo + j];
     const float g = (GATE == KDA) ? A.a[uo + j] : A.a[u];
-    L.cf[p] = p < kH ? g : g * A.R[(size_t)u * kI + (p - kH)];
+    L.cf[fidx(p)] = p < kH ? g : g * A.R[(size_t)u * kI + (p - kH)];
   }
   const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
   // this thread's half row: binary16 words (half 0) and code words
@@ -248,24 +256,24 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
       const int hq = (e >> 1) & 3;
       const uint32_t hw = hq == 0 ? hx.x : (hq == 1 ? hx.y : (hq == 2 ? hx.z : hx.w));
       const float hv = f16_value((uint16_t)(hw >> (16 * (e & 1))));
-      Sr[e] = (seg == 0 ? hv : c) * L.cf[p0 + e];
+      Sr[e] = (seg == 0 ? hv : c) * L.cf[fidx(p0 + e)];
     } else {
-      Sr[e] = c * L.cf[p0 + e];
+      Sr[e] = c * L.cf[fidx(p0 + e)];
     }
   }
   // u_i: this thread's fp64 half sum in position order (a product of two fp32 values is exact
   // in fp64, so each fma adds exactly the product), the pair combined as s0 + s1
   double s = 0.0;
 #pragma unroll
-  for (int e = 0; e < 64; ++e) s = fma((double)Sr[e], L.kd[p0 + e], s);
+  for (int e = 0; e < 64; ++e) s = fma((double)Sr[e], L.kd[didx(p0 + e)], s);
   const double so = __shfl_xor(s, 1);
   const float uu = (float)(seg ? so + s : s + so);
   const float w = A.b[u] * (A.v[uo + i] - uu);
   double t = 0.0;
 #pragma unroll
   for (int e = 0; e < 64; ++e) {
-    Sr[e] = fmaf(w, L.kp[p0 + e], Sr[e]);
-    t = fma((double)Sr[e], L.qd[p0 + e], t);
+    Sr[e] = fmaf(w, L.kp[fidx(p0 + e)], Sr[e]);
+    t = fma((double)Sr[e], L.qd[didx(p0 + e)], t);
   }
   const double to = __shfl_xor(t, 1);
   if (seg == 0) A.o[uo + i] = (float)(t + to);
