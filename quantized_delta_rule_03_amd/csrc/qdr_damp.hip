@@ -107,19 +107,30 @@ __device__ __forceinline__ float f16_value(uint16_t h) {
 }
 
 // Max over the 32 rows of the wave that share this lane's half, for each of the lane's 64
-// positions, as a reduce-scatter over lane bits 5..1: lane l ends with the positions
+// non-negative values, as a reduce-scatter over lane bits 5..1: lane l ends with the positions
 // off + 0 and off + 1 of its half, off = 32 b5 + 16 b4 + 8 b3 + 4 b2 + 2 b1.
 __device__ __forceinline__ void half_colmax(const float (&a)[64], int lane, float& m0, float& m1,
                                             int& off) {
-  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
-  float x[32];
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  // a >= 0, compared as bit patterns (non-negative floats order as unsigned integers;
+  // no NaN canonicalization is needed as for a float max). Lane bits 5 and
+  // 4 by the gfx950 half-swaps: v_permlane32_swap exchanges the upper 32 lanes of its
+  // first operand with the lower 32 lanes of its second, so lanes 0-31 end with both
+  // rows' values of position j and lanes 32-63 with those of j + 32, without selects;
+  // v_permlane16_swap does the same within each half, for lane bit 4.
+  uint32_t x[32];
 #pragma unroll
-  for (int j = 0; j < 32; ++j)
-    x[j] = fmaxf(b5 ? a[j + 32] : a[j], __shfl_xor(b5 ? a[j] : a[j + 32], 32));
+  for (int j = 0; j < 32; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[j]), __float_as_uint(a[j + 32]),
+                                                    false, false);
+    x[j] = max(r[0], r[1]);
+  }
   float y[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    y[j] = fmaxf(b4 ? x[j + 16] : x[j], __shfl_xor(b4 ? x[j] : x[j + 16], 16));
+  for (int j = 0; j < 16; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x[j], x[j + 16], false, false);
+    y[j] = __uint_as_float(max(r[0], r[1]));
+  }
   float z[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) z[j] = fmaxf(b3 ? y[j + 8] : y[j], __shfl_xor(b3 ? y[j] : y[j + 8], 8));
@@ -128,7 +139,8 @@ __device__ __forceinline__ void half_colmax(const float (&a)[64], int lane, floa
   for (int j = 0; j < 4; ++j) v[j] = fmaxf(b2 ? z[j + 4] : z[j], __shfl_xor(b2 ? z[j] : z[j + 4], 4));
   m0 = fmaxf(b1 ? v[2] : v[0], __shfl_xor(b1 ? v[0] : v[2], 2));
   m1 = fmaxf(b1 ? v[3] : v[1], __shfl_xor(b1 ? v[1] : v[3], 2));
-  off = 32 * (int)b5 + 16 * (int)b4 + 8 * (int)b3 + 4 * (int)b2 + 2 * (int)b1;
+  off = 32 * (int)((lane >> 5) & 1) + 16 * (int)((lane >> 4) & 1) + 8 * (int)b3 + 4 * (int)b2 +
+        2 * (int)b1;
 }
 
 // Row i's half-row pointers: raw code words q = 0..3 hold the codes of positions
