@@ -106,6 +106,27 @@ __device__ __forceinline__ float f16_value(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Lane exchanges without LDS round trips: the value of lane ^ 1, ^ 2 (quad permutes) and
+// ^ 8 (row rotation by 8 within each row of 16) by DPP moves; lane ^ 4 by a swizzle.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor8(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swz_xor4(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+}
+__device__ __forceinline__ double dpp_xor1(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(u >> 32), 0xB1, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
 // Max over the 32 rows of the wave that share this lane's half, for each of the lane's 64
 // non-negative values, as a reduce-scatter over lane bits 5..1: lane l ends with the positions
 // off + 0 and off + 1 of its half, off = 32 b5 + 16 b4 + 8 b3 + 4 b2 + 2 b1.
@@ -133,12 +154,12 @@ __device__ __forceinline__ void half_colmax(const float (&a)[64], int lane, floa
   }
   float z[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) z[j] = fmaxf(b3 ? y[j + 8] : y[j], __shfl_xor(b3 ? y[j] : y[j + 8], 8));
+  for (int j = 0; j < 8; ++j) z[j] = fmaxf(b3 ? y[j + 8] : y[j], dpp_xor8(b3 ? y[j] : y[j + 8]));
   float v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = fmaxf(b2 ? z[j + 4] : z[j], __shfl_xor(b2 ? z[j] : z[j + 4], 4));
-  m0 = fmaxf(b1 ? v[2] : v[0], __shfl_xor(b1 ? v[0] : v[2], 2));
-  m1 = fmaxf(b1 ? v[3] : v[1], __shfl_xor(b1 ? v[1] : v[3], 2));
+  for (int j = 0; j < 4; ++j) v[j] = fmaxf(b2 ? z[j + 4] : z[j], swz_xor4(b2 ? z[j] : z[j + 4]));
+  m0 = fmaxf(b1 ? v[2] : v[0], dpp_xor2(b1 ? v[0] : v[2]));
+  m1 = fmaxf(b1 ? v[3] : v[1], dpp_xor2(b1 ? v[1] : v[3]));
   off = 32 * (int)((lane >> 5) & 1) + 16 * (int)((lane >> 4) & 1) + 8 * (int)b3 + 4 * (int)b2 +
         2 * (int)b1;
 }
@@ -199,7 +220,7 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
   // blocks 5-7 (80..127). Each block's codes are packed and stored as 16 bytes.
   float x[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) x[e] = __shfl_xor(Sr[e], 1);
+  for (int e = 0; e < 16; ++e) x[e] = dpp_xor1(Sr[e]);
   int8_t* crow = A.codes + ((size_t)u * kD + i) * kI;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -278,7 +299,7 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
   double s = 0.0;
 #pragma unroll
   for (int e = 0; e < 64; ++e) s = fma((double)Sr[e], L.kd[didx(p0 + e)], s);
-  const double so = __shfl_xor(s, 1);
+  const double so = dpp_xor1(s);
   const float uu = (float)(seg ? so + s : s + so);
   const float w = A.b[u] * (A.v[uo + i] - uu);
   double t = 0.0;
@@ -287,7 +308,7 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
     Sr[e] = fmaf(w, L.kp[fidx(p0 + e)], Sr[e]);
     t = fma((double)Sr[e], L.qd[didx(p0 + e)], t);
   }
-  const double to = __shfl_xor(t, 1);
+  const double to = dpp_xor1(t);
   if (seg == 0) A.o[uo + i] = (float)(t + to);
   damp_requant(L, A, u, Sr);
 }
