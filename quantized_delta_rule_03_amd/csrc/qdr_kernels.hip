@@ -13,8 +13,9 @@
 //    absmax) go through LDS: 8 (wave, K or Q) partial sums or 16 (wave, jg) partial
 //    maxima per row.
 //  - The decode step is persistent: a grid of (CUs x resident groups) work-groups walks
-//    the units, and each group issues the loads of its next unit's codes and vectors
-//    before computing the current one, so HBM reads stay in flight during the compute.
+//    the units, and each group moves its next unit's codes and vectors HBM -> LDS with
+//    LDS-direct loads (no registers hold them) while it computes the current one, so HBM
+//    reads stay in flight during the compute.
 //
 // Arithmetic contract (identical in every rounding to the scalar reference):
 //   dequant + gate   S' = fl(code * G_ij), G_ij = fl(cf_j * rf_i) (the entry's gated step)

@@ -49,12 +49,18 @@ def is_copy(name):
 
 
 def kernel_source_sha256(root):
+    """Hash of the kernel sources' code: line comments, trailing blanks and blank lines are
+    left out, so a summary stays valid across comment-only edits and goes stale on any
+    change to the code."""
     h = hashlib.sha256()
     for rel in ("quantized_delta_rule_03_amd/csrc/qdr_kernels.hip",
                 "quantized_delta_rule_03_amd/csrc/qdr_damp.hip",
                 "quantized_delta_rule_03_amd/csrc/qdr_internal.h"):
-        with open(os.path.join(root, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode("utf-8") + b"\n")
     return h.hexdigest()
 
 
