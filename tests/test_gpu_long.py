@@ -9,7 +9,8 @@ benchmark times, and compare a few sampled requests (every head of each) with th
   mixed widths; the sampled requests start from the pre-warmed outlier states; 64 steps;
 * the serving shape (1024 requests x 32 GDN heads, mixed 8/6/4-bit heads): all 128 steps;
 * the windowed shape (256 requests x 32 KDA heads, 8-bit, W = 64): 16 windows (1024
-  tokens), in window mode (one call per token) and in chunk mode (one call per window).
+  tokens), in window mode (one call per token) and in chunk mode (one call per window);
+* the DAMP-style variant on the serving shape (1024 requests x 32 GDN heads): 128 steps.
 
 Each step (window) is checked teacher-forced -- the oracle stepped from the GPU's own state
 of the sampled requests -- against the bar (codes within 1 LSB on <= 1e-4 of entries, o
@@ -221,3 +222,77 @@ def test_windowed_full_size_16_windows(torch_cuda, mode):
     # the drift bar is stated for 256 tokens; beyond it the free-running pair keeps
     # diverging as any two roundings of a quantized recurrence do (reported above)
     assert drifts[0] <= DRIFT_REL_L2
+
+
+def test_damp_serving_full_size_128_steps(torch_cuda):
+    """The DAMP-style variant over the serving shape's 128 steps, the whole pool in one
+    launch per step: four sampled requests (every head of each) compared teacher-forced
+    (the oracle stepped from the GPU's own state of those units) and free-running. The
+    stochastic rounding is keyed by the unit index, which the oracle's full-size pool
+    keeps; it steps only the sampled units."""
+    from quantized_delta_rule_03_amd import qdr
+
+    torch = torch_cuda
+    w = wl.WORKLOADS[3]
+    H, sample, steps = w.n_head, [0, 333, 700, 1023], 128
+    sel = qdr.damp_select(w.gate, wl.halflives(w), H)
+    gpu = qdr.DampState(w.n_req, H, w.gate, sel, seed=17)
+    free = oracle.DampPool(w.n_req, H, sel, seed=17)  # both start from the zero state
+    tf = free.copy()
+    units = [(r * H, (r + 1) * H) for r in sample]
+    idx = torch.tensor([u for u0, u1 in units for u in range(u0, u1)], device="cuda")
+    a_dev = torch.from_numpy(wl.static_gate(w)).cuda()
+    o = torch.empty((w.n_req, H, 128), dtype=torch.float32, device="cuda")
+    host = {k: np.zeros((w.n_req, H, 128) if k in "qkva" else (w.n_req, H), np.float32)
+            for k in "qkvab"}
+    host["a"] = np.ascontiguousarray(wl.static_gate(w))
+    worst_o = worst_frac = worst_half = 0.0
+    worst_lsb = 0
+    exact = True
+    print(f"[damp serving] {w.n_req}x{H} units, {steps} steps, sample {sample}", flush=True)
+    for t in range(steps):
+        dev, hs = step_inputs_sampled(torch, w, t, sample, a_dev)
+        for k in "qkvb":
+            host[k][sample] = hs[k]
+        # teacher forcing: the oracle's sampled units take the GPU's state
+        tf.half[idx.cpu().numpy()] = gpu.half[idx].cpu().numpy().view(np.uint16)
+        tf.codes[idx.cpu().numpy()] = gpu.codes[idx].cpu().numpy()
+        tf.R[idx.cpu().numpy()] = gpu.R[idx].cpu().numpy()
+        gpu.step(dev["q"], dev["k"], dev["v"], dev["a"], dev["b"], o, step=t)
+        og = o[torch.tensor(sample, device="cuda")].cpu().numpy()
+        o_tf = np.zeros_like(og)
+        for n, (u0, u1) in enumerate(units):
+            args = (w.gate, host["q"], host["k"], host["v"], host["a"], host["b"])
+            o_tf[n] = tf.step(*args, step=t, u0=u0, u1=u1)[sample[n]]
+            free.step(*args, step=t, u0=u0, u1=u1)
+        worst_o = max(worst_o, rel_l2(og, o_tf))
+        gi = idx.cpu().numpy()
+        d = np.abs(gpu.codes[idx].cpu().numpy().astype(np.int32) - tf.codes[gi].astype(np.int32))
+        nh = int((gpu.half[idx].cpu().numpy().view(np.uint16) != tf.half[gi]).sum())
+        worst_lsb = max(worst_lsb, int(d.max()))
+        worst_frac = max(worst_frac, float((d > 0).mean()))
+        worst_half = max(worst_half, nh / d.size)
+        exact = exact and not d.any() and nh == 0
+        if (t + 1) % 32 == 0:
+            print(f"[damp serving] step {t + 1}: worst o rel-L2 tf {worst_o:.2e}, codes max "
+                  f"{worst_lsb} LSB on {worst_frac:.2e}", flush=True)
+    gi = idx.cpu().numpy()
+
+    def sampled(half, codes, R):  # the sampled requests as a pool of their own
+        p = oracle.DampPool(len(sample), H, sel, seed=17)
+        p.half[:], p.codes[:], p.R[:] = half, codes, R
+        return p.dequantize()
+
+    S_gpu = sampled(gpu.half[idx].cpu().numpy().view(np.uint16), gpu.codes[idx].cpu().numpy(),
+                    gpu.R[idx].cpu().numpy())
+    S_ref = sampled(free.half[gi], free.codes[gi], free.R[gi])
+    drift = rel_l2(S_gpu, S_ref)
+    assert np.abs(S_ref).max() > 0  # the compared trajectories are not the zero state
+    print(f"[damp serving] worst o rel-L2 tf={worst_o:.2e}; teacher-forced codes max "
+          f"{worst_lsb} LSB on {worst_frac:.2e}, binary16 on {worst_half:.2e}; bit-exact="
+          f"{exact}; free-running drift after {steps} steps {drift:.2e}", flush=True)
+    assert worst_o <= O_REL_L2
+    assert worst_lsb <= 1 and worst_frac <= CODE_FLIP_FRAC
+    assert worst_half <= CODE_FLIP_FRAC
+    assert drift <= DRIFT_REL_L2
+
