@@ -1911,6 +1911,7 @@ struct ChunkArgs {
   uint16_t* tok_idx;
   float* tok_val;
   const float* S_in;  // when set: the fp32 state [n_unit][128][128] (logical), T = 0
+  int ubits;          // every head of this one width (then no metadata is read), or 0
 };
 
 struct ChunkLds {
@@ -1981,19 +1982,32 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int tid = threadIdx.x;
   const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
   const int u = blockIdx.x;
-  const UnitInfo cur = win_unit_of(A.meta, A.n_head, A.req_bytes, u);
-  const MetaHead* mh = meta_heads(A.meta) + cur.h;
+  // With every head of one width the tile offset follows from the unit index and the
+  // key order is the logical one, so the unit starts without a dependent metadata load.
+  UnitInfo cur;
+  const MetaHead* mh = nullptr;
+  if (A.ubits) {
+    const int r = u / A.n_head, h = u - r * A.n_head;
+    cur.un = (uint32_t)u;
+    cur.toff = (uint64_t)r * A.req_bytes + (uint64_t)h * (A.req_bytes / (uint32_t)A.n_head);
+    cur.sb = (uint32_t)A.ubits * 0x01010101u;
+    cur.h = (uint32_t)h;
+  } else {
+    cur = win_unit_of(A.meta, A.n_head, A.req_bytes, u);
+    mh = meta_heads(A.meta) + cur.h;
+  }
+  const bool ident = A.ubits || mh->identity;
   const size_t uo = (size_t)u * kD;
   const size_t ts = (size_t)A.n_unit * kD;  // token stride of q, k, v, o (and KDA a)
   const int T = A.T;
 
   if (tid < kD) {
-    const int j = mh->identity ? tid : (int)mh->perm[tid];
+    const int j = ident ? tid : (int)mh->perm[tid];
     L.jperm[tid] = (uint8_t)j;
     L.jinv[j] = (uint8_t)tid;
   }
   const int pl = tid & (kD - 1), half = tid >> 7;
-  const int jl = mh->identity ? pl : (int)mh->perm[pl];
+  const int jl = ident ? pl : (int)mh->perm[pl];
   // indices are clamped into range; tokens past T read as k = q = v = 0, a = 1, b = 0
   auto issue = [&](int t0, ChunkPf& f) {
 #pragma unroll
@@ -2034,7 +2048,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int p = 32 * s + 8 * jg + e;
-        const int j = mh->identity ? p : (int)mh->perm[p];
+        const int j = ident ? p : (int)mh->perm[p];
 #pragma unroll
         for (int h = 0; h < 2; ++h) S[h][s][e] = Su[(32 * w + 16 * h + rg) * kD + j];
       }
@@ -2516,8 +2530,16 @@ hipError_t launch_chunk(const Pool& p, int gate, int T, uint8_t* packed, float* 
                         const float* b, float* o, int m, uint16_t* tok_idx, float* tok_val,
                         const float* S_in, hipStream_t s) {
   if (p.n_unit == 0 || (T == 0 && !S_in)) return hipSuccess;
+  // a pool whose heads all have one width: its tiles sit at h * req_bytes / n_head in key
+  // order (a single-width head keeps the logical order)
+  int ubits = 0;
+  if (p.uniform) {
+    static const int widths[3] = {8, 6, 4};
+    for (int c = 0; c < 3; ++c)
+      if (p.n_class[c] == p.n_head) ubits = widths[c];
+  }
   ChunkArgs A{p.meta, p.n_head, p.n_unit, T, p.req_bytes, packed, rs, cs, q, k, v, a, b, o,
-              m, tok_idx, tok_val, S_in};
+              m, tok_idx, tok_val, S_in, ubits};
   if (gate == GDN) hipLaunchKernelGGL(k_chunk<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
   else hipLaunchKernelGGL(k_chunk<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
   return hipGetLastError();

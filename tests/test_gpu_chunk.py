@@ -103,6 +103,18 @@ def test_chunk_kda_mixed_widths_prewarmed(torch_cuda):
     run_chunks(torch_cuda, w, 1, 8, bits, 64, 2, np.ascontiguousarray(S0), "kda mixed T=64")
 
 
+@pytest.mark.parametrize("width", [4, 6])
+def test_chunk_single_width_pools(torch_cuda, width):
+    """Pools whose heads all have one width other than 8 (tile offsets then follow from
+    the unit index alone), several requests and an odd head count."""
+    w = wl.WORKLOADS[1]
+    n_req, n_head = 3, 5
+    bits = wl.uniform_bits(n_head, width)
+    rng = np.random.default_rng(20 + width)
+    S0 = (0.1 * rng.standard_normal((n_req, n_head, 128, 128))).astype(np.float32)
+    run_chunks(torch_cuda, w, n_req, n_head, bits, 20, 2, S0, f"gdn {width}-bit T=20")
+
+
 @pytest.mark.parametrize("T", [1, 15, 17, 100])
 def test_chunk_lengths(torch_cuda, T):
     """One token, sub-block edges, and a chunk longer than the serving window."""
