@@ -16,7 +16,7 @@
 //   readout            o_i from S_new and q as u_i from S' and k
 //   requantize         p < 16: binary16, round to nearest even; p >= 16: A_p = max_i
 //                      |S_ip| (1 if 0), R_p = fl(A_p/127), y = fl(S * fl(1/A_p)),
-//                      code = clamp(floor(y*127 + u), +-127) in fp64, u in [0, 1) = byte
+//                      code = clamp(floor(y*127 + u), +-127) exactly, u in [0, 1) = byte
 //                      p%16 (little-endian over the words) of the Philox4x32-10 block for
 //                      the counter (i*8 + p/16, unit, step lo, step hi) and key (seed lo,
 //                      seed hi), times 2^-8.
@@ -127,39 +127,61 @@ __device__ __forceinline__ double dpp_xor1(double x) {
   return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
+// DPP forms on bit patterns (the float maxima below compare non-negative floats as
+// unsigned integers: no NaN canonicalization, and the moves fuse into the max)
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t dpp_xor8(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t swz_xor4(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x101F);
+}
+
+// max(|a|, |b|) in one instruction (source modifiers; no NaN canonicalization of the operands)
+__device__ __forceinline__ uint32_t absmax2(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_max_f32 %0, |%1|, |%2|" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Max over the 32 rows of the wave that share this lane's half, for each of the lane's 64
-// non-negative values, as a reduce-scatter over lane bits 5..1: lane l ends with the positions
-// off + 0 and off + 1 of its half, off = 32 b5 + 16 b4 + 8 b3 + 4 b2 + 2 b1.
-__device__ __forceinline__ void half_colmax(const float (&a)[64], int lane, float& m0, float& m1,
+// values in absolute value, as a reduce-scatter over lane bits 5..1: lane l ends with the
+// positions off + 0 and off + 1 of its half, off = 32 b5 + 16 b4 + 8 b3 + 4 b2 + 2 b1.
+// The values are exchanged in place and swapped back, so a is unchanged on return.
+__device__ __forceinline__ void half_colmax(float (&a)[64], int lane, float& m0, float& m1,
                                             int& off) {
   const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
-  // a >= 0, compared as bit patterns (non-negative floats order as unsigned integers;
-  // no NaN canonicalization is needed as for a float max). Lane bits 5 and
-  // 4 by the gfx950 half-swaps: v_permlane32_swap exchanges the upper 32 lanes of its
-  // first operand with the lower 32 lanes of its second, so lanes 0-31 end with both
-  // rows' values of position j and lanes 32-63 with those of j + 32, without selects;
-  // v_permlane16_swap does the same within each half, for lane bit 4.
+  // Lane bits 5 and 4 by the gfx950 half-swaps: v_permlane32_swap exchanges the upper 32
+  // lanes of its first operand with the lower 32 lanes of its second, so lanes 0-31 end
+  // with both rows' values of position j and lanes 32-63 with those of j + 32, without
+  // selects; v_permlane16_swap does the same within each half, for lane bit 4. From the
+  // first level on the values are magnitudes, compared as bit patterns.
   uint32_t x[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[j]), __float_as_uint(a[j + 32]),
                                                     false, false);
-    x[j] = max(r[0], r[1]);
+    x[j] = absmax2(r[0], r[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(r[0], r[1], false, false);
+    a[j] = __uint_as_float(t[0]);
+    a[j + 32] = __uint_as_float(t[1]);
   }
-  float y[16];
+  uint32_t y[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const auto r = __builtin_amdgcn_permlane16_swap(x[j], x[j + 16], false, false);
-    y[j] = __uint_as_float(max(r[0], r[1]));
+    y[j] = max(r[0], r[1]);
   }
-  float z[8];
+  uint32_t z[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) z[j] = fmaxf(b3 ? y[j + 8] : y[j], dpp_xor8(b3 ? y[j] : y[j + 8]));
-  float v[4];
+  for (int j = 0; j < 8; ++j) z[j] = max(b3 ? y[j + 8] : y[j], dpp_xor8(b3 ? y[j] : y[j + 8]));
+  uint32_t v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = fmaxf(b2 ? z[j + 4] : z[j], swz_xor4(b2 ? z[j] : z[j + 4]));
-  m0 = fmaxf(b1 ? v[2] : v[0], dpp_xor2(b1 ? v[0] : v[2]));
-  m1 = fmaxf(b1 ? v[3] : v[1], dpp_xor2(b1 ? v[1] : v[3]));
+  for (int j = 0; j < 4; ++j) v[j] = max(b2 ? z[j + 4] : z[j], swz_xor4(b2 ? z[j] : z[j + 4]));
+  m0 = __uint_as_float(max(b1 ? v[2] : v[0], dpp_xor2(b1 ? v[0] : v[2])));
+  m1 = __uint_as_float(max(b1 ? v[3] : v[1], dpp_xor2(b1 ? v[1] : v[3])));
   off = 32 * (int)((lane >> 5) & 1) + 16 * (int)((lane >> 4) & 1) + 8 * (int)b3 + 4 * (int)b2 +
         2 * (int)b1;
 }
@@ -170,14 +192,33 @@ __device__ __forceinline__ int8_t* code_word(int8_t* crow, int seg, int q) {
   return crow + (seg ? 48 + 16 * q : 16 * (q - 1));
 }
 
-// floor(127 y + r 2^-8) clamped to [-127, 127], r the row's random byte. Scaled by 2^8 it is
-// floor(127 2^8 y + r) >> 8 (floor of a floor quotient), and 127 2^8 y + r is exact in
-// fp64 (at most 31 significant bits), as is the unscaled sum; y is clamped to [-1, 1]
-// first, which leaves the clamped result unchanged and keeps the floor inside int32.
-// sr_scaled returns the scaled floor; the code is its second byte (>> 8).
-__device__ __forceinline__ int sr_scaled(float y, uint32_t r8) {
-  const float yc = fminf(fmaxf(y, -1.0f), 1.0f);
-  return (int)floor(fma((double)yc, 32512.0, (double)r8));  // 127 * 2^8
+// Stochastic rounding: floor(127 y + r 2^-8) clamped to [-127, 127], r the row's random
+// byte. Scaled by 2^8 it is floor((floor(127 2^8 y) + r) / 2^8): r is an integer, so it moves
+// out of the inner floor, and the floor of a floor quotient is the floor of the quotient.
+// y is clamped to [-1, 1] first, which leaves the clamped result unchanged and keeps
+// floor(127 2^8 y) + r inside [-32512, 32767]; the code is then its second byte (an
+// arithmetic shift by 8).
+__device__ __forceinline__ float sr_clamp(float y) { return fminf(fmaxf(y, -1.0f), 1.0f); }
+
+// floor(32512 y) for four values y (32512 = 127 * 2^8), exactly: the products are rounded
+// toward -inf (the MODE register's fp32 rounding field set to 2 around them, then back to
+// nearest even), and the floor of the largest fp32 value <= x is floor(x), since every
+// integer of this range is an fp32 value. Two wait states follow each mode write.
+__device__ __forceinline__ void floor_scaled4(const float (&y)[4], int (&f)[4]) {
+  asm("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 2\n\t"
+      "s_nop 1\n\t"
+      "v_mul_f32 %0, %8, %4\n\t"
+      "v_mul_f32 %1, %8, %5\n\t"
+      "v_mul_f32 %2, %8, %6\n\t"
+      "v_mul_f32 %3, %8, %7\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+      "s_nop 1\n\t"
+      "v_cvt_flr_i32_f32 %0, %0\n\t"
+      "v_cvt_flr_i32_f32 %1, %1\n\t"
+      "v_cvt_flr_i32_f32 %2, %2\n\t"
+      "v_cvt_flr_i32_f32 %3, %3"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+      : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "s"(32512.0f));
 }
 
 // ranges and requantization of the register-held half rows, stored in place
@@ -186,12 +227,9 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
   {
-    float ab[64];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) ab[e] = fabsf(Sr[e]);
     float m0, m1;
     int off;
-    half_colmax(ab, lane, m0, m1, off);
+    half_colmax(Sr, lane, m0, m1, off);
     L.part[w][p0 + off] = m0;
     L.part[w][p0 + off + 1] = m1;
   }
@@ -215,16 +253,14 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
     dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
   }
-  // The row's 112 INT8 positions in Philox blocks of 16 (one block per 16 positions):
-  // half 0 takes blocks 1-4 (positions 16..79; 64..79 from its partner's registers), half 1
-  // blocks 5-7 (80..127). Each block's codes are packed and stored as 16 bytes.
-  float x[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) x[e] = dpp_xor1(Sr[e]);
+  // The row's 112 INT8 positions in Philox blocks of 16 (one block per 16 positions), 56 per
+  // thread: half 0 takes blocks 1-3 (positions 16..63), half 1 blocks 5-7 (80..127), each
+  // from its own registers, stored as 16 bytes per block; block 4 (64..79, all in half 1's
+  // registers) is generated by both, half 0 coding 64..71 from its partner's values and
+  // half 1 72..79 from its own, 8 bytes each.
   int8_t* crow = A.codes + ((size_t)u * kD + i) * kI;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if (seg == 1 && b == 3) break;  // half 1 has three blocks
+  for (int b = 0; b < 3; ++b) {
     const int blk = seg ? 5 + b : 1 + b;  // positions 16 blk .. 16 blk + 15
     const uint4 r = philox4x32_10((uint32_t)(i * 8 + blk), (uint32_t)u, s0, s1, k0, k1);
     const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
@@ -232,18 +268,49 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // the codes are the second bytes of the scaled floors: byte selects pack four
-      uint32_t t[4];
+      float yc[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * q + e;  // position 16 blk + j
-        const float sv = seg ? Sr[16 * b + 16 + j] : (b < 3 ? Sr[16 * b + 16 + j] : x[j]);
-        const float y = sv * L.invA[fidx(16 * blk + j)];
-        t[e] = (uint32_t)sr_scaled(y, (rw[q] >> (8 * e)) & 0xFFu);
+        yc[e] = sr_clamp(Sr[16 * b + 16 + j] * L.invA[fidx(16 * blk + j)]);
       }
+      int f[4];
+      floor_scaled4(yc, f);
+      uint32_t t[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (uint32_t)(f[e] + (int)((rw[q] >> (8 * e)) & 0xFFu));
       wd[q] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(t[3], t[2], 0x0C0C0501u),
                                     __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0501u), 0x05040100u);
     }
     *reinterpret_cast<uint4*>(crow + 16 * (blk - 1)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  }
+  {
+    const uint4 r = philox4x32_10((uint32_t)(i * 8 + 4), (uint32_t)u, s0, s1, k0, k1);
+    const uint32_t rw[2] = {seg ? r.z : r.x, seg ? r.w : r.y};
+    float xs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float other = dpp_xor1(Sr[j]);  // half 1's position 64 + j, for half 0
+      xs[j] = seg ? Sr[8 + j] : other;
+    }
+    uint32_t wd[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float yc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * q + e;  // position 64 + 8 seg + j
+        yc[e] = sr_clamp(xs[j] * L.invA[fidx(64 + 8 * seg + j)]);
+      }
+      int f[4];
+      floor_scaled4(yc, f);
+      uint32_t t[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (uint32_t)(f[e] + (int)((rw[q] >> (8 * e)) & 0xFFu));
+      wd[q] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(t[3], t[2], 0x0C0C0501u),
+                                    __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0501u), 0x05040100u);
+    }
+    *reinterpret_cast<uint2*>(crow + 48 + 8 * seg) = make_uint2(wd[0], wd[1]);
   }
 }
 
