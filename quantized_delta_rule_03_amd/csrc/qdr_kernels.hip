@@ -2008,8 +2008,28 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   }
   const int pl = tid & (kD - 1), half = tid >> 7;
   const int jl = ident ? pl : (int)mh->perm[pl];
-  // indices are clamped into range; tokens past T read as k = q = v = 0, a = 1, b = 0
+  // indices are clamped into range; tokens past T read as k = q = v = 0, a = 1, b = 0.
+  // A sub-block with all its tokens in range forms each lane's first offset once and steps
+  // it by the token stride.
   auto issue = [&](int t0, ChunkPf& f) {
+    if (t0 + kCB <= T) {
+      const size_t kq0 = (size_t)(t0 + 8 * half) * ts + uo + jl;
+      const size_t a0 = (size_t)(t0 + 8 * half) * (size_t)A.n_unit + u;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const size_t base = kq0 + (size_t)n * ts;
+        f.k[n] = A.k[base];
+        f.q[n] = A.q[base];
+        f.a[n] = (GATE == KDA) ? A.a[base] : A.a[a0 + (size_t)n * A.n_unit];
+      }
+      const size_t v0 = (size_t)(t0 + 4 * jg) * ts + uo + 32 * w + rg;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f.v[4 * h + r] = A.v[v0 + (size_t)r * ts + 16 * h];
+      f.b = A.b[(size_t)(t0 + (tid & (kCB - 1))) * A.n_unit + u];
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const int tt = t0 + 8 * half + n;
