@@ -49,6 +49,7 @@ struct DampLds {
   float kp[kD + kPadF], cf[kD + kPadF];
   float invA[kD + kPadF];
   float part[4][kD];  // per-wave key-row absmax
+  int wide;           // some range of the unit outside [2^-126, 2^126]
 };
 
 // a ^ b ^ k in one gfx950 three-input bit operation (truth table 0x96), k uniform
@@ -195,9 +196,9 @@ __device__ __forceinline__ int8_t* code_word(int8_t* crow, int seg, int q) {
 // Stochastic rounding: floor(127 y + r 2^-8) clamped to [-127, 127], r the row's random
 // byte. Scaled by 2^8 it is floor((floor(127 2^8 y) + r) / 2^8): r is an integer, so it moves
 // out of the inner floor, and the floor of a floor quotient is the floor of the quotient.
-// y is clamped to [-1, 1] first, which leaves the clamped result unchanged and keeps
-// floor(127 2^8 y) + r inside [-32512, 32767]; the code is then its second byte (an
-// arithmetic shift by 8).
+// y lies in [-1, 1] or is clamped to it (see damp_codes), which leaves the clamped result
+// unchanged and keeps floor(127 2^8 y) + r inside [-32512, 32767]; the code is then its
+// second byte (an arithmetic shift by 8).
 __device__ __forceinline__ float sr_clamp(float y) { return fminf(fmaxf(y, -1.0f), 1.0f); }
 
 // floor(32512 y) for four values y (32512 = 127 * 2^8), exactly: the products are rounded
@@ -221,38 +222,16 @@ __device__ __forceinline__ void floor_scaled4(const float (&y)[4], int (&f)[4]) 
       : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "s"(32512.0f));
 }
 
-// ranges and requantization of the register-held half rows, stored in place
-__device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int u,
-                                             float (&Sr)[64]) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
-  {
-    float m0, m1;
-    int off;
-    half_colmax(Sr, lane, m0, m1, off);
-    L.part[w][p0 + off] = m0;
-    L.part[w][p0 + off + 1] = m1;
-  }
-  __syncthreads();
-  if (tid < kD && tid >= kH) {
-    const int p = tid;
-    const float m = fmaxf(fmaxf(L.part[0][p], L.part[1][p]), fmaxf(L.part[2][p], L.part[3][p]));
-    const float Aa = (m == 0.0f) ? 1.0f : m;
-    A.R[(size_t)u * kI + (p - kH)] = Aa / 127.0f;
-    L.invA[fidx(p)] = 1.0f / Aa;
-  }
-  __syncthreads();
-  const uint32_t k0 = (uint32_t)A.seed, k1 = (uint32_t)(A.seed >> 32);
-  const uint32_t s0 = (uint32_t)A.step, s1 = (uint32_t)(A.step >> 32);
-  if (seg == 0) {
-    uint32_t hw[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      hw[e] = (uint32_t)f16_bits(Sr[2 * e]) | ((uint32_t)f16_bits(Sr[2 * e + 1]) << 16);
-    uint4* dst = reinterpret_cast<uint4*>(A.half + ((size_t)u * kD + i) * kH);
-    dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-  }
+// The INT8 codes of the thread's half row. With every range of the unit in [2^-126, 2^126],
+// fl(1/A) is normal with relative error <= 2^-24, so |S fl(1/A)| <= 1 + 2^-24, which rounds
+// to at most 1: y needs no clamp (CLAMP false). Otherwise y is clamped to [-1, 1].
+template <bool CLAMP>
+__device__ __forceinline__ void damp_codes(const DampLds& L, const DampArgs& A, int u,
+                                           const float (&Sr)[64], uint32_t k0, uint32_t k1,
+                                           uint32_t s0, uint32_t s1) {
+  const int tid = threadIdx.x;
+  const int i = tid >> 1, seg = tid & 1;
+  auto clampy = [](float y) { return CLAMP ? sr_clamp(y) : y; };
   // The row's 112 INT8 positions in Philox blocks of 16 (one block per 16 positions), 56 per
   // thread: half 0 takes blocks 1-3 (positions 16..63), half 1 blocks 5-7 (80..127), each
   // from its own registers, stored as 16 bytes per block; block 4 (64..79, all in half 1's
@@ -272,7 +251,7 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * q + e;  // position 16 blk + j
-        yc[e] = sr_clamp(Sr[16 * b + 16 + j] * L.invA[fidx(16 * blk + j)]);
+        yc[e] = clampy(Sr[16 * b + 16 + j] * L.invA[fidx(16 * blk + j)]);
       }
       int f[4];
       floor_scaled4(yc, f);
@@ -300,7 +279,7 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * q + e;  // position 64 + 8 seg + j
-        yc[e] = sr_clamp(xs[j] * L.invA[fidx(64 + 8 * seg + j)]);
+        yc[e] = clampy(xs[j] * L.invA[fidx(64 + 8 * seg + j)]);
       }
       int f[4];
       floor_scaled4(yc, f);
@@ -312,6 +291,45 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
     }
     *reinterpret_cast<uint2*>(crow + 48 + 8 * seg) = make_uint2(wd[0], wd[1]);
   }
+}
+
+// ranges and requantization of the register-held half rows, stored in place
+__device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int u,
+                                             float (&Sr)[64]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
+  {
+    float m0, m1;
+    int off;
+    half_colmax(Sr, lane, m0, m1, off);
+    L.part[w][p0 + off] = m0;
+    L.part[w][p0 + off + 1] = m1;
+  }
+  if (tid == 0) L.wide = 0;
+  __syncthreads();
+  if (tid < kD && tid >= kH) {
+    const int p = tid;
+    const float m = fmaxf(fmaxf(L.part[0][p], L.part[1][p]), fmaxf(L.part[2][p], L.part[3][p]));
+    const float Aa = (m == 0.0f) ? 1.0f : m;
+    A.R[(size_t)u * kI + (p - kH)] = Aa / 127.0f;
+    L.invA[fidx(p)] = 1.0f / Aa;
+    if (!(Aa >= 0x1p-126f && Aa <= 0x1p126f)) L.wide = 1;
+  }
+  __syncthreads();
+  const uint32_t k0 = (uint32_t)A.seed, k1 = (uint32_t)(A.seed >> 32);
+  const uint32_t s0 = (uint32_t)A.step, s1 = (uint32_t)(A.step >> 32);
+  if (seg == 0) {
+    uint32_t hw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      hw[e] = (uint32_t)f16_bits(Sr[2 * e]) | ((uint32_t)f16_bits(Sr[2 * e + 1]) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(A.half + ((size_t)u * kD + i) * kH);
+    dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+  }
+  const int wide = __builtin_amdgcn_readfirstlane(L.wide);
+  if (wide) damp_codes<true>(L, A, u, Sr, k0, k1, s0, s1);
+  else damp_codes<false>(L, A, u, Sr, k0, k1, s0, s1);
 }
 
 template <int GATE>

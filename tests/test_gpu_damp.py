@@ -50,6 +50,42 @@ def compare(g, r):
         np.array_equal(g.R, r.R)
 
 
+def test_quantize_extreme_ranges_bit_exact(torch_cuda):
+    """Key rows whose range leaves [2^-126, 2^126]: a subnormal range (1/A near 2^127) and
+    a range near the fp32 maximum (1/A subnormal, so y can pass -1 and the clamp decides).
+    Units with such a row take the clamped path, the others the unclamped one; both must
+    match the oracle bit for bit."""
+    from quantized_delta_rule_03_amd import qdr
+
+    w = wl.WORKLOADS[2]
+    n_req, H = 2, 4
+    sel = selection(w, H)
+    rng = np.random.default_rng(11)
+    S = rng.standard_normal((n_req, H, 128, 128)).astype(np.float32)
+    for h in (1, 3):
+        int8_ch = np.flatnonzero(sel[h] == 0)
+        tiny, huge = int8_ch[3], int8_ch[40]
+        S[0, h, :, tiny] = (rng.uniform(-1.0, 1.0, 128) * 2.0 ** -127).astype(np.float32)
+        S[0, h, 5, tiny] = np.float32(2.0 ** -127)
+        S[0, h, 9, tiny] = 0.0
+        # A = 2.4650119e38: fl(1/A) is subnormal and -A fl(1/A) rounds to -(1 + 2^-23),
+        # so floor(127 y + u) reaches -128 for a zero random byte and is clamped
+        big = np.float32(2.4650119e38)
+        S[0, h, :, huge] = (rng.uniform(-1.0, 1.0, 128) * big).astype(np.float32)
+        S[0, h, 20:120, huge] = -big
+        S[0, h, 18, huge] = 0.0
+    gpu = qdr.DampState(n_req, H, w.gate, sel, seed=9)
+    ref = oracle.DampPool(n_req, H, sel, seed=9)
+    for step in (3, 4, 5):
+        gpu.quantize(torch_cuda.from_numpy(S).cuda(), step=step)
+        ref.quantize(S, step=step)
+        half, codes, R = gpu.to_host()
+        assert np.array_equal(half, ref.half), step
+        assert np.array_equal(codes, ref.codes), step
+        assert np.array_equal(R, ref.R), step
+        assert np.abs(codes.astype(np.int32)).max() <= 127
+
+
 def test_init_and_quantize_bit_exact(torch_cuda):
     from quantized_delta_rule_03_amd import qdr
 
