@@ -1222,14 +1222,17 @@ __device__ __forceinline__ float* win_kt(const WinArgs& A, int u) {
   return reinterpret_cast<float*>(A.buf + (size_t)u * window_unit_bytes(A.W));
 }
 
+// WMAX: the largest window the kernel instance serves (the per-token arrays are sized to
+// it; a smaller LDS footprint lets more work-groups share a CU)
+template <int WMAX>
 struct WinLds {
   VecIn vin;  // k, q (logical), v, R, C, a := g_t (logical), b, perm
   StepWork W;
   float ap[kD];  // token gate, physical order
   float gt[kD];  // cumulative gate, physical order
   float qp[kD];  // q, physical order
-  float ab[2][4][kWinMax];  // alpha/beta partials: [which][wave][token]
-  float al[kWinMax], be[kWinMax];
+  float ab[2][4][WMAX];  // alpha/beta partials: [which][wave][token]
+  float al[WMAX], be[WMAX];
   float sp[2][2][kD];  // row sums over buffered tokens: [alpha|beta][token parity][row]
   float xs[kD];        // S0 (g_t k_t) per row
   uint32_t tk_idx[64];  // the unit's compensator tokens
@@ -1253,9 +1256,9 @@ __device__ __forceinline__ UnitInfo win_unit(const WinArgs& A, int u) {
   return win_unit_of(A.meta, A.n_head, A.req_bytes, u);
 }
 
-template <int GATE>
+template <int GATE, int WMAX>
 __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
-  __shared__ __attribute__((aligned(16))) WinLds L;
+  __shared__ __attribute__((aligned(16))) WinLds<WMAX> L;
   const int tid = threadIdx.x;
   const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
   const int u = blockIdx.x;
@@ -2529,14 +2532,17 @@ hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed,
   if (p.n_unit == 0) return hipSuccess;
   WinArgs A{p.meta, p.n_head, W, t, p.req_bytes, packed, rs, cs, buf, q, k, v, a, b, o,
             m, tok_idx, tok_val};
+  const bool small = W <= 64;
   if (gate == GDN) {
-    hipLaunchKernelGGL(k_window_token<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    if (small) hipLaunchKernelGGL((k_window_token<GDN, 64>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    else hipLaunchKernelGGL((k_window_token<GDN, kWinMax>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
     if (t == W - 1) {
       if (m > 0) hipLaunchKernelGGL((k_window_fold<GDN, true>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
       else hipLaunchKernelGGL((k_window_fold<GDN, false>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
     }
   } else {
-    hipLaunchKernelGGL(k_window_token<KDA>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    if (small) hipLaunchKernelGGL((k_window_token<KDA, 64>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
+    else hipLaunchKernelGGL((k_window_token<KDA, kWinMax>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
     if (t == W - 1) {
       if (m > 0) hipLaunchKernelGGL((k_window_fold<KDA, true>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
       else hipLaunchKernelGGL((k_window_fold<KDA, false>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
