@@ -1224,15 +1224,14 @@ __device__ __forceinline__ float* win_kt(const WinArgs& A, int u) {
 
 // WMAX: the largest window the kernel instance serves (the per-token arrays are sized to
 // it; a smaller LDS footprint lets more work-groups share a CU)
+// The token kernel keeps three per-position vectors in StepWork arrays it does not use
+// otherwise (w: the token gate, invA: the cumulative gate, invc: q, all in physical order),
+// and the alpha/beta sums over the waves in place of wave 0's partials.
 template <int WMAX>
 struct WinLds {
   VecIn vin;  // k, q (logical), v, R, C, a := g_t (logical), b, perm
   StepWork W;
-  float ap[kD];  // token gate, physical order
-  float gt[kD];  // cumulative gate, physical order
-  float qp[kD];  // q, physical order
   float ab[2][4][WMAX];  // alpha/beta partials: [which][wave][token]
-  float al[WMAX], be[WMAX];
   float sp[2][2][kD];  // row sums over buffered tokens: [alpha|beta][token parity][row]
   float xs[kD];        // S0 (g_t k_t) per row
   uint32_t tk_idx[64];  // the unit's compensator tokens
@@ -1259,6 +1258,11 @@ __device__ __forceinline__ UnitInfo win_unit(const WinArgs& A, int u) {
 template <int GATE, int WMAX>
 __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   __shared__ __attribute__((aligned(16))) WinLds<WMAX> L;
+  float* const Lap = L.W.w;     // token gate, physical order
+  float* const Lgt = L.W.invA;  // cumulative gate, physical order
+  float* const Lqp = L.W.invc;  // q, physical order
+  float* const Lal = L.ab[0][0];
+  float* const Lbe = L.ab[1][0];
   const int tid = threadIdx.x;
   const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
   const int u = blockIdx.x;
@@ -1285,8 +1289,8 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
     const int j = meta_heads(A.meta)[cur.h].perm[p];
     const float ap = (GATE == KDA) ? A.a[uo + j] : A.a[u];
     const float g = (t > 0 ? gbuf[p] : 1.0f) * ap;
-    L.ap[p] = ap;
-    L.gt[p] = g;
+    Lap[p] = ap;
+    Lgt[p] = g;
     L.vin.a[j] = g;
     L.vin.perm[p] = (uint8_t)j;
     L.vin.k[tid] = A.k[uo + tid];
@@ -1301,7 +1305,7 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
     L.tk_val[tid] = A.tok_val[(size_t)u * A.m + tid];
   }
   __syncthreads();
-  if (tid < kD) L.qp[tid] = L.vin.q[L.vin.perm[tid]];
+  if (tid < kD) Lqp[tid] = L.vin.q[L.vin.perm[tid]];
 
   // 2. exact S0 (g_t k_t), S0 (g_t q_t): digit planes of cf k and cf q, cf = fl(g_t R)
   prep<KDA, true>(L.vin, L.W, w, lane, Bw);
@@ -1338,9 +1342,9 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
     float apl[4], kpl[4], qpl[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      apl[m] = L.ap[pb + m];
+      apl[m] = Lap[pb + m];
       kpl[m] = L.W.kp[pb + m];
-      qpl[m] = L.qp[pb + m];
+      qpl[m] = Lqp[pb + m];
     }
     for (int i0 = 0; i0 < t; i0 += 8) {
       const int i = i0 + tk;
@@ -1370,8 +1374,8 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   }
   __syncthreads();
   if (tid < t) {
-    L.al[tid] = ((L.ab[0][0][tid] + L.ab[0][1][tid]) + L.ab[0][2][tid]) + L.ab[0][3][tid];
-    L.be[tid] = ((L.ab[1][0][tid] + L.ab[1][1][tid]) + L.ab[1][2][tid]) + L.ab[1][3][tid];
+    Lal[tid] = ((L.ab[0][0][tid] + L.ab[0][1][tid]) + L.ab[0][2][tid]) + L.ab[0][3][tid];
+    Lbe[tid] = ((L.ab[1][0][tid] + L.ab[1][1][tid]) + L.ab[1][2][tid]) + L.ab[1][3][tid];
   }
   __syncthreads();
 
@@ -1388,14 +1392,14 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
       for (int u = 0; u < 4; ++u) wv[u] = Wv[(size_t)(i + 2 * u) * kD + row];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        sa[u] = fmaf(L.al[i + 2 * u], wv[u], sa[u]);
-        sb[u] = fmaf(L.be[i + 2 * u], wv[u], sb[u]);
+        sa[u] = fmaf(Lal[i + 2 * u], wv[u], sa[u]);
+        sb[u] = fmaf(Lbe[i + 2 * u], wv[u], sb[u]);
       }
     }
     for (int u = 0; i < t; i += 2, ++u) {
       const float wi = Wv[(size_t)i * kD + row];
-      sa[u] = fmaf(L.al[i], wi, sa[u]);
-      sb[u] = fmaf(L.be[i], wi, sb[u]);
+      sa[u] = fmaf(Lal[i], wi, sa[u]);
+      sb[u] = fmaf(Lbe[i], wi, sb[u]);
     }
     L.sp[0][par][row] = (sa[0] + sa[1]) + (sa[2] + sa[3]);
     L.sp[1][par][row] = (sb[0] + sb[1]) + (sb[2] + sb[3]);
@@ -1424,7 +1428,7 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
                               (double)(L.sp[1][0][i] + L.sp[1][1][i]) + to) + (double)wt * kq);
     Wv[(size_t)t * kD + i] = wt;
     Kt[(size_t)t * kD + i] = L.W.kp[i];
-    gbuf[i] = L.gt[i];
+    gbuf[i] = Lgt[i];
   }
 }
 
