@@ -627,7 +627,14 @@ static int check_damp(const qdr_damp_desc* d, std::vector<uint8_t>* perm) {
 }
 
 static qdr::DampPool damp_pool(const qdr_damp_desc* d, const void* meta) {
-  return {static_cast<const uint8_t*>(meta), d->n_head, d->n_req * d->n_head, d->gate};
+  int ident = 1;
+  for (int h = 0; h < d->n_head && ident; ++h)
+    for (int j = 0; j < qdr::kD; ++j)
+      if ((d->sel[(size_t)h * qdr::kD + j] != 0) != (j < qdr::kDampHalf)) {
+        ident = 0;
+        break;
+      }
+  return {static_cast<const uint8_t*>(meta), d->n_head, d->n_req * d->n_head, d->gate, ident};
 }
 
 int qdr_damp_select(int32_t gate, int32_t n_head, const double* halflife, uint8_t* sel_out) {

@@ -85,6 +85,7 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 struct DampArgs {
   const uint8_t* perm;  // [n_head][128]
   int n_head, gate;
+  int ident;  // perm is the identity for every head (no position-map load)
   uint16_t* half;
   int8_t* codes;
   float* R;
@@ -338,7 +339,9 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
   const int tid = threadIdx.x, u = blockIdx.x, h = u % A.n_head;
   const size_t uo = (size_t)u * kD;
   if (tid < kD) {
-    const int p = tid, j = A.perm[(size_t)h * kD + p];
+    const int p = tid;
+    int j = p;
+    if (!A.ident) j = A.perm[(size_t)h * kD + p];
     const float kv = A.k[uo + j];
     L.kp[fidx(p)] = kv;
     L.kd[didx(p)] = kv;
@@ -439,7 +442,8 @@ hipError_t launch_damp(int op, const DampPool& p, uint16_t* half, int8_t* codes,
                        const float* b, float* o, const float* S, float* Sout, uint64_t seed,
                        uint64_t step, hipStream_t s) {
   if (p.n_unit == 0) return hipSuccess;
-  DampArgs A{p.perm, p.n_head, p.gate, half, codes, R, q, k, v, a, b, o, S, Sout, seed, step};
+  DampArgs A{p.perm, p.n_head, p.gate, p.ident, half, codes, R, q, k, v, a, b, o, S, Sout, seed,
+             step};
   const dim3 grid(p.n_unit), block(kThreads);
   switch (op) {
     case kDampInit: hipLaunchKernelGGL(k_damp_init, grid, block, 0, s, A); break;

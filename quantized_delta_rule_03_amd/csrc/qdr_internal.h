@@ -99,6 +99,7 @@ constexpr int kDampHalf = 16;  // key channels per head kept in binary16
 struct DampPool {
   const uint8_t* perm;  // device [n_head][128]: physical position -> logical channel
   int n_head, n_unit, gate;
+  int ident;  // every head selects channels 0..15 (then perm is the identity)
 };
 enum { kDampInit = 0, kDampQuantize = 1, kDampStep = 2, kDampDequantize = 3 };
 hipError_t launch_damp(int op, const DampPool& p, uint16_t* half, int8_t* codes, float* R,
