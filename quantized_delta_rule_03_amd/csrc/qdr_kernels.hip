@@ -1216,6 +1216,7 @@ struct WinArgs {
   int m;
   uint16_t* tok_idx;
   float* tok_val;
+  int ubits;  // every head of this one width (then no metadata is read), or 0
 };
 
 __device__ __forceinline__ float* win_kt(const WinArgs& A, int u) {
@@ -1266,7 +1267,18 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   const int tid = threadIdx.x;
   const int w = wave_id(), lane = tid & 63, rg = lane & 15, jg = lane >> 4;
   const int u = blockIdx.x;
-  const UnitInfo cur = win_unit(A, u);
+  // with every head of one width the tile offset follows from the unit index and the
+  // key order is the logical one: no dependent metadata load before the state's rows
+  UnitInfo cur;
+  if (A.ubits) {
+    const int r = u / A.n_head, h = u - r * A.n_head;
+    cur.un = (uint32_t)u;
+    cur.toff = (uint64_t)r * A.req_bytes + (uint64_t)h * (A.req_bytes / (uint32_t)A.n_head);
+    cur.sb = (uint32_t)A.ubits * 0x01010101u;
+    cur.h = (uint32_t)h;
+  } else {
+    cur = win_unit(A, u);
+  }
   const Seg sg = seg_from(cur.sb, w);
   const int Bw = sg.bits;
   const size_t uo = (size_t)u * kD;
@@ -1286,7 +1298,8 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   // 1. this token's vectors to LDS
   if (tid < kD) {
     const int p = tid;
-    const int j = meta_heads(A.meta)[cur.h].perm[p];
+    int j = p;
+    if (!A.ubits) j = meta_heads(A.meta)[cur.h].perm[p];
     const float ap = (GATE == KDA) ? A.a[uo + j] : A.a[u];
     const float g = (t > 0 ? gbuf[p] : 1.0f) * ap;
     Lap[p] = ap;
@@ -2529,13 +2542,23 @@ hipError_t launch_step(const Pool& p, int gate, uint8_t* packed, float* rs, floa
   return hipGetLastError();
 }
 
+// the width of a pool whose heads all have one width, else 0: such a pool's tiles sit at
+// h * req_bytes / n_head, in key order (a single-width head keeps the logical order)
+static int uniform_width(const Pool& p) {
+  static const int widths[3] = {8, 6, 4};
+  if (p.uniform)
+    for (int c = 0; c < 3; ++c)
+      if (p.n_class[c] == p.n_head) return widths[c];
+  return 0;
+}
+
 hipError_t launch_window(const Pool& p, int gate, int W, int t, uint8_t* packed, float* rs,
                          float* cs, uint8_t* buf, const float* q, const float* k, const float* v,
                          const float* a, const float* b, float* o, int m, uint16_t* tok_idx,
                          float* tok_val, hipStream_t s) {
   if (p.n_unit == 0) return hipSuccess;
   WinArgs A{p.meta, p.n_head, W, t, p.req_bytes, packed, rs, cs, buf, q, k, v, a, b, o,
-            m, tok_idx, tok_val};
+            m, tok_idx, tok_val, uniform_width(p)};
   const bool small = W <= 64;
   if (gate == GDN) {
     if (small) hipLaunchKernelGGL((k_window_token<GDN, 64>), dim3(p.n_unit), dim3(kThreads), 0, s, A);
@@ -2560,14 +2583,7 @@ hipError_t launch_chunk(const Pool& p, int gate, int T, uint8_t* packed, float* 
                         const float* b, float* o, int m, uint16_t* tok_idx, float* tok_val,
                         const float* S_in, hipStream_t s) {
   if (p.n_unit == 0 || (T == 0 && !S_in)) return hipSuccess;
-  // a pool whose heads all have one width: its tiles sit at h * req_bytes / n_head in key
-  // order (a single-width head keeps the logical order)
-  int ubits = 0;
-  if (p.uniform) {
-    static const int widths[3] = {8, 6, 4};
-    for (int c = 0; c < 3; ++c)
-      if (p.n_class[c] == p.n_head) ubits = widths[c];
-  }
+  const int ubits = uniform_width(p);
   ChunkArgs A{p.meta, p.n_head, p.n_unit, T, p.req_bytes, packed, rs, cs, q, k, v, a, b, o,
               m, tok_idx, tok_val, S_in, ubits};
   if (gate == GDN) hipLaunchKernelGGL(k_chunk<GDN>, dim3(p.n_unit), dim3(kThreads), 0, s, A);
