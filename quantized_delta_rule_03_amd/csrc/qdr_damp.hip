@@ -21,11 +21,13 @@
 //                      the counter (i*8 + p/16, unit, step lo, step hi) and key (seed lo,
 //                      seed hi), times 2^-8.
 //
-// Work decomposition: one work-group of 256 threads per unit. Thread t holds value row
-// t >> 1 at the 64 positions of half t & 1 in registers (the fp64 half sums of the
-// prediction and the readout are then in-thread and in position order); the key-row
-// absmax is a shuffle reduce-scatter over the wave's 32 rows, then a max over the four
-// waves through LDS. LDS holds only the input vectors and the ranges (3.5 KB).
+// Work decomposition: one work-group of 256 threads per unit. Thread t holds 64 positions
+// of value row t >> 1 in registers, half s = t & 1 of the row's positions (dpos): 8
+// binary16 positions, 48 INT8 positions that make three whole Philox blocks and the half
+// of block 4 that the thread codes, so that both threads of a row do the same work (the
+// fp64 half sums of the prediction and the readout are in-thread); the key-row absmax is a
+// shuffle reduce-scatter over the wave's 32 rows, then a max over the four waves through
+// LDS. LDS holds only the input vectors and the ranges (3.5 KB).
 #include "qdr_internal.h"
 
 namespace qdr {
@@ -43,6 +45,14 @@ constexpr int kPadF = 4;  // floats
 constexpr int kPadD = 2;  // doubles
 __device__ __forceinline__ int fidx(int p) { return p + (p >> 6) * kPadF; }
 __device__ __forceinline__ int didx(int p) { return p + (p >> 6) * kPadD; }
+
+// Physical position of register e of a thread of half s: registers 0..7 hold the binary16
+// positions 8 s + e; 8..55 the INT8 positions 16..63 (s = 0) or 80..127 (s = 1), Philox
+// blocks 1-3 or 5-7; 56..63 the positions 64..71 or 72..79, its half of block 4. Codes
+// [0, 48) of the thread lie at byte 64 s of the row's 112, codes [48, 56) at byte 48 + 8 s.
+__device__ __forceinline__ int dpos(int s, int e) {
+  return e < 8 ? 8 * s + e : (e < 56 ? 8 + 64 * s + e : 8 + 8 * s + e);
+}
 
 struct DampLds {
   double kd[kD + kPadD], qd[kD + kPadD];  // k, q in fp64 for the dot products
@@ -188,12 +198,6 @@ __device__ __forceinline__ void half_colmax(float (&a)[64], int lane, float& m0,
         2 * (int)b1;
 }
 
-// Row i's half-row pointers: raw code words q = 0..3 hold the codes of positions
-// p0 + 16q .. p0 + 16q + 15 (for half 0, word 0 would be the binary16 positions: unused).
-__device__ __forceinline__ int8_t* code_word(int8_t* crow, int seg, int q) {
-  return crow + (seg ? 48 + 16 * q : 16 * (q - 1));
-}
-
 // Stochastic rounding: floor(127 y + r 2^-8) clamped to [-127, 127], r the row's random
 // byte. Scaled by 2^8 it is floor((floor(127 2^8 y) + r) / 2^8): r is an integer, so it moves
 // out of the inner floor, and the floor of a floor quotient is the floor of the quotient.
@@ -234,10 +238,9 @@ __device__ __forceinline__ void damp_codes(const DampLds& L, const DampArgs& A, 
   const int i = tid >> 1, seg = tid & 1;
   auto clampy = [](float y) { return CLAMP ? sr_clamp(y) : y; };
   // The row's 112 INT8 positions in Philox blocks of 16 (one block per 16 positions), 56 per
-  // thread: half 0 takes blocks 1-3 (positions 16..63), half 1 blocks 5-7 (80..127), each
-  // from its own registers, stored as 16 bytes per block; block 4 (64..79, all in half 1's
-  // registers) is generated by both, half 0 coding 64..71 from its partner's values and
-  // half 1 72..79 from its own, 8 bytes each.
+  // thread: blocks 1-3 (half 0) or 5-7 (half 1) from registers 8..55, stored as 16 bytes per
+  // block; block 4 (positions 64..79) is generated by both threads, each coding its 8
+  // positions (registers 56..63), 8 bytes each.
   int8_t* crow = A.codes + ((size_t)u * kD + i) * kI;
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
@@ -251,8 +254,8 @@ __device__ __forceinline__ void damp_codes(const DampLds& L, const DampArgs& A, 
       float yc[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int j = 4 * q + e;  // position 16 blk + j
-        yc[e] = clampy(Sr[16 * b + 16 + j] * L.invA[fidx(16 * blk + j)]);
+        const int j = 4 * q + e;  // position 16 blk + j, register 8 + 16 b + j
+        yc[e] = clampy(Sr[8 + 16 * b + j] * L.invA[fidx(16 * blk + j)]);
       }
       int f[4];
       floor_scaled4(yc, f);
@@ -267,20 +270,14 @@ __device__ __forceinline__ void damp_codes(const DampLds& L, const DampArgs& A, 
   {
     const uint4 r = philox4x32_10((uint32_t)(i * 8 + 4), (uint32_t)u, s0, s1, k0, k1);
     const uint32_t rw[2] = {seg ? r.z : r.x, seg ? r.w : r.y};
-    float xs[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float other = dpp_xor1(Sr[j]);  // half 1's position 64 + j, for half 0
-      xs[j] = seg ? Sr[8 + j] : other;
-    }
     uint32_t wd[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       float yc[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int j = 4 * q + e;  // position 64 + 8 seg + j
-        yc[e] = clampy(xs[j] * L.invA[fidx(64 + 8 * seg + j)]);
+        const int j = 4 * q + e;  // position 64 + 8 seg + j, register 56 + j
+        yc[e] = clampy(Sr[56 + j] * L.invA[fidx(64 + 8 * seg + j)]);
       }
       int f[4];
       floor_scaled4(yc, f);
@@ -298,13 +295,13 @@ __device__ __forceinline__ void damp_codes(const DampLds& L, const DampArgs& A, 
 __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int u,
                                              float (&Sr)[64]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
+  const int i = tid >> 1, seg = tid & 1;
   {
     float m0, m1;
     int off;
     half_colmax(Sr, lane, m0, m1, off);
-    L.part[w][p0 + off] = m0;
-    L.part[w][p0 + off + 1] = m1;
+    L.part[w][dpos(seg, off)] = m0;  // registers off, off + 1: adjacent positions
+    L.part[w][dpos(seg, off) + 1] = m1;
   }
   if (tid == 0) L.wide = 0;
   __syncthreads();
@@ -319,14 +316,13 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
   __syncthreads();
   const uint32_t k0 = (uint32_t)A.seed, k1 = (uint32_t)(A.seed >> 32);
   const uint32_t s0 = (uint32_t)A.step, s1 = (uint32_t)(A.step >> 32);
-  if (seg == 0) {
-    uint32_t hw[8];
+  {
+    uint32_t hw[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 4; ++e)
       hw[e] = (uint32_t)f16_bits(Sr[2 * e]) | ((uint32_t)f16_bits(Sr[2 * e + 1]) << 16);
-    uint4* dst = reinterpret_cast<uint4*>(A.half + ((size_t)u * kD + i) * kH);
-    dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    dst[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    *reinterpret_cast<uint4*>(A.half + ((size_t)u * kD + i) * kH + 8 * seg) =
+        make_uint4(hw[0], hw[1], hw[2], hw[3]);
   }
   const int wide = __builtin_amdgcn_readfirstlane(L.wide);
   if (wide) damp_codes<true>(L, A, u, Sr, k0, k1, s0, s1);
@@ -349,52 +345,48 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
     const float g = (GATE == KDA) ? A.a[uo + j] : A.a[u];
     L.cf[fidx(p)] = p < kH ? g : g * A.R[(size_t)u * kI + (p - kH)];
   }
-  const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
-  // this thread's half row: binary16 words (half 0) and code words
-  uint4 raw[4], hraw[2];
+  const int i = tid >> 1, seg = tid & 1;
+  // this thread's half row: 8 binary16 values and 56 codes (see dpos)
+  const uint4 hraw = *reinterpret_cast<const uint4*>(A.half + (uo + i) * kH + 8 * seg);
   const int8_t* crow = A.codes + (uo + i) * kI;
+  uint4 craw[3];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    raw[q] = (q == 0 && seg == 0) ? make_uint4(0, 0, 0, 0)
-                                  : *reinterpret_cast<const uint4*>(code_word(const_cast<int8_t*>(crow), seg, q));
-  if (seg == 0) {
-    const uint4* hr = reinterpret_cast<const uint4*>(A.half + (uo + i) * kH);
-    hraw[0] = hr[0];
-    hraw[1] = hr[1];
-  } else {
-    hraw[0] = hraw[1] = make_uint4(0, 0, 0, 0);
-  }
+  for (int q = 0; q < 3; ++q) craw[q] = *reinterpret_cast<const uint4*>(crow + 64 * seg + 16 * q);
+  const uint2 caw = *reinterpret_cast<const uint2*>(crow + 48 + 8 * seg);
   __syncthreads();
   // gated dequantization into registers
   float Sr[64];
 #pragma unroll
   for (int e = 0; e < 64; ++e) {
-    const uint4 x = raw[e >> 4];
-    const uint32_t word = ((e >> 2) & 3) == 0 ? x.x : (((e >> 2) & 3) == 1 ? x.y : (((e >> 2) & 3) == 2 ? x.z : x.w));
-    const float c = (float)(int8_t)(word >> (8 * (e & 3)));
-    if (e < kH) {
-      const uint4 hx = hraw[e >> 3];
-      const int hq = (e >> 1) & 3;
-      const uint32_t hw = hq == 0 ? hx.x : (hq == 1 ? hx.y : (hq == 2 ? hx.z : hx.w));
-      const float hv = f16_value((uint16_t)(hw >> (16 * (e & 1))));
-      Sr[e] = (seg == 0 ? hv : c) * L.cf[fidx(p0 + e)];
+    float x;
+    if (e < 8) {
+      const int hq = e >> 1;
+      const uint32_t hw = hq == 0 ? hraw.x : (hq == 1 ? hraw.y : (hq == 2 ? hraw.z : hraw.w));
+      x = f16_value((uint16_t)(hw >> (16 * (e & 1))));
+    } else if (e < 56) {
+      const int c = e - 8, cq = (c >> 2) & 3;
+      const uint4 cx = craw[c >> 4];
+      const uint32_t word = cq == 0 ? cx.x : (cq == 1 ? cx.y : (cq == 2 ? cx.z : cx.w));
+      x = (float)(int8_t)(word >> (8 * (c & 3)));
     } else {
-      Sr[e] = c * L.cf[fidx(p0 + e)];
+      const int c = e - 56;
+      x = (float)(int8_t)((c < 4 ? caw.x : caw.y) >> (8 * (c & 3)));
     }
+    Sr[e] = x * L.cf[fidx(dpos(seg, e))];
   }
-  // u_i: this thread's fp64 half sum in position order (a product of two fp32 values is exact
-  // in fp64, so each fma adds exactly the product), the pair combined as s0 + s1
+  // u_i: this thread's fp64 half sum in register order (a product of two fp32 values is
+  // exact in fp64, so each fma adds exactly the product), the pair combined as s0 + s1
   double s = 0.0;
 #pragma unroll
-  for (int e = 0; e < 64; ++e) s = fma((double)Sr[e], L.kd[didx(p0 + e)], s);
+  for (int e = 0; e < 64; ++e) s = fma((double)Sr[e], L.kd[didx(dpos(seg, e))], s);
   const double so = dpp_xor1(s);
   const float uu = (float)(seg ? so + s : s + so);
   const float w = A.b[u] * (A.v[uo + i] - uu);
   double t = 0.0;
 #pragma unroll
   for (int e = 0; e < 64; ++e) {
-    Sr[e] = fmaf(w, L.kp[fidx(p0 + e)], Sr[e]);
-    t = fma((double)Sr[e], L.qd[didx(p0 + e)], t);
+    Sr[e] = fmaf(w, L.kp[fidx(dpos(seg, e))], Sr[e]);
+    t = fma((double)Sr[e], L.qd[didx(dpos(seg, e))], t);
   }
   const double to = dpp_xor1(t);
   if (seg == 0) A.o[uo + i] = (float)(t + to);
@@ -404,12 +396,12 @@ __global__ void __launch_bounds__(kThreads) k_damp_step(DampArgs A) {
 __global__ void __launch_bounds__(kThreads) k_damp_quantize(DampArgs A) {
   __shared__ __attribute__((aligned(16))) DampLds L;
   const int tid = threadIdx.x, u = blockIdx.x, h = u % A.n_head;
-  const int i = tid >> 1, seg = tid & 1, p0 = 64 * seg;
+  const int i = tid >> 1, seg = tid & 1;
   const float* Si = A.S + ((size_t)u * kD + i) * kD;
   const uint8_t* perm = A.perm + (size_t)h * kD;
   float Sr[64];
 #pragma unroll
-  for (int e = 0; e < 64; ++e) Sr[e] = Si[perm[p0 + e]];
+  for (int e = 0; e < 64; ++e) Sr[e] = Si[perm[dpos(seg, e)]];
   damp_requant(L, A, u, Sr);
 }
 
