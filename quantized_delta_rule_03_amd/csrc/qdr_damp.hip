@@ -309,8 +309,8 @@ __device__ __forceinline__ void damp_requant(DampLds& L, const DampArgs& A, int 
     const int p = tid;
     const float m = fmaxf(fmaxf(L.part[0][p], L.part[1][p]), fmaxf(L.part[2][p], L.part[3][p]));
     const float Aa = (m == 0.0f) ? 1.0f : m;
-    A.R[(size_t)u * kI + (p - kH)] = Aa / 127.0f;
-    L.invA[fidx(p)] = 1.0f / Aa;
+    A.R[(size_t)u * kI + (p - kH)] = div_qmax(Aa, 8);  // Aa / 127
+    L.invA[fidx(p)] = recip_rn(Aa);
     if (!(Aa >= 0x1p-126f && Aa <= 0x1p126f)) L.wide = 1;
   }
   __syncthreads();

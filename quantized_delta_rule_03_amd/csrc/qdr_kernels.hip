@@ -46,37 +46,6 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
-// 1/x, correctly rounded (the IEEE division): for x in [2^-126, 2^126) the hardware
-// reciprocal followed by one Newton step r = y + y(1 - xy) (two fmas) is exactly that --
-// checked on the GPU against the division for every fp32 pattern of that range; for
-// subnormal x, or x whose reciprocal is subnormal, the division itself runs (such
-// scales are rare, so the lanes almost never take that branch).
-__device__ __forceinline__ float recip_rn(float x) {
-  const float y = __builtin_amdgcn_rcpf(x);
-  const float e = fmaf(-x, y, 1.0f);
-  float r = fmaf(e, y, y);
-  if (__builtin_amdgcn_ballot_w64(!(x >= 0x1p-126f && x < 0x1p126f))) {
-    // a branch the wave skips when no lane needs it (the empty volatile asm keeps the
-    // compiler from evaluating the division unconditionally)
-    float xx = x;
-    asm volatile("" : "+v"(xx));
-    if (!(xx >= 0x1p-126f && xx < 0x1p126f)) r = 1.0f / xx;
-  }
-  return r;
-}
-
-// a / Qmax for Qmax = 2^(b-1) - 1 (b in {4, 6, 8}), correctly rounded: the product with
-// fl(1/Qmax) and one remainder correction, q = q0 + fl(1/Qmax)(a - q0 Qmax) (two fmas,
-// the remainder exact) -- equal to the IEEE division for every positive fp32 a and each
-// of the three Qmax (checked on the GPU over every fp32 pattern).
-__device__ __forceinline__ float div_qmax(float a, int b) {
-  const float q = b == 8 ? 127.0f : (b == 6 ? 31.0f : 7.0f);
-  const float iq = b == 8 ? 1.0f / 127.0f : (b == 6 ? 1.0f / 31.0f : 1.0f / 7.0f);
-  const float q0 = a * iq;
-  const float r = fmaf(-q0, q, a);
-  return fmaf(r, iq, q0);
-}
-
 struct Seg {
   int bits;
   uint32_t off;  // byte offset of the segment inside the tile
