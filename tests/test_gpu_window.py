@@ -35,7 +35,7 @@ def token_inputs(w, t, n_req, n_head):
     return {k: np.ascontiguousarray(v[:, :n_head]) for k, v in inp.items()}
 
 
-def run_windows(torch, w, n_req, n_head, bits, W, n_windows, S0, name):
+def run_windows(torch, w, n_req, n_head, bits, W, n_windows, S0, name, gate_fn=None):
     from quantized_delta_rule_03_amd import qdr
 
     gpu = qdr.StatePool(n_req, n_head, w.gate, bits, window=W)
@@ -46,6 +46,9 @@ def run_windows(torch, w, n_req, n_head, bits, W, n_windows, S0, name):
     worst_o, worst_flip, worst_lsb, worst_o_free = 0.0, 0.0, 0, 0.0
     for win in range(n_windows):
         toks = [token_inputs(w, win * W + t, n_req, n_head) for t in range(W)]
+        if gate_fn is not None:
+            for t, x in enumerate(toks):
+                x["a"] = gate_fn(win * W + t, x["a"])
         stack = {k: np.stack([x[k] for x in toks]) for k in toks[0]}
         tf = gpu_to_oracle(gpu, bits)  # teacher-forced: the GPU's state at the window start
         o_tf = tf.window(w.gate, stack["q"], stack["k"], stack["v"], stack["a"], stack["b"])
@@ -113,6 +116,25 @@ def test_window_longest(torch_cuda):
     rng = np.random.default_rng(6)
     S0 = (0.1 * rng.standard_normal((1, 4, 128, 128))).astype(np.float32)
     run_windows(torch_cuda, w, 1, 4, bits, 256, 1, S0, "kda mixed W=256")
+
+
+def test_window_extreme_gates(torch_cuda):
+    """Gates of exactly 0 and 1 and tiny values: the buffered keys are decayed one token at
+    a time and the cumulative gate is a running product, so nothing overflows or divides."""
+    w = wl.WORKLOADS[2]
+    bits = bits_for(w, n_head=4)
+    rng = np.random.default_rng(9)
+    S0 = (0.1 * rng.standard_normal((1, 4, 128, 128))).astype(np.float32)
+
+    def gates(t, a):
+        g = np.random.default_rng(2000 + t)
+        x = a.copy()
+        x[..., :16] = 1e-30                      # tiny on some channels
+        x[..., 16:24] = 0.0 if t % 5 == 0 else 1.0  # resets and no decay
+        x[..., 24:32] = g.uniform(0.0, 1e-3, size=x[..., 24:32].shape).astype(np.float32)
+        return x.astype(np.float32)
+
+    run_windows(torch_cuda, w, 1, 4, bits, 24, 2, S0, "kda extreme gates W=24", gates)
 
 
 def test_window_zero_requests_is_noop(torch_cuda):
