@@ -78,16 +78,20 @@ def profile_record(path=PROFILE):
 
 def window_algorithmic_bytes(tile_bytes: int, n_unit: int, W: int) -> int:
     """Bytes one window (W tokens + fold) must move: per token the fixed packed state and
-    its scales, q/k/v, the per-channel gate and b, o; the buffered (k, w) pairs of the
-    earlier tokens read and the decayed keys written back, the new pair appended, the
-    cumulative gate read and written; at the end the buffer and state read once more and
-    the requantized state and scales written."""
+    its scales, q/k/v, the per-channel gate and b, o; the buffered (key, w) pairs of the
+    earlier tokens read, the new pair appended, the cumulative gate and the keys' decay
+    since their base read and written; at the last token the buffered keys written back
+    decayed (the base moves there; on this workload no gate product falls low enough to
+    move it earlier); at the end the buffer and state read once more and the requantized
+    state and scales written."""
     per_unit = 0
     for t in range(W):
         per_unit += tile_bytes + 2 * 512      # packed state + key-row and value-column scales
         per_unit += 3 * 512 + 512 + 4 + 512   # q, k, v, a (per channel), b; o
-        per_unit += 1024 * t + 512 * t        # buffer read (keys, deltas); decayed keys written
-        per_unit += 1024 + (512 if t else 0) + 512  # append (k, w); gate read + written
+        per_unit += 1024 * t                  # buffer read (keys, deltas)
+        per_unit += 1024 + 2 * ((512 if t else 0) + 512)  # append (k, w); g and h read + written
+        if t == W - 1:
+            per_unit += 512 * t               # decayed keys written (the base moves)
     per_unit += tile_bytes + 1024 + 1024 * W + 512  # fold: state, scales, buffer, gate read
     per_unit += tile_bytes + 1024                   # requantized state and scales written
     return per_unit * n_unit

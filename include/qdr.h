@@ -175,8 +175,8 @@ int qdr_decode_window(const qdr_desc *desc, const void *meta, void *packed,
  * which is what carries a window from token to token (nothing in it needs clearing: token
  * t = 0 ignores what it holds). Every call on one GPU shares it, so windows of different
  * states must not interleave on a GPU, and calls on one GPU that overlap (other streams,
- * other threads) race. Limit: n_req * n_head * (W * 1024 + 512) bytes <= 32 MiB (e.g.
- * 508 units at W = 64); a larger pool returns QDR_EUNSUPPORTED with the sizes in the error
+ * other threads) race. Limit: n_req * n_head * (W * 1024 + 1024) bytes <= 32 MiB (e.g.
+ * 504 units at W = 64); a larger pool returns QDR_EUNSUPPORTED with the sizes in the error
  * text. Errors: as qdr_decode_window. */
 int qdr_decode_window_static(const qdr_desc *desc, const void *meta, void *packed,
                              float *row_scale, float *col_scale, int32_t t, const float *q,

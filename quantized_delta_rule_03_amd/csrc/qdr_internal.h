@@ -54,8 +54,9 @@ inline size_t meta_bytes(int n_head) {
 }
 
 // Bytes of one window-buffer slot set per unit: W slots of (kappa[128], delta[128]) fp32
-// plus the running cumulative gate g[128] fp32.
-__host__ __device__ inline size_t window_unit_bytes(int W) { return (size_t)W * 2 * kD * 4 + (size_t)kD * 4; }
+// plus the running cumulative gate g[128] and the buffered keys' decay since their base
+// h[128], fp32.
+__host__ __device__ inline size_t window_unit_bytes(int W) { return (size_t)W * 2 * kD * 4 + (size_t)2 * kD * 4; }
 
 struct Pool {
   const void* meta;

@@ -446,7 +446,8 @@ struct VecIn {
   float k[kD], q[kD];  // logical key order
   float v[kD], R[kD];  // R: key-row scales, physical order
   float C[kD], a[kD];  // C: value-column scales; a: KDA gate, logical order
-  float b, ag, pad0, pad1;  // write strength; GDN gate
+  float b, ag;               // write strength; GDN gate
+  uint32_t flag[2];          // per-wave flags of the window token kernel
   uint8_t perm[kD];         // physical position -> logical key channel
 };
 
@@ -1155,15 +1156,20 @@ k_step(StepArgs A) {
 //   o_t = S0 (g_t q_t) + sum_{i<t} w_i (Kt_i(t) . q_t) + (k_t . q_t) w_t.
 // Per token (k_window_token): S0 (g_t k_t) and S0 (g_t q_t) are exact matrix-core
 // digit-plane sums (the prediction machinery of the decode step with the column factor
-// cf_j = fl(g_tj R_j), row factor c_i); the buffered keys are decayed in place and
-// dotted with k_t and q_t, one lane per buffered token; the row sums over buffered
-// tokens run one thread per value row. At t = W-1 (k_window_fold) the buffered
-// updates are folded into the state on the matrix cores (bf16 in, fp32 accumulate,
-// each fp32 operand split into three bf16 parts so the contraction keeps fp32
-// accuracy) and the state is refit and requantized once.
+// cf_j = fl(g_tj R_j), row factor c_i); the buffered keys are dotted with k_t and q_t,
+// eight lanes per buffered token; the row sums over buffered tokens run one thread per
+// value row. The buffered keys are kept relative to a base token b: with
+// h_t = a_{b+1} * ... * a_t, the buffer holds B_i = Kt_i(b) for i <= b and k_i / h_i for
+// i > b, so that Kt_i(t) = B_i h_t and Kt_i(t) . k_t = B_i . (h_t k_t) -- no rewrite per
+// token. When some h_t drops below 2^-80 (and at t = W-1) the base moves to t: the keys
+// are decayed in place to B_i h_t = Kt_i(t) and h_t restarts at 1, which keeps every B_i
+// within 2^80 of its key (gates of 0 move the base at once). At t = W-1 (k_window_fold)
+// the buffered updates are folded into the state on the matrix cores (bf16 in, fp32
+// accumulate, each fp32 operand split into three bf16 parts so the contraction keeps
+// fp32 accuracy) and the state is refit and requantized once.
 //
 // Buffer of one unit (fp32): Kt[W][128] (physical key order), Wv[W][128] (value rows),
-// g[128] (physical key order).
+// g[128] (the cumulative gate g_t, physical order), h[128] (h_t, physical order).
 // ------------------------------------------------------------------------------
 constexpr int kWinMax = kWindowMax;
 
@@ -1228,7 +1234,7 @@ __device__ __forceinline__ UnitInfo win_unit(const WinArgs& A, int u) {
 template <int GATE, int WMAX>
 __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   __shared__ __attribute__((aligned(16))) WinLds<WMAX> L;
-  float* const Lap = L.W.w;     // token gate, physical order
+  float* const Lap = L.W.w;     // h_t, the buffered keys' decay since the base, physical order
   float* const Lgt = L.W.invA;  // cumulative gate, physical order
   float* const Lqp = L.W.invc;  // q, physical order
   float* const Lal = L.ab[0][0];
@@ -1255,6 +1261,7 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   float* Kt = win_kt(A, u);
   float* Wv = Kt + (size_t)W * kD;
   float* gbuf = Wv + (size_t)W * kD;
+  float* hbuf = gbuf + kD;
   // the fixed state's rows, straight from HBM (each is used once per token), in flight
   // while the token's vectors are staged and the digit planes formed
   Raw raw[8];
@@ -1264,14 +1271,17 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
     for (int rr = 0; rr < 8; ++rr) raw[rr] = load_row_any(seg, Bw, rg + 16 * rr, jg);
   }
 
-  // 1. this token's vectors to LDS
+  // 1. this token's vectors to LDS; whether the base moves to this token
+  bool low = false;
   if (tid < kD) {
     const int p = tid;
     int j = p;
     if (!A.ubits) j = meta_heads(A.meta)[cur.h].perm[p];
     const float ap = (GATE == KDA) ? A.a[uo + j] : A.a[u];
     const float g = (t > 0 ? gbuf[p] : 1.0f) * ap;
-    Lap[p] = ap;
+    const float h = t > 0 ? hbuf[p] * ap : 1.0f;  // the base starts at token 0
+    low = !(h >= 0x1p-80f);
+    Lap[p] = h;
     Lgt[p] = g;
     L.vin.a[j] = g;
     L.vin.perm[p] = (uint8_t)j;
@@ -1286,8 +1296,13 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
     L.tk_idx[tid] = A.tok_idx[(size_t)u * A.m + tid];
     L.tk_val[tid] = A.tok_val[(size_t)u * A.m + tid];
   }
+  {
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(low);
+    if (lane == 0 && w < 2) L.vin.flag[w] = bal != 0 ? 1u : 0u;
+  }
   __syncthreads();
   if (tid < kD) Lqp[tid] = L.vin.q[L.vin.perm[tid]];
+  const bool rebase = t == W - 1 || (L.vin.flag[0] | L.vin.flag[1]) != 0;
 
   // 2. exact S0 (g_t k_t), S0 (g_t q_t): digit planes of cf k and cf q, cf = fl(g_t R)
   prep<KDA, true>(L.vin, L.W, w, lane, Bw);
@@ -1321,12 +1336,14 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
   {
     const int sub = lane & 7, tk = lane >> 3;
     const int pb = 32 * w + 4 * sub;
+    // moving the base: the keys are decayed to Kt_i(t) in place and dotted with k_t, q_t;
+    // otherwise B_i is dotted with h_t k_t, h_t q_t and stays as it is
     float apl[4], kpl[4], qpl[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       apl[m] = Lap[pb + m];
-      kpl[m] = L.W.kp[pb + m];
-      qpl[m] = Lqp[pb + m];
+      kpl[m] = rebase ? L.W.kp[pb + m] : apl[m] * L.W.kp[pb + m];
+      qpl[m] = rebase ? Lqp[pb + m] : apl[m] * Lqp[pb + m];
     }
     for (int i0 = 0; i0 < t; i0 += 8) {
       const int i = i0 + tk;
@@ -1334,14 +1351,22 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
       if (i < t) {
         u32x4* kt = reinterpret_cast<u32x4*>(Kt + (size_t)i * kD + pb);
         u32x4 x = *kt;
+        if (rebase) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float e = __uint_as_float(x[m]) * apl[m];
-          sa = fmaf(e, kpl[m], sa);
-          sb = fmaf(e, qpl[m], sb);
-          x[m] = __float_as_uint(e);
+          for (int m = 0; m < 4; ++m) {
+            const float e = __uint_as_float(x[m]) * apl[m];
+            sa = fmaf(e, kpl[m], sa);
+            sb = fmaf(e, qpl[m], sb);
+            x[m] = __float_as_uint(e);
+          }
+          *kt = x;
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            sa = fmaf(__uint_as_float(x[m]), kpl[m], sa);
+            sb = fmaf(__uint_as_float(x[m]), qpl[m], sb);
+          }
         }
-        *kt = x;
       }
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1) {
@@ -1409,8 +1434,9 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
     A.o[uo + i] = (float)(fma((double)L.W.rf[i], L.W.osum[i],
                               (double)(L.sp[1][0][i] + L.sp[1][1][i]) + to) + (double)wt * kq);
     Wv[(size_t)t * kD + i] = wt;
-    Kt[(size_t)t * kD + i] = L.W.kp[i];
+    Kt[(size_t)t * kD + i] = rebase ? L.W.kp[i] : L.W.kp[i] / Lap[i];  // B_t = k_t / h_t
     gbuf[i] = Lgt[i];
+    hbuf[i] = rebase ? 1.0f : Lap[i];
   }
 }
 

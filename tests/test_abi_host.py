@@ -48,7 +48,7 @@ def test_state_bytes_matches_oracle_layout(oref, gate):
     assert L.packed_bytes == 7 * pool.req_bytes
     assert L.scale_bytes == 7 * 32 * 128 * 4
     assert L.meta_bytes == 64 + 32 * 272 + 64
-    assert L.window_bytes == 7 * 32 * (64 * 2 * 128 * 4 + 128 * 4)
+    assert L.window_bytes == 7 * 32 * (64 * 2 * 128 * 4 + 2 * 128 * 4)
 
 
 def _desc(n_req=2, n_head=4, dk=128, dv=128, gate=0, bits=None, window=0, rule=0):
