@@ -1329,8 +1329,9 @@ __global__ void __launch_bounds__(kThreads) k_window_token(WinArgs A) {
     }
   }
 
-  // 3. buffered keys: decay by a_t in place; dot with k_t and q_t over this wave's 32
-  //    positions. Eight lanes share a buffered token (16 bytes each: one contiguous
+  // 3. buffered keys: dot with h_t k_t and h_t q_t (or, when the base moves, decay by h_t
+  //    in place and dot with k_t and q_t) over this wave's 32 positions. Eight lanes share
+  //    a buffered token (16 bytes each: one contiguous
   //    128-byte segment per token and load), eight tokens per pass; the eight partial
   //    sums combine in a fixed butterfly order.
   {
