@@ -107,6 +107,19 @@ def test_pointer_validation_before_any_launch():
     assert rc == qdr.QDR_EALIGN
 
 
+def test_static_window_size_limit():
+    """qdr_decode_window_static holds n_req * n_head * (1024 W + 1024) bytes in its 32 MiB
+    array: 504 units at W = 64 fit (the call goes on to its pointer checks), 505 do not."""
+    L = qdr.lib()
+    P = 1 << 20
+    d, keep = _desc(n_req=505, n_head=1, window=64)
+    rc = L.qdr_decode_window_static(ctypes.byref(d), P, P, P, P, 0, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EUNSUPPORTED and "33612800 bytes" in qdr.last_error()
+    d, keep = _desc(n_req=504, n_head=1, window=64)
+    rc = L.qdr_decode_window_static(ctypes.byref(d), None, P, P, P, 0, P, P, P, P, P, P, None)
+    assert rc == qdr.QDR_EINVAL and "meta" in qdr.last_error()
+
+
 def test_window_position_validation():
     d, keep = _desc(window=0)
     L = qdr.lib()
