@@ -9,8 +9,8 @@
 // Arithmetic (the scalar reference's, except for the order of the fp64 dot products):
 //   gate + dequantize  S'_ip = fl(f32(h_ip) * g_p) (p < 16), fl(code_ip * fl(g_p * R_p))
 //   u_i                fl32 of the fp64 sum of S'_ip k_p; each product is exact in fp64,
-//                      summed here as two half sums (positions 0..63 and 64..127, each in
-//                      position order) added, where the reference takes one sum in key
+//                      summed here as two half sums (each thread's 64 positions in register
+//                      order, see dpos) added, where the reference takes one sum in key
 //                      channel order: the fp32 results can differ on rare rounding ties
 //   delta / update     w_i = fl(b fl(v_i - u_i)), S_new = fma(w_i, k_p, S'_ip)
 //   readout            o_i from S_new and q as u_i from S' and k
@@ -27,7 +27,7 @@
 // of block 4 that the thread codes, so that both threads of a row do the same work (the
 // fp64 half sums of the prediction and the readout are in-thread); the key-row absmax is a
 // shuffle reduce-scatter over the wave's 32 rows, then a max over the four waves through
-// LDS. LDS holds only the input vectors and the ranges (3.5 KB).
+// LDS. LDS holds only the input vectors, those maxima and the ranges (5.6 KB).
 #include "qdr_internal.h"
 
 namespace qdr {
@@ -38,9 +38,10 @@ constexpr int KDA = 1;
 constexpr int kH = kDampHalf;     // binary16 channels
 constexpr int kI = kD - kDampHalf;  // INT8 channels
 
-// Per-position vectors in LDS. The two threads of a row read positions e and 64 + e of
-// one vector at once; 16 bytes of padding after position 63 put the two halves on
-// different banks (without it, 512 bytes apart, every such read is a bank conflict).
+// Per-position vectors in LDS. The two threads of a row read the positions of one register
+// at once, 8 or 64 apart (dpos); 16 bytes of padding after position 63 put positions 64
+// apart on different banks (without it, 512 bytes apart, every such read is a bank
+// conflict).
 constexpr int kPadF = 4;  // floats
 constexpr int kPadD = 2;  // doubles
 __device__ __forceinline__ int fidx(int p) { return p + (p >> 6) * kPadF; }
