@@ -137,6 +137,24 @@ def test_window_extreme_gates(torch_cuda):
     run_windows(torch_cuda, w, 1, 4, bits, 24, 2, S0, "kda extreme gates W=24", gates)
 
 
+def test_window_base_moves_mid_window(torch_cuda):
+    """Gates between 0.2 and 0.35 on half the channels: their decay product since the base
+    falls below 2^-80 after 40-60 tokens, so the buffered keys are re-based in the middle of
+    the window and later tokens are stored relative to the new base."""
+    w = wl.WORKLOADS[2]
+    bits = bits_for(w, n_head=4)
+    rng = np.random.default_rng(13)
+    S0 = (0.1 * rng.standard_normal((2, 4, 128, 128))).astype(np.float32)
+    lo = np.random.default_rng(77).uniform(0.2, 0.35, size=64).astype(np.float32)
+
+    def gates(t, a):
+        x = a.copy()
+        x[..., ::2] = lo
+        return x
+
+    run_windows(torch_cuda, w, 2, 4, bits, 64, 2, S0, "kda small gates W=64", gates)
+
+
 def test_window_zero_requests_is_noop(torch_cuda):
     from quantized_delta_rule_03_amd import qdr
 
