@@ -1,7 +1,7 @@
 """Helpers for the GPU parity tests: build oracle references, move states between the
 GPU pool and an oracle pool, and compare them at the stated tolerances.
 
-Tolerances (spec bar): packed codes differ by at most 1 LSB on at most 1e-4 of
+Tolerances (the parity bar): packed codes differ by at most 1 LSB on at most 1e-4 of
 entries; each step's readout o has relative L2 error <= 1e-4; the dequantized state
 after 256 free-running steps drifts by <= 1e-3 relative L2.
 """
