@@ -8,7 +8,8 @@ magnitudes: smaller flat index first); the residual has those entries set to 0.
 Pins: the selection against a brute-force sort by numpy's lexsort; the exact split
 S = residual + tokens; ties, empty slots, the zero state; m = 0 reducing to the plain
 quantization and window; the window starting from the dequantized residual plus the
-tokens; spikes kept exactly and the quantization error they would cause removed.
+tokens; spikes kept exactly and the quantization error they would cause removed; a
+per-key-channel power-of-two smoothing absorbed exactly by the two-stage fit.
 """
 import numpy as np
 import pytest
@@ -92,6 +93,25 @@ def test_m0_is_the_plain_quantization():
     c2, R2, k2 = oracle.quantize(S, MIXED)
     assert idx.size == 0 and np.array_equal(c1, c2)
     assert np.array_equal(R1, R2) and np.array_equal(k1, k2)
+
+
+def test_key_channel_smoothing_is_absorbed_by_the_fit():
+    """The residual's smoothing is read as the existing two-stage fit (no separate
+    transform). What pins that reading: a per-key-channel diagonal smoothing S D (D a
+    diagonal of powers of two, as a smoothing would apply per channel) leaves every code and
+    value-column scale unchanged and multiplies each key-row range by its factor exactly,
+    because the key-row stage divides those ranges out before any rounding; so does a
+    global power-of-two factor."""
+    S, _ = spiky_state(9)
+    c0, R0, k0 = oracle.quantize(S, MIXED)
+    e = np.random.default_rng(3).integers(-6, 7, size=128)
+    D = np.ldexp(np.ones(128, np.float32), e).astype(np.float32)
+    c1, R1, k1 = oracle.quantize(np.ascontiguousarray(S * D[None, :]), MIXED)
+    assert np.array_equal(c1, c0) and np.array_equal(k1, k0)
+    assert np.array_equal(R1, (R0 * D).astype(np.float32))
+    c2, R2, k2 = oracle.quantize(np.ascontiguousarray(S * np.float32(2.0 ** -5)), MIXED)
+    assert np.array_equal(c2, c0) and np.array_equal(k2, k0)
+    assert np.array_equal(R2, (R0 * np.float32(2.0 ** -5)).astype(np.float32))
 
 
 def test_spikes_are_kept_exactly_and_their_error_removed():
