@@ -1595,19 +1595,20 @@ __device__ __forceinline__ void comp_select(float (&S)[64], int m_, uint16_t* to
       if (lane == 0) C.T0 = t0;
     }
   } else {
-    // wave w counts for the maxima 64 w + lane against all 256
-    const uint32_t x = C.qm[tid];
+    // the m-th largest of the 256 maxima, built bit by bit from the top (magnitudes: bit
+    // 31 is clear) from ballot counts; every wave finds the same value, wave 0 stores it
     const uint32_t y0 = C.qm[lane], y1 = C.qm[64 + lane], y2 = C.qm[128 + lane],
                    y3 = C.qm[192 + lane];
-    uint32_t ge = 0;
-#pragma unroll 16
-    for (int j = 0; j < 64; ++j)
-      ge += (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y0, j) >= x) +
-            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y1, j) >= x) +
-            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y2, j) >= x) +
-            (uint32_t)((uint32_t)__builtin_amdgcn_readlane((int)y3, j) >= x);
-    const uint32_t t0 = wave_max_u32(ge >= m ? x : 0u);
-    if (lane == 0) atomicMax(&C.T0, t0);
+    uint32_t T = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      const uint32_t cnt = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(y0 >= c)) +
+                           (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(y1 >= c)) +
+                           (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(y2 >= c)) +
+                           (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(y3 >= c));
+      if (cnt >= m) T = c;
+    }
+    if (tid == 0) C.T0 = T;
   }
   block_sync();
   // candidates: |S| >= T0 and nonzero (T0 raised to the smallest positive magnitude).
