@@ -1,8 +1,9 @@
 """GPU parity of the DAMP-style storage variant (qdr_damp_*) against the oracle's DampPool.
 
 The oracle takes the two dot products (u = S'k, o = S_new q) as one fp64 sum over the key
-channels in logical order; the kernel sums the same exact fp64 products in its own order,
-so u and o can differ in the last fp32 bit on rare rounding ties. Everything else (binary16
+channels in logical order. The kernel sums the same exact fp64 products of u in its own
+order, so u can differ in the last fp32 bit on rare rounding ties; it sums the readout o,
+which feeds nothing back into the state, in fp32. Everything else (binary16
 rounding, the per-row ranges, Philox4x32-10 stochastic rounding keyed by seed, unit and
 step) is the same rule on both sides. The bar asserted is that of the main format (codes
 within 1 LSB on <= 1e-4 of entries, o rel-L2 <= 1e-4, dequantized-state drift <= 1e-3);
