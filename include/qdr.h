@@ -265,14 +265,14 @@ int qdr_dequantize_state(const qdr_desc *desc, const void *meta, const void *pac
  *   meta  [n_head][128]                 physical position -> key channel (written by init)
  * Physical positions 0..15 are the selected channels, 16..127 the others, each in
  * increasing channel order. One decode step: S'_ij = fl(f32(h) a_j) or fl(code fl(a_j R_j));
- * u_i = S' k and o_i = S_new q accumulated in fp64 and rounded once to fp32 (the products
- * are exact in fp64; the order of the fp64 sums is the kernel's, so u and o can differ from
- * another fp64 order in the last fp32 bit on rare ties); w_i = fl(b fl(v_i - u_i));
+ * u_i = S' k accumulated in fp64 and rounded once to fp32 (the products are exact in fp64;
+ * the order of the fp64 sum is the kernel's, so u can differ from another fp64 order in the
+ * last fp32 bit on rare ties); o_i = S_new q accumulated in fp32 (within 1e-4 rel-L2); w_i = fl(b fl(v_i - u_i));
  * S_new = fma(w_i, k_j, S'_ij); then binary16 (round to nearest even) for the selected
  * channels and, for the others, A_j = max_i |S_ij| (1 if 0), R_j = fl(A_j/127),
  * y = fl(S fl(1/A_j)), code = clamp(floor(y*127 + u), +-127) evaluated in fp64 with u the
- * byte position%16 (little-endian across the four words, times 2^-8) of Philox4x32-10
- * (Salmon et al., SC11) for counter (row*8 + position/16, unit, step low, step high) and
+ * byte position%16 (little-endian across the four words, times 2^-8) of Philox4x32-7
+ * (Salmon et al., SC11: the published round function and key schedule, seven rounds) for counter (row*8 + position/16, unit, step low, step high) and
  * key (seed low, seed high), i.e. one generator block per 16 codes of a row;
  * unit = request*n_head + head. The caller passes a fresh step per call. Errors: as for
  * the main format; QDR_EUNSUPPORTED if a head does not select exactly 16 channels. */

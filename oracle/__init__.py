@@ -81,6 +81,7 @@ def lib():
             "oref_comp_window_pool": (i32, [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, i32,
                                             P, P, P, P, P, P, i64, i64]),
             "oref_philox4x32_10": (None, [P, P, P]),
+            "oref_philox4x32": (None, [P, P, ctypes.c_int, P]),
             "oref_f32_to_f16": (ctypes.c_uint16, [f32]),
             "oref_f16_to_f32": (f32, [ctypes.c_uint16]),
             "oref_damp_perm": (i32, [i32, P, P]),
@@ -469,6 +470,18 @@ class Pool:
 # ---------------------------------------------------------------------------
 
 DAMP_HALF = 16
+
+
+DAMP_PHILOX_ROUNDS = 7
+
+
+def philox4x32(ctr, key, rounds):
+    """Philox4x32 block with `rounds` rounds: 4 counter words, 2 key words -> 4 words."""
+    c = np.asarray(ctr, np.uint32).copy()
+    k = np.asarray(key, np.uint32).copy()
+    out = np.zeros(4, np.uint32)
+    lib().oref_philox4x32(_p(c), _p(k), int(rounds), _p(out))
+    return out
 
 
 def philox4x32_10(ctr, key):

@@ -690,13 +690,15 @@ int oref_comp_window_pool(int n_req, int n_head, int dv, int dk, int gate, const
  * Written from the storage description and the arithmetic contract in the header.
  * ---------------------------------------------------------------------------- */
 
-/* Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
- * 1, 2, 3" (SC11). Ten rounds of two 32x32->64 multiplies on the counter, the key
- * bumped by the Weyl constants between rounds. */
-void oref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+/* Philox4x32-R: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+ * 1, 2, 3" (SC11). R rounds of two 32x32->64 multiplies on the counter, the key
+ * bumped by the Weyl constants between rounds. The paper's default is R = 10; the
+ * stochastic rounding below uses R = 7, the fewest rounds with which the paper reports
+ * Philox4x32 passing its statistical test batteries. */
+void oref_philox4x32(const uint32_t ctr[4], const uint32_t key[2], int rounds, uint32_t out[4]) {
     uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
     uint32_t k0 = key[0], k1 = key[1];
-    for (int r = 0; r < 10; ++r) {
+    for (int r = 0; r < rounds; ++r) {
         if (r > 0) {
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
@@ -716,6 +718,10 @@ void oref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t o
     out[1] = c1;
     out[2] = c2;
     out[3] = c3;
+}
+
+void oref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    oref_philox4x32(ctr, key, 10, out);
 }
 
 /* IEEE 754 binary16 from binary32, round to nearest even (subnormals kept, overflow to
@@ -773,7 +779,7 @@ float oref_f16_to_f32(uint16_t h) {
 }
 
 /* uniform in [0, 1) for state entry (i, p) of a unit at a step: byte p mod 16 (little-endian
- * across the four words) of the Philox block for the counter (i*8 + p/16, unit, step low,
+ * across the four words) of the Philox4x32-7 block for the counter (i*8 + p/16, unit, step low,
  * step high), key = seed, times 2^-8 (one block serves sixteen consecutive positions of a
  * row) */
 static double damp_uniform(uint64_t seed, uint32_t unit, uint64_t step, int i, int p) {
@@ -781,7 +787,7 @@ static double damp_uniform(uint64_t seed, uint32_t unit, uint64_t step, int i, i
                              (uint32_t)(step >> 32)};
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     uint32_t out[4];
-    oref_philox4x32_10(ctr, key, out);
+    oref_philox4x32(ctr, key, OREF_DAMP_PHILOX_ROUNDS, out);
     const uint32_t byte = (out[(p / 4) % 4] >> (8 * (p % 4))) & 0xFFu;
     return ldexp((double)byte, -8);
 }

@@ -198,10 +198,14 @@ int oref_comp_window_pool(int n_req, int n_head, int dv, int dk, int gate, const
  *   requantize   selected: binary16 round-to-nearest-even; others: A_j = max_i |S_ij|
  *                (1 if 0), R_j = fl(A_j/127), y = fl(S * fl(1/A_j)),
  *                code = clamp(floor(y*127 + u), +-127) in fp64, u = uniform [0, 1):
- *                byte p mod 16 (little-endian over the four words) of Philox4x32-10 for
+ *                byte p mod 16 (little-endian over the four words) of Philox4x32-7 for
  *                counter (i*8 + p/16, unit, step lo, step hi) and key seed, times 2^-8. */
 #define OREF_DAMP_HALF 16
+#define OREF_DAMP_PHILOX_ROUNDS 7
 
+/* Philox4x32 with `rounds` rounds (the key bumped between rounds); _10 is the paper's
+ * default, kept for its published known answers */
+void oref_philox4x32(const uint32_t ctr[4], const uint32_t key[2], int rounds, uint32_t out[4]);
 void oref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 uint16_t oref_f32_to_f16(float x);
 float oref_f16_to_f32(uint16_t h);

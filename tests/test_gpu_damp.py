@@ -4,7 +4,7 @@ The oracle takes the two dot products (u = S'k, o = S_new q) as one fp64 sum ove
 channels in logical order. The kernel sums the same exact fp64 products of u in its own
 order, so u can differ in the last fp32 bit on rare rounding ties; it sums the readout o,
 which feeds nothing back into the state, in fp32. Everything else (binary16
-rounding, the per-row ranges, Philox4x32-10 stochastic rounding keyed by seed, unit and
+rounding, the per-row ranges, Philox4x32-7 stochastic rounding keyed by seed, unit and
 step) is the same rule on both sides. The bar asserted is that of the main format (codes
 within 1 LSB on <= 1e-4 of entries, o rel-L2 <= 1e-4, dequantized-state drift <= 1e-3);
 bit-exactness is reported, not required.

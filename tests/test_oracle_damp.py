@@ -4,7 +4,9 @@ The variant follows the freedom251 page's description of DAMP (section "DAMP: ac
 depends on the task"): a few selected key channels per head in FP16, the rest in INT8 with
 stochastic rounding; the page gives 16 channels per head and 9.9 effective bits per value.
 Pins: Philox4x32-10 against the known-answer vectors published with the generator
-(Salmon et al., SC11, Random123 distribution); binary16 conversion against numpy's
+(Salmon et al., SC11, Random123 distribution), and the seven-round generator that the
+stochastic rounding uses as the first seven of those ten rounds (finishing it with the last
+three rounds reproduces the known answers); binary16 conversion against numpy's
 independent implementation (exhaustively in one direction); stochastic rounding's support
 and unbiasedness; the write property through the variant's step; the identity step on
 FP16 channels; the zero state; bit accounting against the page's numbers.
@@ -29,6 +31,26 @@ def test_philox_known_answers():
     ]
     for ctr, key, want in kat:
         assert [int(x) for x in oracle.philox4x32_10(ctr, key)] == want
+
+
+def test_philox_seven_rounds_are_a_prefix_of_ten():
+    """Philox4x32-7 is the published generator stopped after seven rounds: the key of round
+    r is key + r * (0x9E3779B9, 0xBB67AE85), so three more rounds started from the 7-round
+    output with the key bumped seven times give the 10-round block, which the known answers
+    above pin. A wrong round count, a key bumped before the first round or a dropped bump
+    fails it."""
+    weyl = (0x9E3779B9, 0xBB67AE85)
+    rng = np.random.default_rng(29)
+    cases = [([0, 0, 0, 0], [0, 0]), ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2)]
+    cases += [(list(rng.integers(0, 2**32, 4)), list(rng.integers(0, 2**32, 2))) for _ in range(8)]
+    for ctr, key in cases:
+        seven = oracle.philox4x32(ctr, key, oracle.DAMP_PHILOX_ROUNDS)
+        k7 = [(int(key[i]) + 7 * weyl[i]) % 2**32 for i in range(2)]
+        assert [int(x) for x in oracle.philox4x32(seven, k7, 3)] == \
+            [int(x) for x in oracle.philox4x32_10(ctr, key)]
+    assert oracle.DAMP_PHILOX_ROUNDS == 7
+    assert not np.array_equal(oracle.philox4x32([1, 2, 3, 4], [5, 6], 7),
+                              oracle.philox4x32_10([1, 2, 3, 4], [5, 6]))
 
 
 def test_f16_to_f32_exhaustive():
@@ -139,8 +161,8 @@ def test_rounding_depends_on_seed_unit_and_step_only():
 
 def test_rounding_uses_the_documented_counter():
     """Each INT8 code is floor(y*127 + u) with u byte p mod 16 (little-endian across the
-    four words) of the Philox block for counter (i*8 + p/16, unit, step low, step high)
-    and key seed, times 2^-8 (the generator itself is pinned by its known answers above);
+    four words) of the Philox4x32-7 block for counter (i*8 + p/16, unit, step low, step high)
+    and key seed, times 2^-8 (the generator itself is pinned by the tests above);
     checked entry by entry on a unit past the first and a step above 2^32, at positions
     that cover every word and byte of a block and the first and last block of a row."""
     n_req, H = 2, 2
@@ -160,7 +182,7 @@ def test_rounding_uses_the_documented_counter():
         y = np.float32(col[i]) * (np.float32(1.0) / np.float32(A))
         ctr = [i * 8 + pos // 16, u, step & 0xFFFFFFFF, step >> 32]
         key = [seed & 0xFFFFFFFF, seed >> 32]
-        word = int(oracle.philox4x32_10(ctr, key)[(pos // 4) % 4])
+        word = int(oracle.philox4x32(ctr, key, 7)[(pos // 4) % 4])
         uu = ((word >> (8 * (pos % 4))) & 0xFF) / 256.0
         want = int(np.clip(np.floor(float(y) * 127.0 + uu), -127, 127))
         assert int(p.codes[u, i, pos - 16]) == want, (u, i, pos)
