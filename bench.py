@@ -71,7 +71,8 @@ def profile_record(path=PROFILE):
                     rec[k] = v.strip()
     except OSError:
         return {}
-    if rec.get("kernel_source_sha256") != rocprof_summary.kernel_source_sha256(ROOT):
+    kernels = "damp" if "damp" in os.path.basename(path) else "k_step<"
+    if rec.get("kernel_source_sha256") != rocprof_summary.kernel_source_sha256(ROOT, kernels):
         return {}
     return rec
 

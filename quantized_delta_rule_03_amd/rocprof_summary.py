@@ -48,14 +48,20 @@ def is_copy(name):
     return "elementwise" in name and "MulFunctor" in name
 
 
-def kernel_source_sha256(root):
-    """Hash of the kernel sources' code: line comments, trailing blanks and blank lines are
-    left out, so a summary stays valid across comment-only edits and goes stale on any
-    change to the code."""
+def kernel_sources(kernels):
+    """The source files whose code a summary of `kernels` (name fragments) depends on: the
+    DAMP-style variant's kernels live in qdr_damp.hip, every other kernel in qdr_kernels.hip;
+    both include qdr_internal.h."""
+    main = "qdr_damp.hip" if "damp" in kernels else "qdr_kernels.hip"
+    return (f"quantized_delta_rule_03_amd/csrc/{main}", "quantized_delta_rule_03_amd/csrc/qdr_internal.h")
+
+
+def kernel_source_sha256(root, kernels="k_step<"):
+    """Hash of the code of the sources that `kernels` are built from: line comments,
+    trailing blanks and blank lines are left out, so a summary stays valid across
+    comment-only edits and goes stale on any change to that code."""
     h = hashlib.sha256()
-    for rel in ("quantized_delta_rule_03_amd/csrc/qdr_kernels.hip",
-                "quantized_delta_rule_03_amd/csrc/qdr_damp.hip",
-                "quantized_delta_rule_03_amd/csrc/qdr_internal.h"):
+    for rel in kernel_sources(kernels):
         with open(os.path.join(root, rel), encoding="utf-8") as f:
             for line in f:
                 code = line.split("//", 1)[0].rstrip()
@@ -114,7 +120,7 @@ def main():
     if not os.path.exists(os.path.join(d, "fetch_counter_collection.csv")):
         lines.append("## Machine-readable")
         lines.append("")
-        lines.append(f"kernel_source_sha256: {kernel_source_sha256(root)}")
+        lines.append(f"kernel_source_sha256: {kernel_source_sha256(root, args.kernels)}")
         print("\n".join(lines))
         return
     fetch = counters(os.path.join(d, "fetch_counter_collection.csv"), is_step)["FETCH_SIZE"]
@@ -177,7 +183,7 @@ def main():
     lines.append(f"write_scale: {f_write:.4f}")
     for name in sorted(means):
         lines.append(f"{name}: {means[name]:.0f}")
-    lines.append(f"kernel_source_sha256: {kernel_source_sha256(root)}")
+    lines.append(f"kernel_source_sha256: {kernel_source_sha256(root, args.kernels)}")
     print("\n".join(lines))
 
 
